@@ -1,0 +1,106 @@
+"""CPU oracle for the MiniMax-M3 lightning-indexer decode pass (fp64, plain C).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the package smoke check and the
+benchmark's CPU-baseline leg are the only callers. Nothing on the product path
+imports this package. The computation itself is in msa_oracle.c, whose header
+states the definition it follows and the passages it comes from.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from .build import build, library_path
+
+HEADS = 4
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+class Oracle:
+    """Bindings to one build of msa_oracle.c (the default build, or a test's variant)."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        P = ctypes.c_void_p
+        i32, i64 = ctypes.c_int32, ctypes.c_int64
+        lib.msa_oracle_block_scores.argtypes = [P, P, P, P, i32, i32, i32, i64, P]
+        lib.msa_oracle_block_scores.restype = ctypes.c_int
+        lib.msa_oracle_select.argtypes = [P, P, i32, i32, i32, i32, i32, P, P]
+        lib.msa_oracle_select.restype = ctypes.c_int
+        lib.msa_oracle_num_threads.argtypes = []
+        lib.msa_oracle_num_threads.restype = ctypes.c_int
+        self.lib = lib
+        self.path = path
+
+    def num_threads(self) -> int:
+        return int(self.lib.msa_oracle_num_threads())
+
+    def block_scores(self, q, k_cache, block_table, seq_lens) -> np.ndarray:
+        """fp64 block scores [B, 4, W]; -inf at and past each row's end."""
+        q = np.ascontiguousarray(q, dtype=np.uint16)
+        k_cache = np.ascontiguousarray(k_cache, dtype=np.uint16)
+        block_table = np.ascontiguousarray(block_table, dtype=np.int32)
+        seq_lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+        B, W = block_table.shape
+        assert q.shape == (B, HEADS, 128) and k_cache.shape[1:] == (128, 128)
+        assert seq_lens.shape == (B,)
+        out = np.empty((B, HEADS, W), dtype=np.float64)
+        rc = self.lib.msa_oracle_block_scores(_ptr(q), _ptr(k_cache), _ptr(block_table),
+                                              _ptr(seq_lens), B, W, W, k_cache.shape[0], _ptr(out))
+        if rc != 0:
+            raise ValueError(f"oracle block_scores failed with code {rc}")
+        return out
+
+    def select(self, scores, seq_lens, topk: int, n_init: int, n_local: int):
+        """Pinned top-k per (row, head): (ids int32 [B,4,topk], scores fp64 [B,4,topk])."""
+        scores = np.ascontiguousarray(scores, dtype=np.float64)
+        seq_lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+        B, H, W = scores.shape
+        assert H == HEADS and seq_lens.shape == (B,)
+        ids = np.empty((B, HEADS, topk), dtype=np.int32)
+        out = np.empty((B, HEADS, topk), dtype=np.float64)
+        rc = self.lib.msa_oracle_select(_ptr(scores), _ptr(seq_lens), B, W, topk, n_init, n_local,
+                                        _ptr(ids), _ptr(out))
+        if rc != 0:
+            raise ValueError(f"oracle select failed with code {rc}")
+        return ids, out
+
+    def decode(self, inp):
+        """Whole pass on a synth.Inputs: (ids, selected scores, block scores)."""
+        s = self.block_scores(inp.q, inp.k_cache, inp.block_table, inp.seq_lens)
+        ids, sc = self.select(s, inp.seq_lens, inp.topk, inp.n_init, inp.n_local)
+        return ids, sc, s
+
+
+_default = None
+
+
+def default() -> Oracle:
+    global _default
+    if _default is None:
+        path = library_path()
+        if not os.path.exists(path):
+            build()
+        _default = Oracle(path)
+    return _default
+
+
+def num_threads() -> int:
+    return default().num_threads()
+
+
+def block_scores(q, k_cache, block_table, seq_lens) -> np.ndarray:
+    return default().block_scores(q, k_cache, block_table, seq_lens)
+
+
+def select(scores, seq_lens, topk: int, n_init: int, n_local: int):
+    return default().select(scores, seq_lens, topk, n_init, n_local)
+
+
+def decode(inp):
+    return default().decode(inp)

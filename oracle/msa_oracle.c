@@ -1,0 +1,218 @@
+/*
+ * msa_oracle.c -- plain CPU oracle for the MiniMax-M3 lightning-indexer decode pass.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the test suite, the package smoke check and the
+ * benchmark's CPU-baseline leg may load or run this library. It shares no code,
+ * header, table or helper with the GPU library and must never be used to produce
+ * a product result.
+ *
+ * It is written to be obviously correct, not fast: plain loops, fp64 arithmetic,
+ * a library sort for the selection, OpenMP only over independent (row, block)
+ * pairs. Every value it computes has a plain definition, which the code writes out.
+ *
+ * What it computes, per decode row b (one decode token) and index head h:
+ *
+ *   block score   S[b][h][j] = max over the valid tokens t of block j of
+ *                              sum_d q[b][h][d] * k[page][t][d]
+ *       - The four index heads share one index-K head, so one page is scored
+ *         for all heads (vLLM PR #57832, "Problem"; SGLang PR #41488,
+ *         "Motivation" and "Modifications": four heads, dim 128, 128-token
+ *         blocks, max scoring).
+ *       - A block's score is the max over its tokens; the max starts at -inf
+ *         (TensorRT-LLM PR #17008, "Description" calls the pass a max-score
+ *         pass; "Accuracy" seeds each per-tile max at -infinity).
+ *       - The visible tokens of a single decode token are all seq_len context
+ *         tokens: the causal clamp min(q_end + offset_q, kv_len) equals kv_len
+ *         for the last query position (TensorRT-LLM PR #17008, "Description").
+ *         Tokens of the partial last block past seq_len are not scored.
+ *       - No positive scale is applied: top-k order does not change under one
+ *         (vLLM blog "Following the Bottleneck", section 2, "What work repeats?").
+ *       - Logical block j lives in physical page block_table[b][j]; a page holds
+ *         128 tokens x 128 dims (vLLM PR #57832 runs with --block-size 128;
+ *         vLLM blog section 3 maps selected logical blocks to physical pages).
+ *
+ *   selection     the top m = min(topk, nb) blocks of each (b, h), where nb is
+ *                 the number of blocks in row b:
+ *       - selection is per index head; heads are never mixed (vLLM PR #57832,
+ *         "Solution" steps 3-4 and the withdrawn head-mixing design in
+ *         "Test Result");
+ *       - the first n_init blocks and the last n_local blocks are pinned and
+ *         always selected (vLLM PR #57832, "Solution": forced init/sink and
+ *         sliding-window blocks; SGLang PR #41488: initial/recent priorities);
+ *       - order: pinned first, then higher score, then lower block id (ties
+ *         broken by ascending id); scores compare numerically, so -0 == +0;
+ *       - slots m .. topk-1 hold id -1 and score -inf; an empty row has none.
+ *
+ * bf16 inputs are widened exactly (bits << 16 is the fp32 value; fp32 -> fp64
+ * is exact), products of two bf16 values are exact in fp64, and the 128-term
+ * sums are accumulated in fp64.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define OR_HEADS 4
+#define OR_DIM 128
+#define OR_BLOCK 128
+
+#define OR_OK 0
+#define OR_ERR_ARG -1
+#define OR_ERR_PAGE -2
+#define OR_ERR_NONFINITE -3
+
+static double widen_bf16(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+static int64_t row_len(const int32_t *seq_lens, int32_t b, int32_t max_blocks)
+{
+    int64_t L = seq_lens[b];
+    int64_t cap = (int64_t)max_blocks * OR_BLOCK;
+    if (L < 0) L = 0;
+    if (L > cap) L = cap;
+    return L;
+}
+
+int msa_oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/*
+ * Block scores, out[b][h][j] for j < max_blocks (fp64). Blocks at or past the
+ * row's end hold -inf. Returns OR_ERR_PAGE if a block the row needs maps to a
+ * page outside [0, num_pages).
+ */
+int msa_oracle_block_scores(const uint16_t *q, const uint16_t *k_cache,
+                            const int32_t *block_table, const int32_t *seq_lens,
+                            int32_t batch, int32_t max_blocks, int32_t bt_stride,
+                            int64_t num_pages, double *out)
+{
+    if (batch < 0 || max_blocks < 0 || bt_stride < max_blocks) return OR_ERR_ARG;
+    int64_t total = (int64_t)batch * max_blocks;
+    int status = OR_OK;
+
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t bj = 0; bj < total; ++bj) {
+        int32_t b = (int32_t)(bj / max_blocks);
+        int32_t j = (int32_t)(bj % max_blocks);
+        int64_t L = row_len(seq_lens, b, max_blocks);
+        int64_t nb = (L + OR_BLOCK - 1) / OR_BLOCK;
+        double best[OR_HEADS];
+        for (int h = 0; h < OR_HEADS; ++h) best[h] = -INFINITY;
+
+        if (j < nb) {
+            int64_t page = block_table[(int64_t)b * bt_stride + j];
+            if (page < 0 || page >= num_pages) {
+#pragma omp atomic write
+                status = OR_ERR_PAGE;
+            } else {
+                int64_t valid = L - (int64_t)j * OR_BLOCK;
+                if (valid > OR_BLOCK) valid = OR_BLOCK;
+                for (int64_t t = 0; t < valid; ++t) {
+                    const uint16_t *tok = k_cache + (page * OR_BLOCK + t) * OR_DIM;
+                    double kt[OR_DIM];
+                    for (int d = 0; d < OR_DIM; ++d) kt[d] = widen_bf16(tok[d]);
+                    for (int h = 0; h < OR_HEADS; ++h) {
+                        const uint16_t *qh = q + ((int64_t)b * OR_HEADS + h) * OR_DIM;
+                        double s = 0.0;
+                        for (int d = 0; d < OR_DIM; ++d) s += widen_bf16(qh[d]) * kt[d];
+                        if (s > best[h]) best[h] = s;
+                    }
+                }
+                for (int h = 0; h < OR_HEADS; ++h) {
+                    if (!isfinite(best[h])) {
+#pragma omp atomic write
+                        status = OR_ERR_NONFINITE;
+                    }
+                }
+            }
+        }
+        for (int h = 0; h < OR_HEADS; ++h)
+            out[((int64_t)b * OR_HEADS + h) * max_blocks + j] = best[h];
+    }
+    return status;
+}
+
+typedef struct {
+    int pinned;
+    double score;
+    int32_t id;
+} cand_t;
+
+/* pinned first, then higher score, then lower id */
+static int cand_order(const void *pa, const void *pb)
+{
+    const cand_t *a = (const cand_t *)pa, *b = (const cand_t *)pb;
+    if (a->pinned != b->pinned) return a->pinned ? -1 : 1;
+    if (a->score > b->score) return -1;
+    if (a->score < b->score) return 1;
+    return (a->id < b->id) ? -1 : (a->id > b->id);
+}
+
+/*
+ * Pinned top-k per (row, head) from block scores scores[b][h][j] (j < max_blocks).
+ * Writes out_ids[b][h][i] and out_scores[b][h][i] for i < topk.
+ */
+int msa_oracle_select(const double *scores, const int32_t *seq_lens,
+                      int32_t batch, int32_t max_blocks, int32_t topk,
+                      int32_t n_init, int32_t n_local,
+                      int32_t *out_ids, double *out_scores)
+{
+    if (batch < 0 || max_blocks < 0 || topk < 1 || n_init < 0 || n_local < 0)
+        return OR_ERR_ARG;
+    int status = OR_OK;
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bh = 0; bh < (int64_t)batch * OR_HEADS; ++bh) {
+        int32_t b = (int32_t)(bh / OR_HEADS);
+        int64_t L = row_len(seq_lens, b, max_blocks);
+        int64_t nb = (L + OR_BLOCK - 1) / OR_BLOCK;
+        int64_t m = nb < topk ? nb : topk;
+        const double *row = scores + bh * max_blocks;
+        cand_t *c = (cand_t *)malloc((size_t)(nb > 0 ? nb : 1) * sizeof(cand_t));
+        if (!c) {
+#pragma omp atomic write
+            status = OR_ERR_ARG;
+            continue;
+        }
+        for (int64_t j = 0; j < nb; ++j) {
+            c[j].pinned = (j < n_init) || (j >= nb - n_local);
+            c[j].score = row[j];
+            c[j].id = (int32_t)j;
+        }
+        qsort(c, (size_t)nb, sizeof(cand_t), cand_order);
+        for (int64_t i = 0; i < topk; ++i) {
+            out_ids[bh * topk + i] = i < m ? c[i].id : -1;
+            out_scores[bh * topk + i] = i < m ? c[i].score : -INFINITY;
+        }
+        free(c);
+    }
+    return status;
+}
+
+/* Both steps: block scores into scratch (caller-sized [batch][4][max_blocks]), then selection. */
+int msa_oracle_decode(const uint16_t *q, const uint16_t *k_cache,
+                      const int32_t *block_table, const int32_t *seq_lens,
+                      int32_t batch, int32_t max_blocks, int32_t bt_stride,
+                      int64_t num_pages, int32_t topk, int32_t n_init, int32_t n_local,
+                      double *scratch_scores, int32_t *out_ids, double *out_scores)
+{
+    int rc = msa_oracle_block_scores(q, k_cache, block_table, seq_lens, batch, max_blocks,
+                                     bt_stride, num_pages, scratch_scores);
+    if (rc != OR_OK) return rc;
+    return msa_oracle_select(scratch_scores, seq_lens, batch, max_blocks, topk, n_init,
+                             n_local, out_ids, out_scores);
+}

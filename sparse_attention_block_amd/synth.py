@@ -1,0 +1,276 @@
+"""Seeded synthetic inputs for the MiniMax-M3 lightning-indexer decode pass.
+
+This module only draws and lays out inputs. It holds none of the pass's
+arithmetic (no dot products, maxima or selection), so the GPU path and the
+CPU oracle can both consume exactly the same bf16 bits from it.
+
+Layouts (row-major, as both sides read them):
+  q            uint16 [B, 4, 128]        bf16 bit patterns, one decode token per row
+  k_cache      uint16 [P, 128, 128]      bf16 bit patterns, page-major, token-major
+  block_table  int32  [B, W]             logical block j of row b -> physical page
+  seq_lens     int32  [B]                tokens in row b's context (0 .. W*128)
+
+Workload shapes follow the pages: 4 index heads of dim 128 sharing one index-K
+head, 128-token pages (SGLang PR #41488 "[AMD] Add opt-in MiniMax-M3 TP4 indexer
+context partitioning", Modifications; TensorRT-LLM PR #17008, Performance/Kernel
+table), a top-16 with pinned initial and recent blocks (vLLM PR #57832, Solution).
+
+Random draws use NumPy PCG64. Big arrays are drawn in fixed chunks, each from
+its own SeedSequence child, so the result does not depend on how the chunks
+are scheduled.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+HEADS = 4
+DIM = 128
+BLOCK = 128  # tokens per logical block == tokens per page
+
+_CHUNK_ELEMS = 1 << 22  # elements per independently seeded chunk
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit patterns, round to nearest even (finite inputs)."""
+    a = np.array(x, dtype=np.float32, order="C", copy=True)
+    u = a.reshape(-1).view(np.uint32)
+    lsb = u >> 16
+    lsb &= 1
+    u += lsb
+    u += np.uint32(0x7FFF)
+    u >>= 16
+    return u.astype(np.uint16).reshape(a.shape)
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> fp32 values (exact)."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def _child(seed: int, stream: int, chunk: int = 0) -> np.random.Generator:
+    return np.random.default_rng(np.random.SeedSequence([seed, stream, chunk]))
+
+
+def normal_bf16(seed: int, stream: int, shape) -> np.ndarray:
+    """~N(0,1) bf16 bit patterns of `shape`, drawn chunk by chunk."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint16)
+    for c, lo in enumerate(range(0, n, _CHUNK_ELEMS)):
+        hi = min(n, lo + _CHUNK_ELEMS)
+        out[lo:hi] = bf16_bits(_child(seed, stream, c).standard_normal(hi - lo, dtype=np.float32))
+    return out.reshape(shape)
+
+
+@dataclass
+class Inputs:
+    """One decode-pass input set plus the selection parameters."""
+
+    name: str
+    q: np.ndarray
+    k_cache: np.ndarray
+    block_table: np.ndarray
+    seq_lens: np.ndarray
+    topk: int = 16
+    n_init: int = 1
+    n_local: int = 2
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def batch(self) -> int:
+        return int(self.q.shape[0])
+
+    @property
+    def max_blocks(self) -> int:
+        return int(self.block_table.shape[1])
+
+    @property
+    def num_pages(self) -> int:
+        return int(self.k_cache.shape[0])
+
+    @property
+    def index_k_bytes(self) -> int:
+        """Index-K bytes the pass must read: sum of seq_len * 128 dims * 2 B."""
+        return int(np.asarray(self.seq_lens, dtype=np.int64).clip(min=0).sum()) * DIM * 2
+
+
+def _nblocks(lens: np.ndarray) -> np.ndarray:
+    return (np.asarray(lens, dtype=np.int64) + BLOCK - 1) // BLOCK
+
+
+def poison_tokens(n: int, value: float = 64.0) -> np.ndarray:
+    """Tokens that must never be read: +value / -value vectors, alternating.
+
+    A pass that wrongly scores one of them gets |value * sum(q)|, far above
+    any ~N(0,1) block score, whatever the sign of the query sum.
+    """
+    tok = np.empty((n, DIM), dtype=np.float32)
+    tok[0::2] = value
+    tok[1::2] = -value
+    return bf16_bits(tok)
+
+
+def paged_case(seed: int, seq_lens, max_blocks: int, *, permute: bool = True,
+               poison: bool = True, extra_pages: int = 0, name: str | None = None,
+               topk: int = 16, n_init: int = 1, n_local: int = 2) -> Inputs:
+    """Random ~N(0,1) q / index-K with a paged block table.
+
+    Every valid block gets its own page. With `permute` the pages are a random
+    permutation; with `poison`, table entries past a row's last block point to
+    a poison page and the invalid tail tokens of partial blocks are poison, so
+    any read the pass should not make shows up in its scores.
+    """
+    lens = np.asarray(seq_lens, dtype=np.int32)
+    B = int(lens.shape[0])
+    W = int(max_blocks)
+    nb = _nblocks(lens)
+    assert np.all(lens >= 0) and np.all(nb <= W)
+    n_valid = int(nb.sum())
+    n_pages = n_valid + extra_pages + (1 if poison else 0)
+    q = normal_bf16(seed, 0, (B, HEADS, DIM))
+    k = normal_bf16(seed, 1, (n_pages, BLOCK, DIM))
+    order = _child(seed, 2).permutation(n_pages) if permute else np.arange(n_pages)
+    order = order.astype(np.int32)
+    bt = np.zeros((B, W), dtype=np.int32)
+    poison_page = int(order[-1]) if poison else 0
+    pos = 0
+    for b in range(B):
+        n = int(nb[b])
+        bt[b, :n] = order[pos:pos + n]
+        pos += n
+        bt[b, n:] = poison_page if poison else 0
+    if poison:
+        k[poison_page] = poison_tokens(BLOCK)
+        for b in range(B):
+            v = int(lens[b]) - (int(nb[b]) - 1) * BLOCK
+            if nb[b] > 0 and v < BLOCK:
+                k[bt[b, nb[b] - 1], v:] = poison_tokens(BLOCK - v)
+    return Inputs(name or f"paged(seed={seed},B={B},W={W})", q, k, bt, lens,
+                  topk=topk, n_init=n_init, n_local=n_local,
+                  meta={"poison_page": poison_page if poison else None})
+
+
+# ---------------------------------------------------------------------------
+# The five workloads.
+
+
+def config1() -> Inputs:
+    """Batch 1, 8192 tokens (64 full blocks), identity block table."""
+    B, L, W = 1, 8192, 64
+    q = normal_bf16(1, 0, (B, HEADS, DIM))
+    k = normal_bf16(1, 1, (W, BLOCK, DIM))
+    bt = np.arange(W, dtype=np.int32).reshape(1, W)
+    return Inputs("cfg1 B=1 x 8192", q, k, bt, np.full(B, L, dtype=np.int32))
+
+
+def config2() -> Inputs:
+    """Batch 8, 32768 tokens each (256 blocks), pages a random permutation."""
+    B, L, W = 8, 32768, 256
+    q = normal_bf16(2, 0, (B, HEADS, DIM))
+    k = normal_bf16(2, 1, (B * W, BLOCK, DIM))
+    bt = _child(2, 2).permutation(B * W).astype(np.int32).reshape(B, W)
+    return Inputs("cfg2 B=8 x 32768", q, k, bt, np.full(B, L, dtype=np.int32))
+
+
+def config3() -> Inputs:
+    """Batch 32, 131072 tokens each (1024 blocks, 1 GiB of index-K), shuffled pages."""
+    B, L, W = 32, 131072, 1024
+    q = normal_bf16(3, 0, (B, HEADS, DIM))
+    k = normal_bf16(3, 1, (B * W, BLOCK, DIM))
+    bt = _child(3, 2).permutation(B * W).astype(np.int32).reshape(B, W)
+    return Inputs("cfg3 B=32 x 131072", q, k, bt, np.full(B, L, dtype=np.int32))
+
+
+def config4() -> Inputs:
+    """Batch 16 of mixed lengths: one 131072-token row, one empty row, the rest U[1,1024].
+
+    Lengths are drawn first (they size the page pool), then q, K and the page
+    permutation. One poison page backs every table entry past a row's end, and
+    the invalid tail tokens of partial blocks are poison.
+    """
+    B, W = 16, 1024
+    rng = _child(4, 3)
+    rows = rng.permutation(B)
+    long_row, empty_row = int(rows[0]), int(rows[1])
+    lens = rng.integers(1, 1025, size=B).astype(np.int32)
+    lens[long_row] = 131072
+    lens[empty_row] = 0
+    inp = paged_case(4, lens, W, name="cfg4 B=16 mixed")
+    inp.meta.update(long_row=long_row, empty_row=empty_row)
+    return inp
+
+
+# Planted runs for the adversarial workload. Each entry: per-head list of
+# (first block, [target score per block of the run]); an empty list plants
+# nothing for that head. Scores are exact integers, see config5().
+def _cfg5_runs():
+    t100 = [100] * 16
+    runs = {
+        0: [(16, t100)] * 4,                                   # split-aligned run, all tied
+        1: [(5, [110, 120, 110, 110, 120, 110, 110, 120, 110, 110, 120, 110, 110, 120, 110, 120])] * 4,
+        2: [(0, t100)] * 4,                                    # overlaps pinned initial block
+        3: [(52, t100)] * 4,                                   # overlaps both pinned recent blocks
+        4: [(32, list(range(115, 99, -1)))] * 4,               # distinct descending targets
+        5: [(20, [100] * 10)] * 4,                             # 3 slots left to background ties
+        6: [(40, t100), (44, t100), (48, t100), (36, t100)],   # heads disagree
+        7: [(48, t100)] * 4,                                   # plus a planted masked tail
+        8: [] ,                                                # background only: ties everywhere
+        9: [(1, t100)] * 4,
+        10: [(50, t100)] * 4,
+        11: [(3, t100), (19, t100), (35, t100), (51, t100)],
+        12: [(24, [100, 100, 100] + [127] * 13)] * 4,
+        13: [(10, [105] * 20)] * 4,                            # more tied winners than slots
+        14: [(8, [100, 101] * 8)] * 4,
+        15: [(60, [100] * 8)] * 4,                             # reaches the pinned tail blocks
+    }
+    return {b: (r if r else [(0, [])] * 4) for b, r in runs.items()}
+
+
+def config5() -> Inputs:
+    """Batch 16 x 8700 tokens (68 blocks, last one has 124 valid), planted adversarial scores.
+
+    Every score is an exact small integer, so any fp32 summation order gives
+    the same value and the selected IDs must agree bit for bit:
+      * q[b,h,:] is +-1 (signs of a seeded normal draw);
+      * background index-K entries are uniform in {-1, 0, +1};
+      * in each row a run of blocks gets, in token slot h, the vector q[b,h,:]
+        with all but its first T entries zeroed, so that token scores exactly
+        T >= 100 for head h, far above any background token;
+      * row 7 also plants q[b,h,:] itself (score 128) in the invalid tail slots
+        124+h of the partial last block, which the pass must ignore.
+    Runs cover exact ties, runs aligned and unaligned to splits, runs that
+    overlap the pinned initial / recent blocks and heads that disagree.
+    """
+    B, L, W = 16, 8700, 68
+    seed = 5
+    sgn = _child(seed, 0).standard_normal((B, HEADS, DIM))
+    qf = np.where(sgn >= 0, 1.0, -1.0).astype(np.float32)
+    q = bf16_bits(qf)
+    n_pages = B * W
+    kf = _child(seed, 1).integers(-1, 2, size=(n_pages, BLOCK, DIM)).astype(np.float32)
+    bt = _child(seed, 2).permutation(n_pages).astype(np.int32).reshape(B, W)
+    planted = {}
+    for b, per_head in _cfg5_runs().items():
+        for h, (w0, targets) in enumerate(per_head):
+            for i, t in enumerate(targets):
+                j = w0 + i
+                tok = qf[b, h].copy()
+                tok[t:] = 0.0
+                kf[bt[b, j], h] = tok
+                planted[(b, h, j)] = t
+    masked_row = 7
+    last = (L - 1) // BLOCK
+    v = L - last * BLOCK
+    for h in range(HEADS):
+        kf[bt[masked_row, last], v + h] = qf[masked_row, h]
+    k = bf16_bits(kf)
+    return Inputs("cfg5 B=16 x 8700 planted", q, k, bt, np.full(B, L, dtype=np.int32),
+                  meta={"planted": planted, "masked_row": masked_row})
+
+
+CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
+
+
+def config(i: int) -> Inputs:
+    return CONFIGS[i]()
