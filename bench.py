@@ -1,0 +1,206 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the MiniMax-M3 lightning-indexer pass on one MI355X.
+
+One step = one msa_indexer_decode-equivalent pass (stage 1: split scoring + per-split
+top-16; stage 2: exact merge) over batch 32 x 131072-token rows (1024 blocks of 128
+tokens each, 1 GiB of bf16 index-K behind a shuffled block table), 4 index heads x 128,
+top-16 with 1 initial and 2 recent blocks pinned. Inputs are seeded synthetic data,
+resident in HBM before timing starts.
+
+Prints one JSON line: the metric is index-K GB/s (bytes = sum seq_len * 128 * 2 per step)
+with us/step beside it, a roofline object for the dominant kernel (stage 1, timed with HIP
+events on the launch stream), and the CPU oracle's rate on the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "µs/decode step + index-K GB/s (% of 8 TB/s) at batch 32 × 128K ctx"
+HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCE = os.path.join(ROOT, "sparse_attention_block_amd", "csrc", "msa_indexer.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_split_kernel_b32_128k.json")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(engine: int):
+    """HBM bytes per stage-1 launch from the committed rocprofv3 counter runs, if they were
+    taken on the current kernel source; otherwise None."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash() or rec.get("engine") != engine:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, repeats: int = 3):
+    import oracle
+    times = []
+    for _ in range(repeats):
+        t0 = time.perf_counter()
+        oracle.decode(inp)
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times)
+    return {
+        "value": round(inp.index_k_bytes / t / 1e9, 3),
+        "unit": "GB/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"the whole workload (all {inp.batch} rows x {inp.max_blocks} blocks), "
+                  f"median of {repeats} passes of scores + selection, fp64, {t * 1e3:.1f} ms/pass",
+        "ms_per_step": round(t * 1e3, 3),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--engine", type=int, default=0, help="0 default, 1 VALU dot2, 2 MFMA")
+    ap.add_argument("--splits", type=int, default=0, help="0 = automatic split count")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a 1 GiB device copy (for scaling HBM counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    if args.copy_calibration:
+        # A plain device-to-device copy of exactly 1 GiB, to calibrate FETCH_SIZE/WRITE_SIZE.
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup + args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {args.warmup + args.steps} x 1 GiB")
+        return 0
+
+    import sparse_attention_block_amd as msa
+    from sparse_attention_block_amd import synth
+
+    lib = msa.load()  # raises if the HIP library is not built
+    log("generating the batch 32 x 131072 workload (1 GiB of bf16 index-K)")
+    t0 = time.time()
+    inp = synth.config3()
+    log(f"generated in {time.time() - t0:.1f} s")
+    B, W, topk, n_init, n_local = inp.batch, inp.max_blocks, inp.topk, inp.n_init, inp.n_local
+    nbytes = inp.index_k_bytes
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    q = torch.from_numpy(inp.q.view(np.int16)).to(dev).view(torch.bfloat16)
+    k = torch.from_numpy(inp.k_cache.view(np.int16)).to(dev).view(torch.bfloat16)
+    bt = torch.from_numpy(inp.block_table).to(dev)
+    lens = torch.from_numpy(inp.seq_lens).to(dev)
+    splits = msa.num_splits(B, W, topk, args.splits)
+    ws = msa.new_workspace(B, W, topk, args.splits, dev)
+    ids = torch.empty((B, 4, topk), dtype=torch.int32, device=dev)
+    sc = torch.empty((B, 4, topk), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    log(f"inputs resident in HBM; {splits} splits per row, engine {args.engine}")
+
+    stream = torch.cuda.current_stream()
+
+    def step(ev0=None, ev1=None):
+        if ev0 is not None:
+            ev0.record(stream)
+        msa.msa_indexer_split_topk(q, k, bt, lens, ws, topk, n_init, n_local,
+                                   num_splits=args.splits, engine=args.engine)
+        if ev1 is not None:
+            ev1.record(stream)
+        msa.msa_indexer_merge(lens, W, ws, ids, sc, topk, num_splits=args.splits)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps)")
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for e0, e1 in ev:
+        step(e0, e1)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    kernel_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+    log(f"timed {args.steps} steps in {elapsed:.3f} s")
+    if msa.msa_indexer_read_error(ws) != 0:
+        log("device error flag set")
+        return 1
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    us_per_step = ms_per_step * 1e3
+    gbs = nbytes / (ms_per_step * 1e-3) / 1e9
+    k_ms = statistics.mean(kernel_ms)
+    k_gbs = nbytes / (k_ms * 1e-3) / 1e9
+    engine = args.engine if args.engine else 1
+    traffic = measured_traffic(engine)
+
+    out = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_step": round(us_per_step, 2),
+        "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 q and index-K, shuffled page table)",
+        "config": {
+            "workload": "batch 32 x 131072-token rows, 1024 blocks of 128 tokens, 4 index heads x 128, "
+                        "top-16, 1 initial + 2 recent blocks pinned",
+            "batch": B, "seq_len": int(inp.seq_lens[0]), "index_heads": 4, "head_dim": 128,
+            "block_tokens": 128, "topk": topk, "n_init": n_init, "n_local": n_local,
+            "num_splits": splits, "engine": engine, "index_k_bytes": nbytes,
+        },
+        "roofline": {
+            "kernel": "split_kernel (stage 1: block scores + per-split top-16)",
+            "bound": "hbm",
+            "achieved": round(k_gbs, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(k_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel_us": round(k_ms * 1e3, 2),
+            "algorithmic_bytes_per_launch": nbytes,
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on the same workload")
+        out["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

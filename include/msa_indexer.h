@@ -1,0 +1,181 @@
+/*
+ * msa_indexer.h -- C ABI of the MI355X (gfx950) MiniMax-M3 lightning-indexer decode pass.
+ *
+ * The pass, for each decode row b (one decode token) and each of the 4 index heads h:
+ *   1. scores every 128-token block j of the row's paged bf16 index-K cache as
+ *      S[b][h][j] = max over the block's valid tokens t of sum_d q[b][h][d] * k[t][d],
+ *      accumulated in fp32, with no scale applied;
+ *   2. selects the top `topk` blocks, with the first `n_init` blocks and the last
+ *      `n_local` blocks of the row always selected (pinned).
+ * Sources:
+ *   - vLLM PR #57832 "context-parallel decode scoring for MiniMax-M3's sparse lightning
+ *     indexer on ROCm": Problem (one index-K head shared by the 4 index heads, every
+ *     block of the context scored), Solution (per-head top-k, packed int64 (score, block
+ *     id) keys, exact merge of per-shard top-k, pinned init/sink and sliding-window
+ *     blocks), CUDA graph capture (shapes from a bound, block counts and strides as
+ *     runtime arguments, chunks past a row's end return at once).
+ *   - SGLang PR #41488 "[AMD] Add opt-in MiniMax-M3 TP4 indexer context partitioning":
+ *     Modifications (4 heads, dim 128, 128-token blocks, max scoring, top-16, initial /
+ *     recent block priorities, every K tile scored for all heads while resident, 16
+ *     candidates kept per shard).
+ *   - TensorRT-LLM PR #17008 "MiniMax-M3 MSA: split the KV axis for the decode indexer
+ *     proxy": Description and Changes (full-context max-score pass; split-KV to shorten
+ *     the per-workgroup serial tile chain), Accuracy (each split's max seeded at -inf,
+ *     so splitting the KV axis cannot change a score).
+ *   - vLLM blog "Following the Bottleneck: Optimizing MiniMax M3 on AMD Instinct MI355X",
+ *     section 2 (no positive score scale: it cannot change top-k order).
+ *
+ * Conventions for every entry point:
+ *   - Pointers named q, k_cache, block_table, seq_lens, out_*, workspace are DEVICE
+ *     pointers (hipMalloc'd memory of the current device). The caller owns every buffer;
+ *     the library never allocates or frees memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). All work is
+ *     enqueued on it and the call returns without synchronizing. Errors found on the
+ *     device surface at the caller's next synchronization or through the workspace's
+ *     error word (msa_indexer_read_error).
+ *   - Grid and workspace sizes depend only on (batch, max_blocks_per_seq, topk,
+ *     num_splits), never on seq_lens or block_table contents, so a call can be captured
+ *     once in a HIP graph and replayed after seq_lens / block_table change on device.
+ *   - Argument checks run on the host before any HIP call; a failed check returns a
+ *     negative status and enqueues nothing. Nothing aborts.
+ *   - Concurrent calls that share a workspace on one device race; give each stream its own.
+ */
+#ifndef MSA_INDEXER_H
+#define MSA_INDEXER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define MSA_OK 0
+#define MSA_ERR_INVALID_ARG (-1)         /* null/misaligned pointer, bad size or parameter */
+#define MSA_ERR_WORKSPACE_TOO_SMALL (-2) /* workspace_bytes < msa_indexer_workspace_bytes(...) */
+#define MSA_ERR_UNSUPPORTED (-3)         /* shape beyond what this build handles */
+#define MSA_ERR_HIP (-4)                 /* the HIP runtime refused a launch */
+
+/* Fixed model geometry (SGLang PR #41488, Modifications). */
+#define MSA_INDEX_HEADS 4
+#define MSA_HEAD_DIM 128
+#define MSA_BLOCK_TOKENS 128
+
+/* Limits of this build. */
+#define MSA_MAX_TOPK 64
+#define MSA_MAX_BLOCKS_PER_SEQ 16384     /* 2M tokens per row */
+
+/* Block-scoring engines (msa_indexer_split_topk / msa_indexer_block_scores). */
+#define MSA_ENGINE_DEFAULT 0
+#define MSA_ENGINE_VALU 1                /* bf16 dot2 instructions + in-row DPP sums */
+#define MSA_ENGINE_MFMA 2                /* v_mfma_f32_16x16x32_bf16, heads padded to 16 */
+
+/* Device error bits, OR-ed into the workspace's error word by the kernels. */
+#define MSA_DEVERR_PAGE_OUT_OF_RANGE 1u  /* a needed block_table entry was outside [0, num_pages) */
+
+/* Human-readable text for a status code. Never NULL. */
+const char *msa_status_string(int32_t status);
+
+/*
+ * Number of KV splits S a call uses: num_splits > 0 asks for that many (the library
+ * may use fewer so that no split is empty by construction); 0 picks S from batch and
+ * max_blocks_per_seq. Returns a negative status on invalid arguments.
+ * Split s of row b owns logical blocks [s*C, min((s+1)*C, nb_b)), C = ceil(W/S)
+ * (TensorRT-LLM PR #17008, Changes: split the KV axis into contiguous tile ranges).
+ */
+int32_t msa_indexer_num_splits(int32_t batch, int32_t max_blocks_per_seq, int32_t topk,
+                               int32_t num_splits);
+
+/*
+ * Workspace bytes a call with these arguments needs (0 on invalid arguments).
+ * Layout: a 256-byte header whose first uint32 is the device error word, then the
+ * per-split candidate keys, uint64 [batch][S][4][topk].
+ */
+size_t msa_indexer_workspace_bytes(int32_t batch, int32_t max_blocks_per_seq, int32_t topk,
+                                   int32_t num_splits);
+
+/*
+ * The whole decode pass: block scores, per-split top-k, exact merge.
+ *
+ *   q            bf16 [batch][4][128], contiguous, 16-byte aligned: post-RoPE index queries,
+ *                one decode token per row.
+ *   k_cache      bf16 [num_pages][128 tokens][128 dims], contiguous, 16-byte aligned:
+ *                the shared single-head index-K cache, one logical block per page.
+ *   block_table  int32 [batch][bt_stride]: logical block j of row b lives in page
+ *                block_table[b*bt_stride + j]. Only entries j < nb_b are read; each must
+ *                lie in [0, num_pages). An entry outside is never dereferenced: its block
+ *                scores -inf and the workspace error word gets MSA_DEVERR_PAGE_OUT_OF_RANGE.
+ *   seq_lens     int32 [batch]: context tokens of row b (the decode token included).
+ *                Values are clamped to [0, max_blocks_per_seq*128]; nb_b = ceil(len/128).
+ *   batch >= 0 (0 is a successful no-op), 0 <= max_blocks_per_seq <= MSA_MAX_BLOCKS_PER_SEQ,
+ *   bt_stride >= max_blocks_per_seq, num_pages >= 0.
+ *   topk in [1, MSA_MAX_TOPK]; n_init, n_local >= 0 and n_init + n_local <= topk.
+ *     Pinned blocks of row b: j < n_init and j >= nb_b - n_local (whole blocks; a partial
+ *     last block counts). They are selected first, in score order.
+ *   out_ids      int32 [batch][4][topk]: selected logical block ids of (b, h), in order
+ *                (pinned first, then higher score, then lower id); slots past
+ *                m = min(topk, nb_b) hold -1.
+ *   out_scores   fp32 [batch][4][topk]: the selected blocks' scores (-0.0 reads as +0.0);
+ *                slots past m hold -inf.
+ *   workspace    device memory of at least msa_indexer_workspace_bytes(...) bytes, 256-byte
+ *                aligned. Its error word must be zero before the first call (clear it once,
+ *                e.g. with hipMemset); the library only ever ORs bits into it.
+ *   num_splits   0 = automatic; see msa_indexer_num_splits.
+ */
+int32_t msa_indexer_decode(const void *q, const void *k_cache, const int32_t *block_table,
+                           const int32_t *seq_lens, int32_t batch, int32_t max_blocks_per_seq,
+                           int32_t bt_stride, int64_t num_pages, int32_t topk, int32_t n_init,
+                           int32_t n_local, int32_t *out_ids, float *out_scores, void *workspace,
+                           size_t workspace_bytes, int32_t num_splits, void *stream);
+
+/*
+ * Stage 1 of msa_indexer_decode alone: one workgroup per (row, split) scores its blocks
+ * for all 4 heads from a single read of each page and writes each head's top-topk
+ * candidate keys of the split into the workspace. `engine` picks the scoring
+ * instructions (MSA_ENGINE_*). Other arguments as in msa_indexer_decode.
+ * Key layout (vLLM PR #57832, Solution step 3: one sortable int64 per candidate):
+ *   bit 63 pinned | bits 62..31 order-preserving image of the fp32 score | bits 30..0
+ *   (2^31-1 - block id); keys compare as unsigned integers, larger is better.
+ */
+int32_t msa_indexer_split_topk(const void *q, const void *k_cache, const int32_t *block_table,
+                               const int32_t *seq_lens, int32_t batch,
+                               int32_t max_blocks_per_seq, int32_t bt_stride, int64_t num_pages,
+                               int32_t topk, int32_t n_init, int32_t n_local, void *workspace,
+                               size_t workspace_bytes, int32_t num_splits, int32_t engine,
+                               void *stream);
+
+/*
+ * Stage 2 of msa_indexer_decode alone: per (row, head), the exact top-min(topk, nb_b) of
+ * the union of the splits' candidates, decoded into out_ids / out_scores. Exact because a
+ * block in the global top-k is in the top-k of its own split (vLLM PR #57832, Solution;
+ * SGLang PR #41488, Modifications). Arguments as in msa_indexer_decode; the workspace
+ * must hold stage 1's keys for the same (batch, max_blocks_per_seq, topk, num_splits).
+ */
+int32_t msa_indexer_merge(const int32_t *seq_lens, int32_t batch, int32_t max_blocks_per_seq,
+                          int32_t topk, int32_t *out_ids, float *out_scores,
+                          const void *workspace, size_t workspace_bytes, int32_t num_splits,
+                          void *stream);
+
+/*
+ * Test and debugging aid: the full block-score matrix out[b][h][j], fp32
+ * [batch][4][max_blocks_per_seq], -inf for j >= nb_b and for blocks whose page is out of
+ * range. Uses the same scoring code as stage 1. num_splits and engine as above.
+ */
+int32_t msa_indexer_block_scores(const void *q, const void *k_cache, const int32_t *block_table,
+                                 const int32_t *seq_lens, int32_t batch,
+                                 int32_t max_blocks_per_seq, int32_t bt_stride,
+                                 int64_t num_pages, float *out, int32_t num_splits,
+                                 int32_t engine, void *stream);
+
+/*
+ * Copies the workspace's device error word to *host_flags after synchronizing `stream`,
+ * then clears it on the device. Returns MSA_ERR_HIP if a HIP call fails.
+ */
+int32_t msa_indexer_read_error(void *workspace, uint32_t *host_flags, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSA_INDEXER_H */

@@ -1,0 +1,22 @@
+"""MI355X-native MiniMax-M3 lightning-indexer decode pass.
+
+The pass runs in hand-written HIP kernels for gfx950 behind the C ABI in
+include/msa_indexer.h; this package holds the thin ctypes binding (same names as
+the C entry points), the in-tree build, and the seeded input generators.
+"""
+from ._lib import (  # noqa: F401
+    ENGINE_DEFAULT,
+    ENGINE_MFMA,
+    ENGINE_VALU,
+    MsaError,
+    load,
+    msa_indexer_block_scores,
+    msa_indexer_decode,
+    msa_indexer_merge,
+    msa_indexer_read_error,
+    msa_indexer_split_topk,
+    new_workspace,
+    num_splits,
+    status_string,
+    workspace_bytes,
+)

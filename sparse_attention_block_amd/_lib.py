@@ -1,0 +1,223 @@
+"""ctypes binding of libmsa_indexer.so (include/msa_indexer.h).
+
+Argument marshalling only: every step of the pass runs in the library's HIP kernels.
+PyTorch supplies device memory and the current stream. There is no fallback: if the
+library is missing, or a tensor is not a suitable device tensor, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+from .build import HERE, INCLUDE, library_path
+
+MSA_OK = 0
+MSA_ERR_INVALID_ARG = -1
+MSA_ERR_WORKSPACE_TOO_SMALL = -2
+MSA_ERR_UNSUPPORTED = -3
+MSA_ERR_HIP = -4
+
+ENGINE_DEFAULT = 0
+ENGINE_VALU = 1
+ENGINE_MFMA = 2
+
+DEVERR_PAGE_OUT_OF_RANGE = 1
+
+HEADS = 4
+DIM = 128
+BLOCK = 128
+MAX_TOPK = 64
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+
+_SIGNATURES = {
+    "msa_status_string": ([_I32], ctypes.c_char_p),
+    "msa_indexer_num_splits": ([_I32, _I32, _I32, _I32], _I32),
+    "msa_indexer_workspace_bytes": ([_I32, _I32, _I32, _I32], _SZ),
+    "msa_indexer_decode": ([_P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32, _I32, _P, _P, _P,
+                            _SZ, _I32, _P], _I32),
+    "msa_indexer_split_topk": ([_P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32, _I32, _P, _SZ,
+                                _I32, _I32, _P], _I32),
+    "msa_indexer_merge": ([_P, _I32, _I32, _I32, _P, _P, _P, _SZ, _I32, _P], _I32),
+    "msa_indexer_block_scores": ([_P, _P, _P, _P, _I32, _I32, _I32, _I64, _P, _I32, _I32, _P],
+                                 _I32),
+    "msa_indexer_read_error": ([_P, _P, _P], _I32),
+}
+
+_lib = None
+
+
+class MsaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} returned {status} ({status_string(status)})")
+        self.status = status
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/msa_indexer.h declares."""
+    text = open(os.path.join(INCLUDE, "msa_indexer.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"\b(msa_\w+)\s*\(", text)
+
+
+def load(path: str | None = None):
+    """Loads the built library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    path = path or library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with sparse_attention_block_amd.build.build() "
+                           "(or __graft_entry__.build()); there is no non-HIP fallback")
+    lib = ctypes.CDLL(path)
+    for name, (args, res) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    if path == library_path():
+        _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().msa_status_string(status).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != MSA_OK:
+        raise MsaError(fn, status)
+
+
+def num_splits(batch: int, max_blocks: int, topk: int, splits: int = 0) -> int:
+    s = load().msa_indexer_num_splits(batch, max_blocks, topk, splits)
+    _check("msa_indexer_num_splits", min(s, 0))
+    return s
+
+
+def workspace_bytes(batch: int, max_blocks: int, topk: int, splits: int = 0) -> int:
+    return int(load().msa_indexer_workspace_bytes(batch, max_blocks, topk, splits))
+
+
+# ---------------------------------------------------------------------------
+# Tensor marshalling.
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dev(t, name, dtype, shape=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    return _P(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return _P(s.cuda_stream)
+
+
+def _inputs(q, k_cache, block_table, seq_lens):
+    torch = _torch()
+    B = q.shape[0]
+    if q.dim() != 3 or tuple(q.shape[1:]) != (HEADS, DIM):
+        raise ValueError("q: expected [batch, 4, 128]")
+    if k_cache.dim() != 3 or tuple(k_cache.shape[1:]) != (BLOCK, DIM):
+        raise ValueError("k_cache: expected [pages, 128, 128]")
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table: expected [batch, max_blocks]")
+    ptrs = (_dev(q, "q", torch.bfloat16), _dev(k_cache, "k_cache", torch.bfloat16),
+            _dev(block_table, "block_table", torch.int32),
+            _dev(seq_lens, "seq_lens", torch.int32, (B,)))
+    return ptrs, B, block_table.shape[1], block_table.stride(0), k_cache.shape[0]
+
+
+def new_workspace(batch: int, max_blocks: int, topk: int, splits: int = 0, device="cuda"):
+    """A zeroed workspace tensor (uint8) of the size the library asks for."""
+    torch = _torch()
+    n = workspace_bytes(batch, max_blocks, topk, splits)
+    if n == 0:
+        raise ValueError("invalid arguments for a workspace")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def msa_indexer_decode(q, k_cache, block_table, seq_lens, topk=16, n_init=1, n_local=2,
+                       out_ids=None, out_scores=None, workspace=None, num_splits=0, stream=None):
+    """The decode pass. Returns (out_ids int32 [B,4,topk], out_scores fp32 [B,4,topk])."""
+    torch = _torch()
+    (pq, pk, pbt, pl), B, W, stride, pages = _inputs(q, k_cache, block_table, seq_lens)
+    if out_ids is None:
+        out_ids = torch.empty((B, HEADS, topk), dtype=torch.int32, device=q.device)
+    if out_scores is None:
+        out_scores = torch.empty((B, HEADS, topk), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = new_workspace(B, W, topk, num_splits, q.device)
+    rc = load().msa_indexer_decode(
+        pq, pk, pbt, pl, B, W, stride, pages, topk, n_init, n_local,
+        _dev(out_ids, "out_ids", torch.int32, (B, HEADS, topk)),
+        _dev(out_scores, "out_scores", torch.float32, (B, HEADS, topk)),
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(), num_splits, _stream(stream))
+    _check("msa_indexer_decode", rc)
+    return out_ids, out_scores
+
+
+def msa_indexer_split_topk(q, k_cache, block_table, seq_lens, workspace, topk=16, n_init=1,
+                           n_local=2, num_splits=0, engine=ENGINE_DEFAULT, stream=None):
+    """Stage 1 alone: per-split top-k candidate keys into `workspace`."""
+    torch = _torch()
+    (pq, pk, pbt, pl), B, W, stride, pages = _inputs(q, k_cache, block_table, seq_lens)
+    rc = load().msa_indexer_split_topk(pq, pk, pbt, pl, B, W, stride, pages, topk, n_init, n_local,
+                                       _dev(workspace, "workspace", torch.uint8), workspace.numel(),
+                                       num_splits, engine, _stream(stream))
+    _check("msa_indexer_split_topk", rc)
+
+
+def msa_indexer_merge(seq_lens, max_blocks, workspace, out_ids, out_scores, topk=16,
+                      num_splits=0, stream=None):
+    """Stage 2 alone: exact merge of the split candidates into out_ids / out_scores."""
+    torch = _torch()
+    B = seq_lens.shape[0]
+    rc = load().msa_indexer_merge(_dev(seq_lens, "seq_lens", torch.int32, (B,)), B, max_blocks, topk,
+                                  _dev(out_ids, "out_ids", torch.int32, (B, HEADS, topk)),
+                                  _dev(out_scores, "out_scores", torch.float32, (B, HEADS, topk)),
+                                  _dev(workspace, "workspace", torch.uint8), workspace.numel(),
+                                  num_splits, _stream(stream))
+    _check("msa_indexer_merge", rc)
+
+
+def msa_indexer_block_scores(q, k_cache, block_table, seq_lens, num_splits=0,
+                             engine=ENGINE_DEFAULT, out=None, stream=None):
+    """fp32 block scores [B, 4, W]; -inf past each row's end."""
+    torch = _torch()
+    (pq, pk, pbt, pl), B, W, stride, pages = _inputs(q, k_cache, block_table, seq_lens)
+    if out is None:
+        out = torch.empty((B, HEADS, W), dtype=torch.float32, device=q.device)
+    rc = load().msa_indexer_block_scores(pq, pk, pbt, pl, B, W, stride, pages,
+                                         _dev(out, "out", torch.float32, (B, HEADS, W)),
+                                         num_splits, engine, _stream(stream))
+    _check("msa_indexer_block_scores", rc)
+    return out
+
+
+def msa_indexer_read_error(workspace, stream=None) -> int:
+    """Device error bits of `workspace` (synchronizes the stream, then clears them)."""
+    torch = _torch()
+    flags = ctypes.c_uint32(0)
+    rc = load().msa_indexer_read_error(_dev(workspace, "workspace", torch.uint8),
+                                       ctypes.byref(flags), _stream(stream))
+    _check("msa_indexer_read_error", rc)
+    return int(flags.value)

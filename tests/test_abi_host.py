@@ -1,0 +1,147 @@
+"""The C ABI without a GPU: the library loads, exports what the header declares, and
+rejects bad arguments on the host before any HIP call (vLLM PR #57832, Test Result:
+unsupported configurations fail at startup instead of running)."""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+from sparse_attention_block_amd import _lib
+from sparse_attention_block_amd.build import library_path
+
+OK, INVALID, WS_SMALL, UNSUPPORTED = 0, -1, -2, -3
+
+# Aligned, never-dereferenced stand-ins for device pointers: every call below must be
+# refused by the host-side checks, so nothing ever reaches the device.
+FAKE = 1 << 20
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(library_path()):
+        from sparse_attention_block_amd.build import build
+        build()
+    return _lib.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _lib.header_functions()
+    assert len(declared) >= 8
+    out = subprocess.run(["nm", "-D", "--defined-only", library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in declared:
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_status_strings(lib):
+    for code in (OK, INVALID, WS_SMALL, UNSUPPORTED, -4):
+        assert lib.msa_status_string(code)
+    assert lib.msa_status_string(123) == b"unknown status"
+
+
+def test_split_plan(lib):
+    ns = lib.msa_indexer_num_splits
+    # Automatic plan: about batch*W/1024 blocks per split, between 4 and 64.
+    assert ns(32, 1024, 16, 0) == 32
+    assert ns(1, 64, 16, 0) == 16
+    assert ns(16, 68, 16, 0) == 17
+    # Requested counts are honoured up to empty trailing splits.
+    assert ns(16, 68, 16, 4) == 4
+    assert ns(16, 68, 16, 60) == 34
+    assert ns(1, 1024, 16, 1024) == 256            # at most 256 splits per row
+    assert ns(1, 1024, 64, 0) == 64                # S * topk <= 4096
+    assert ns(1, 0, 16, 0) == 1
+    assert ns(1, 16385, 16, 0) == UNSUPPORTED
+    assert ns(1, 8192, 64, 0) == UNSUPPORTED       # 128 blocks per split needed
+    assert ns(-1, 8, 16, 0) == INVALID
+    assert ns(1, 8, 0, 0) == INVALID and ns(1, 8, 65, 0) == INVALID
+    assert ns(1, 8, 16, -1) == INVALID
+
+
+def test_workspace_size(lib):
+    ws = lib.msa_indexer_workspace_bytes
+    assert ws(32, 1024, 16, 0) == 256 + 32 * 32 * 4 * 16 * 8
+    assert ws(0, 1024, 16, 0) == 256
+    assert ws(1, 8, 0, 0) == 0
+
+
+def _decode(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, bt=FAKE, lens=FAKE, batch=2, W=8, stride=8, pages=16, topk=16,
+             n_init=1, n_local=2, ids=FAKE, scores=FAKE, ws=FAKE, ws_bytes=1 << 20, splits=0,
+             stream=None)
+    a.update(kw)
+    return lib.msa_indexer_decode(a["q"], a["k"], a["bt"], a["lens"], a["batch"], a["W"],
+                                  a["stride"], a["pages"], a["topk"], a["n_init"], a["n_local"],
+                                  a["ids"], a["scores"], a["ws"], a["ws_bytes"], a["splits"],
+                                  a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INVALID),
+    (dict(k=None), INVALID),
+    (dict(bt=None), INVALID),
+    (dict(lens=None), INVALID),
+    (dict(ids=None), INVALID),
+    (dict(scores=None), INVALID),
+    (dict(ws=None), INVALID),
+    (dict(q=FAKE + 8), INVALID),            # 16-byte alignment of q
+    (dict(k=FAKE + 2), INVALID),            # 16-byte alignment of the cache
+    (dict(ws=FAKE + 64), INVALID),          # 256-byte alignment of the workspace
+    (dict(ids=FAKE + 2), INVALID),
+    (dict(batch=-1), INVALID),
+    (dict(W=-1), INVALID),
+    (dict(stride=7), INVALID),              # stride below the table width
+    (dict(pages=-1), INVALID),
+    (dict(topk=0), INVALID),
+    (dict(topk=65), INVALID),
+    (dict(n_init=-1), INVALID),
+    (dict(n_local=-1), INVALID),
+    (dict(n_init=10, n_local=7), INVALID),  # pins exceed topk
+    (dict(splits=-3), INVALID),
+    (dict(W=16385, stride=16385), UNSUPPORTED),
+    (dict(ws_bytes=255), WS_SMALL),
+])
+def test_decode_rejects_on_host(lib, kw, code):
+    assert _decode(lib, **kw) == code
+
+
+def test_batch_zero_is_a_no_op(lib):
+    assert _decode(lib, batch=0, q=None, k=None, bt=None, lens=None, ids=None, scores=None,
+                   ws=None, ws_bytes=0) == OK
+
+
+def test_stage_entry_points_reject_on_host(lib):
+    st = lib.msa_indexer_split_topk(FAKE, FAKE, FAKE, FAKE, 2, 8, 8, 16, 16, 1, 2, FAKE, 1 << 20,
+                                    0, 7, None)
+    assert st == INVALID                     # unknown engine
+    st = lib.msa_indexer_split_topk(FAKE, FAKE, FAKE, FAKE, 2, 8, 8, 16, 16, 1, 2, FAKE, 100, 0, 1,
+                                    None)
+    assert st == WS_SMALL
+    mg = lib.msa_indexer_merge(FAKE, 2, 8, 16, None, FAKE, FAKE, 1 << 20, 0, None)
+    assert mg == INVALID
+    mg = lib.msa_indexer_merge(FAKE, 2, 8, 16, FAKE, FAKE, FAKE, 8, 0, None)
+    assert mg == WS_SMALL
+    bs = lib.msa_indexer_block_scores(FAKE, FAKE, FAKE, FAKE, 2, 8, 8, 16, None, 0, 0, None)
+    assert bs == INVALID
+    bs = lib.msa_indexer_block_scores(FAKE, FAKE, FAKE, FAKE, 2, 8, 8, 16, FAKE, 0, 3, None)
+    assert bs == INVALID
+    assert lib.msa_indexer_read_error(None, ctypes.byref(ctypes.c_uint32()), None) == INVALID
+
+
+def test_binding_refuses_host_tensors():
+    torch = pytest.importorskip("torch")
+    from sparse_attention_block_amd import msa_indexer_decode
+    q = torch.zeros((1, 4, 128), dtype=torch.bfloat16)
+    k = torch.zeros((1, 128, 128), dtype=torch.bfloat16)
+    bt = torch.zeros((1, 1), dtype=torch.int32)
+    lens = torch.zeros((1,), dtype=torch.int32)
+    with pytest.raises((ValueError, RuntimeError, AssertionError)):
+        msa_indexer_decode(q, k, bt, lens, workspace=torch.zeros(1024, dtype=torch.uint8))
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(RuntimeError, match="no non-HIP fallback"):
+        _lib.load(str(tmp_path / "absent.so"))
