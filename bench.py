@@ -116,23 +116,32 @@ def main() -> int:
     k = torch.from_numpy(inp.k_cache.view(np.int16)).to(dev).view(torch.bfloat16)
     bt = torch.from_numpy(inp.block_table).to(dev)
     lens = torch.from_numpy(inp.seq_lens).to(dev)
-    splits = msa.num_splits(B, W, topk, args.splits)
+    plan = msa.plan(B, W, topk, args.splits)
+    splits = plan["splits"]
     ws = msa.new_workspace(B, W, topk, args.splits, dev)
     ids = torch.empty((B, 4, topk), dtype=torch.int32, device=dev)
     sc = torch.empty((B, 4, topk), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
-    log(f"inputs resident in HBM; {splits} splits per row, engine {args.engine}")
+    log(f"inputs resident in HBM; plan {plan}, engine {args.engine}")
 
     stream = torch.cuda.current_stream()
+    engine_arg = args.engine if args.engine else None
 
     def step(ev0=None, ev1=None):
+        # A fused plan is one kernel launch per step (the last split of each row merges
+        # it); otherwise stage 1 is timed alone and stage 2 follows it.
         if ev0 is not None:
             ev0.record(stream)
-        msa.msa_indexer_split_topk(q, k, bt, lens, ws, topk, n_init, n_local,
-                                   num_splits=args.splits, engine=args.engine)
+        if plan["fused"]:
+            msa.msa_indexer_decode(q, k, bt, lens, topk, n_init, n_local, out_ids=ids, out_scores=sc,
+                                   workspace=ws, num_splits=args.splits, engine=engine_arg)
+        else:
+            msa.msa_indexer_split_topk(q, k, bt, lens, ws, topk, n_init, n_local,
+                                       num_splits=args.splits, engine=args.engine)
         if ev1 is not None:
             ev1.record(stream)
-        msa.msa_indexer_merge(lens, W, ws, ids, sc, topk, num_splits=args.splits)
+        if not plan["fused"]:
+            msa.msa_indexer_merge(lens, W, ws, ids, sc, topk, num_splits=args.splits)
 
     for _ in range(args.warmup):
         step()
@@ -181,10 +190,13 @@ def main() -> int:
                         "top-16, 1 initial + 2 recent blocks pinned",
             "batch": B, "seq_len": int(inp.seq_lens[0]), "index_heads": 4, "head_dim": 128,
             "block_tokens": 128, "topk": topk, "n_init": n_init, "n_local": n_local,
-            "num_splits": splits, "engine": engine, "index_k_bytes": nbytes,
+            "num_splits": splits, "blocks_per_split": plan["blocks_per_split"],
+            "fused_merge": plan["fused"], "engine": engine, "index_k_bytes": nbytes,
         },
         "roofline": {
-            "kernel": "split_kernel (stage 1: block scores + per-split top-16)",
+            "kernel": ("split_kernel, fused: block scores + per-split top-16 + merge by each row's "
+                       "last split (the whole step)") if plan["fused"] else
+                      "split_kernel (stage 1: block scores + per-split top-16)",
             "bound": "hbm",
             "achieved": round(k_gbs, 2),
             "peak": HBM_PEAK_GBS,

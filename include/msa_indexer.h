@@ -67,7 +67,7 @@ extern "C" {
 #define MSA_MAX_BLOCKS_PER_SEQ 16384     /* 2M tokens per row */
 
 /* Block-scoring engines (msa_indexer_split_topk / msa_indexer_block_scores). */
-#define MSA_ENGINE_DEFAULT 0
+#define MSA_ENGINE_DEFAULT 0                /* the VALU engine */
 #define MSA_ENGINE_VALU 1                /* bf16 dot2 instructions + in-row DPP sums */
 #define MSA_ENGINE_MFMA 2                /* v_mfma_f32_16x16x32_bf16, heads padded to 16 */
 
@@ -88,9 +88,24 @@ int32_t msa_indexer_num_splits(int32_t batch, int32_t max_blocks_per_seq, int32_
                                int32_t num_splits);
 
 /*
+ * The plan a call with these arguments uses: S splits per row, C blocks per split, Lk =
+ * min(topk, C) candidates kept per (split, head), and whether the merge runs inside the
+ * split kernel (fused: one launch) or as a second launch. Any output pointer may be NULL.
+ * Returns MSA_OK or a negative status.
+ */
+int32_t msa_indexer_plan(int32_t batch, int32_t max_blocks_per_seq, int32_t topk, int32_t num_splits,
+                         int32_t *splits, int32_t *blocks_per_split, int32_t *candidates_per_split,
+                         int32_t *fused);
+
+/*
  * Workspace bytes a call with these arguments needs (0 on invalid arguments).
- * Layout: a 256-byte header whose first uint32 is the device error word, then the
- * per-split candidate keys, uint64 [batch][S][4][topk].
+ * Layout: a 256-byte header whose first uint32 is the device error word and whose next
+ * `batch` uint32 (spilling past 256 bytes for large batches) are per-row counters of
+ * finished splits, padded to a 256-byte boundary; then the per-split candidate keys,
+ * uint64 [batch][S][4][Lk]. The whole workspace must be zero before its first use (e.g.
+ * hipMemset once after allocation). The library leaves the counters at zero at the end of
+ * every call, so the same workspace can be reused, and replayed in a graph, without
+ * clearing it again; the error word only ever gains bits (msa_indexer_read_error clears it).
  */
 size_t msa_indexer_workspace_bytes(int32_t batch, int32_t max_blocks_per_seq, int32_t topk,
                                    int32_t num_splits);
@@ -119,9 +134,10 @@ size_t msa_indexer_workspace_bytes(int32_t batch, int32_t max_blocks_per_seq, in
  *   out_scores   fp32 [batch][4][topk]: the selected blocks' scores (-0.0 reads as +0.0);
  *                slots past m hold -inf.
  *   workspace    device memory of at least msa_indexer_workspace_bytes(...) bytes, 256-byte
- *                aligned. Its error word must be zero before the first call (clear it once,
- *                e.g. with hipMemset); the library only ever ORs bits into it.
+ *                aligned, zeroed once before its first use (see msa_indexer_workspace_bytes).
  *   num_splits   0 = automatic; see msa_indexer_num_splits.
+ * When the plan is fused (msa_indexer_plan) this is one kernel launch: the last split of
+ * each row to finish merges the row. Otherwise stage 1 and stage 2 are two launches.
  */
 int32_t msa_indexer_decode(const void *q, const void *k_cache, const int32_t *block_table,
                            const int32_t *seq_lens, int32_t batch, int32_t max_blocks_per_seq,
@@ -130,9 +146,21 @@ int32_t msa_indexer_decode(const void *q, const void *k_cache, const int32_t *bl
                            size_t workspace_bytes, int32_t num_splits, void *stream);
 
 /*
- * Stage 1 of msa_indexer_decode alone: one workgroup per (row, split) scores its blocks
- * for all 4 heads from a single read of each page and writes each head's top-topk
- * candidate keys of the split into the workspace. `engine` picks the scoring
+ * msa_indexer_decode with an explicit scoring engine (MSA_ENGINE_*): for measuring the
+ * engines against each other on the whole pass. msa_indexer_decode uses MSA_ENGINE_DEFAULT,
+ * which is the VALU engine (faster on MI355X, where the pass is bound by HBM bandwidth).
+ */
+int32_t msa_indexer_decode_engine(const void *q, const void *k_cache, const int32_t *block_table,
+                                  const int32_t *seq_lens, int32_t batch,
+                                  int32_t max_blocks_per_seq, int32_t bt_stride, int64_t num_pages,
+                                  int32_t topk, int32_t n_init, int32_t n_local, int32_t *out_ids,
+                                  float *out_scores, void *workspace, size_t workspace_bytes,
+                                  int32_t num_splits, int32_t engine, void *stream);
+
+/*
+ * Stage 1 of msa_indexer_decode alone (never fused): one workgroup per (row, split) scores its blocks
+ * for all 4 heads from a single read of each page and writes each head's top-Lk
+ * (Lk = min(topk, C)) candidate keys of the split, best first, into the workspace. `engine` picks the scoring
  * instructions (MSA_ENGINE_*). Other arguments as in msa_indexer_decode.
  * Key layout (vLLM PR #57832, Solution step 3: one sortable int64 per candidate):
  *   bit 63 pinned | bits 62..31 order-preserving image of the fp32 score | bits 30..0

@@ -17,6 +17,7 @@ from ._lib import (  # noqa: F401
     msa_indexer_split_topk,
     new_workspace,
     num_splits,
+    plan,
     status_string,
     workspace_bytes,
 )

@@ -38,8 +38,11 @@ _SIGNATURES = {
     "msa_status_string": ([_I32], ctypes.c_char_p),
     "msa_indexer_num_splits": ([_I32, _I32, _I32, _I32], _I32),
     "msa_indexer_workspace_bytes": ([_I32, _I32, _I32, _I32], _SZ),
+    "msa_indexer_plan": ([_I32, _I32, _I32, _I32, _P, _P, _P, _P], _I32),
     "msa_indexer_decode": ([_P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32, _I32, _P, _P, _P,
                             _SZ, _I32, _P], _I32),
+    "msa_indexer_decode_engine": ([_P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32, _I32, _P, _P,
+                                   _P, _SZ, _I32, _I32, _P], _I32),
     "msa_indexer_split_topk": ([_P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32, _I32, _P, _SZ,
                                 _I32, _I32, _P], _I32),
     "msa_indexer_merge": ([_P, _I32, _I32, _I32, _P, _P, _P, _SZ, _I32, _P], _I32),
@@ -96,6 +99,15 @@ def num_splits(batch: int, max_blocks: int, topk: int, splits: int = 0) -> int:
     s = load().msa_indexer_num_splits(batch, max_blocks, topk, splits)
     _check("msa_indexer_num_splits", min(s, 0))
     return s
+
+
+def plan(batch: int, max_blocks: int, topk: int, splits: int = 0) -> dict:
+    """The library's plan: splits per row, blocks per split, candidates kept, fused merge."""
+    out = [ctypes.c_int32() for _ in range(4)]
+    rc = load().msa_indexer_plan(batch, max_blocks, topk, splits, *[ctypes.byref(o) for o in out])
+    _check("msa_indexer_plan", rc)
+    return {"splits": out[0].value, "blocks_per_split": out[1].value,
+            "candidates_per_split": out[2].value, "fused": bool(out[3].value)}
 
 
 def workspace_bytes(batch: int, max_blocks: int, topk: int, splits: int = 0) -> int:
@@ -156,8 +168,10 @@ def new_workspace(batch: int, max_blocks: int, topk: int, splits: int = 0, devic
 
 
 def msa_indexer_decode(q, k_cache, block_table, seq_lens, topk=16, n_init=1, n_local=2,
-                       out_ids=None, out_scores=None, workspace=None, num_splits=0, stream=None):
-    """The decode pass. Returns (out_ids int32 [B,4,topk], out_scores fp32 [B,4,topk])."""
+                       out_ids=None, out_scores=None, workspace=None, num_splits=0, stream=None,
+                       engine=None):
+    """The decode pass. Returns (out_ids int32 [B,4,topk], out_scores fp32 [B,4,topk]).
+    With `engine` set, calls msa_indexer_decode_engine instead."""
     torch = _torch()
     (pq, pk, pbt, pl), B, W, stride, pages = _inputs(q, k_cache, block_table, seq_lens)
     if out_ids is None:
@@ -166,12 +180,16 @@ def msa_indexer_decode(q, k_cache, block_table, seq_lens, topk=16, n_init=1, n_l
         out_scores = torch.empty((B, HEADS, topk), dtype=torch.float32, device=q.device)
     if workspace is None:
         workspace = new_workspace(B, W, topk, num_splits, q.device)
-    rc = load().msa_indexer_decode(
-        pq, pk, pbt, pl, B, W, stride, pages, topk, n_init, n_local,
-        _dev(out_ids, "out_ids", torch.int32, (B, HEADS, topk)),
-        _dev(out_scores, "out_scores", torch.float32, (B, HEADS, topk)),
-        _dev(workspace, "workspace", torch.uint8), workspace.numel(), num_splits, _stream(stream))
-    _check("msa_indexer_decode", rc)
+    args = [pq, pk, pbt, pl, B, W, stride, pages, topk, n_init, n_local,
+            _dev(out_ids, "out_ids", torch.int32, (B, HEADS, topk)),
+            _dev(out_scores, "out_scores", torch.float32, (B, HEADS, topk)),
+            _dev(workspace, "workspace", torch.uint8), workspace.numel(), num_splits]
+    if engine is None:
+        rc = load().msa_indexer_decode(*args, _stream(stream))
+        _check("msa_indexer_decode", rc)
+    else:
+        rc = load().msa_indexer_decode_engine(*args, engine, _stream(stream))
+        _check("msa_indexer_decode_engine", rc)
     return out_ids, out_scores
 
 

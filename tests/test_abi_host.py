@@ -52,7 +52,7 @@ def test_split_plan(lib):
     assert ns(16, 68, 16, 4) == 4
     assert ns(16, 68, 16, 60) == 34
     assert ns(1, 1024, 16, 1024) == 256            # at most 256 splits per row
-    assert ns(1, 1024, 64, 0) == 64                # S * topk <= 4096
+    assert ns(1, 1024, 64, 0) == 256               # 4-block splits keep 4 keys: S * Lk <= 4096
     assert ns(1, 0, 16, 0) == 1
     assert ns(1, 16385, 16, 0) == UNSUPPORTED
     assert ns(1, 8192, 64, 0) == UNSUPPORTED       # 128 blocks per split needed
@@ -63,9 +63,21 @@ def test_split_plan(lib):
 
 def test_workspace_size(lib):
     ws = lib.msa_indexer_workspace_bytes
-    assert ws(32, 1024, 16, 0) == 256 + 32 * 32 * 4 * 16 * 8
+    # error word (256 B), one 256-byte counter line per row, then the keys
+    assert ws(32, 1024, 16, 0) == 256 + 32 * 256 + 32 * 32 * 4 * 16 * 8
+    assert ws(16, 68, 16, 0) == 256 + 16 * 256 + 16 * 17 * 4 * 4 * 8   # 4-block splits keep 4 keys
     assert ws(0, 1024, 16, 0) == 256
     assert ws(1, 8, 0, 0) == 0
+
+
+def test_plan_fuses_the_merge_when_it_fits(lib):
+    from sparse_attention_block_amd import plan
+    assert plan(32, 1024, 16) == {"splits": 32, "blocks_per_split": 32,
+                                  "candidates_per_split": 16, "fused": True}
+    assert plan(1, 64, 16)["fused"] and plan(16, 68, 16)["fused"] and plan(8, 256, 16)["fused"]
+    assert plan(16, 1024, 16)["fused"]
+    big = plan(1, 16384, 16)          # 256 splits x 16 candidates: merged by a second kernel
+    assert big["splits"] == 256 and not big["fused"]
 
 
 def _decode(lib, **kw):

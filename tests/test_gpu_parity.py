@@ -219,3 +219,47 @@ def test_graph_replay_with_changing_lengths(msa):
         cur = synth.Inputs("replay", big.q, big.k_cache, perm, new_lens)
         ref = oracle.block_scores(cur.q, cur.k_cache, cur.block_table, cur.seq_lens)
         check_selection_vs_oracle(got_ids.cpu().numpy(), ref, new_lens, 16, 1, 2)
+
+
+def test_unfused_plan_parity(msa):
+    # Long rows at batch 2: 256 splits x 16 candidates per head do not fit the fused merge,
+    # so decode runs stage 1 and the separate merge kernel.
+    lens = [128 * 3000 + 65, 128 * 4096]
+    assert not msa.plan(2, 4096, 16)["fused"]
+    inp = synth.paged_case(110, lens, 4096)
+    ref = oracle.block_scores(inp.q, inp.k_cache, inp.block_table, inp.seq_lens)
+    run_case(msa, inp, ref, engine_list=[1], splits=(0,))
+
+
+def test_workspace_reuse_and_counter_reset(msa):
+    # One workspace across calls with changing lengths and split counts: the per-row
+    # counters must come back to zero after every fused call.
+    inp = synth.paged_case(111, [128 * 200] * 6, 200)
+    q, k, bt, lens = to_device(inp)
+    plans = [0, 4, 13, 50, 200, 7, 0, 25]
+    size = max(msa.workspace_bytes(6, 200, 16, ns) for ns in plans)
+    ws = torch.zeros(size, dtype=torch.uint8, device="cuda")
+    rng = np.random.default_rng(1)
+    for it, ns in enumerate(plans):
+        new_lens = rng.integers(0, 128 * 200 + 1, size=6).astype(np.int32)
+        new_lens[it % 6] = 0
+        lens.copy_(torch.from_numpy(new_lens))
+        ids, sc = msa.msa_indexer_decode(q, k, bt, lens, num_splits=ns, workspace=ws)
+        torch.cuda.synchronize()
+        counters = ws[4:4 + 4 * 6].view(torch.int32).cpu().numpy()
+        assert np.all(counters == 0), (it, counters)
+        cur = synth.Inputs("reuse", inp.q, inp.k_cache, inp.block_table, new_lens)
+        ref = oracle.block_scores(cur.q, cur.k_cache, cur.block_table, cur.seq_lens)
+        gpu_s = msa.msa_indexer_block_scores(q, k, bt, lens).cpu().numpy()
+        check_selection_exact_given_scores(ids.cpu().numpy(), sc.cpu().numpy(), gpu_s, new_lens, 16, 1, 2)
+        check_selection_vs_oracle(ids.cpu().numpy(), ref, new_lens, 16, 1, 2)
+
+
+def test_decode_engines_agree_on_exact_data(msa):
+    # Both engines through the whole pass on the planted workload: bit-exact ids and scores.
+    inp, want_ids, want_sc, _ = cfg(5)
+    q, k, bt, lens = to_device(inp)
+    for engine in ENGINES:
+        ids, sc = msa.msa_indexer_decode(q, k, bt, lens, engine=engine)
+        assert np.array_equal(ids.cpu().numpy(), want_ids)
+        assert np.array_equal(sc.cpu().numpy().astype(np.float64), want_sc)
