@@ -108,6 +108,19 @@ __device__ __forceinline__ uint64_t readlane_u64(uint64_t x, int lane) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+// Number of lanes i < n whose x is larger than this lane's x (all lanes active). Lanes
+// past n are read too when n is not a multiple of 8; callers keep them at 0, which is
+// never larger. Eight reads per step keep the loop from stalling on each one.
+__device__ __forceinline__ int count_larger(uint64_t x, int n) {
+  int r = 0;
+  const int n8 = (n + 7) & ~7;
+  for (int i0 = 0; i0 < n8; i0 += 8) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) r += readlane_u64(x, i0 + u) > x ? 1 : 0;
+  }
+  return r;
+}
+
 // Largest value over the 64 lanes of a wave (all lanes active).
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
   x = umax64(x, dpp_u64<kQuadSwap1>(x));
@@ -344,37 +357,97 @@ __device__ __forceinline__ uint64_t merge_rounds(const uint64_t* lk, int ns, int
 // only lists with r < m and positions i < m - r can hold a winner; and no winner is below
 // T0, the m-th largest head (m heads are at least T0). The at most m(m+1)/2 survivors are
 // ranked by counting; since every key above a winner is itself a survivor, ranks among
-// survivors are the global ranks for the winners. cand: LDS scratch of
-// m(m+1)/2 + m keys, count: one LDS int, both private to this wave.
+// survivors are the global ranks for the winners. Every count reads LDS at one address
+// for all lanes (broadcast), 16 reads in flight, rather than a chain of readlanes.
+// cand: kPrunedScratch keys of LDS private to this wave.
 constexpr int kPrunedMaxM = 16;
-constexpr int kPrunedScratch = kPrunedMaxM * (kPrunedMaxM + 1) / 2 + kPrunedMaxM;
+constexpr int kPrunedScratch = 64 + kPrunedMaxM * (kPrunedMaxM + 1) / 2 + 16;
+
+// Number of keys among a[0 .. n) (LDS, read by every lane at the same address, so the
+// reads broadcast) that are larger than x; 16 reads in flight per step. a must hold at
+// least round_up(n, 16) readable keys.
+__device__ __forceinline__ int count_larger_lds(const uint64_t* a, int n, uint64_t x) {
+  int r = 0;
+  for (int j0 = 0; j0 < n; j0 += 16) {
+    uint64_t v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v[u] = a[j0 + u];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) r += (j0 + u < n && v[u] > x) ? 1 : 0;
+  }
+  return r;
+}
+
+// Exclusive prefix sum over the wave of c in [0, 31], without LDS: one ballot per bit.
+__device__ __forceinline__ int wave_prefix_small(int c, int lane) {
+  int off = 0;
+#pragma unroll
+  for (int bit = 0; bit < 5; ++bit) {
+    const uint64_t mask = __ballot((c >> bit) & 1);
+    const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+    off += (int)below << bit;
+  }
+  (void)lane;
+  return off;
+}
+
+__device__ __forceinline__ int wave_sum_small(int c) {
+  int total = 0;
+#pragma unroll
+  for (int bit = 0; bit < 5; ++bit) total += __popcll(__ballot((c >> bit) & 1)) << bit;
+  return total;
+}
 
 __device__ __forceinline__ uint64_t merge_pruned(const uint64_t* lk, int ns, int Lk, int stride, int m,
-                                                 int lane, uint64_t* cand, int* count) {
+                                                 int lane, uint64_t* cand) {
+  // Heads into a dense array, then every lane counts the heads above its own.
+  uint64_t* heads = cand;  // kPrunedHeads keys, reused below
   const uint64_t head = lane < ns ? lk[lane * stride] : 0;
-  int r = 0;
-  for (int i = 0; i < ns; ++i) r += readlane_u64(head, i) > head ? 1 : 0;
+  heads[lane] = head;
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  const int r = count_larger_lds(heads, ns, head);
   const uint64_t at_m = __ballot(lane < ns && head != 0 && r == m - 1);
-  uint64_t t0 = at_m ? readlane_u64(head, __builtin_ctzll(at_m)) : 1;  // fewer than m lists: no cut
+  const uint64_t t0 = at_m ? readlane_u64(head, __builtin_ctzll(at_m)) : 1;  // fewer than m lists: no cut
+  // This lane's survivors: a prefix of its list (at most kPrunedMaxM keys, read at once).
+  const int lim = (lane < ns && head != 0 && r < m) ? min(Lk, m - r) : 0;
+  uint64_t v[kPrunedMaxM];
   int c = 0;
-  if (lane < ns && head != 0 && r < m) {
-    const int lim = min(Lk, m - r);
-    while (c < lim && lk[lane * stride + c] >= t0) ++c;
+  if (lim > 0) {
+#pragma unroll
+    for (int i = 0; i < kPrunedMaxM; ++i) v[i] = i < Lk ? lk[lane * stride + i] : 0;
   }
-  if (lane == 0) *count = 0;
+#pragma unroll
+  for (int i = 0; i < kPrunedMaxM; ++i) c += (i < lim && v[i] >= t0) ? 1 : 0;
+  const int off = wave_prefix_small(c, lane);
+  const int nc = __builtin_amdgcn_readfirstlane(wave_sum_small(c));
+  uint64_t* sv = cand + 64;  // survivors, after the heads
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // heads read before sv overwrites
+#pragma unroll
+  for (int i = 0; i < kPrunedMaxM; ++i)
+    if (i < c) sv[off + i] = v[i];
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  const int off = c ? atomicAdd(count, c) : 0;
-  for (int i = 0; i < c; ++i) cand[off + i] = lk[lane * stride + i];
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  const int nc = __builtin_amdgcn_readfirstlane(
-      __hip_atomic_load(count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT));
-  uint64_t* winners = cand + kPrunedScratch - kPrunedMaxM;
-  for (int k = lane; k < nc; k += 64) {
-    const uint64_t x = cand[k];
-    int rank = 0;
-    for (int j = 0; j < nc; ++j) rank += cand[j] > x ? 1 : 0;
-    if (rank < m) winners[rank] = x;
+  // Rank each survivor by counting the survivors above it; winners land at their rank.
+  uint64_t* winners = cand;  // the heads are no longer needed
+  uint64_t x[3];
+#pragma unroll
+  for (int t = 0; t < 3; ++t) x[t] = lane + 64 * t < nc ? sv[lane + 64 * t] : 0;
+  int rank[3] = {0, 0, 0};
+  for (int j0 = 0; j0 < nc; j0 += 16) {
+    uint64_t w[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) w[u] = sv[j0 + u];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const bool in = j0 + u < nc;
+#pragma unroll
+      for (int t = 0; t < 3; ++t) rank[t] += (in && w[u] > x[t]) ? 1 : 0;
+    }
   }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+  for (int t = 0; t < 3; ++t)
+    if (lane + 64 * t < nc && rank[t] < m) winners[rank[t]] = x[t];
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   return lane < m ? winners[lane] : 0;
 }
@@ -440,7 +513,6 @@ template <int ENGINE, int MODE>
 __global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
   extern __shared__ uint64_t lk[];  // fused mode: [S][4][Lk] lists of one row, then merge scratch
   __shared__ float sc[kMaxSplitBlocks][kHeads];
-  __shared__ int s_count[kHeads];
   __shared__ int s_last;
 
   const int s = blockIdx.x;
@@ -501,8 +573,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
     const int jj = j0 + lane;
     key = make_key(sc[lane][h], jj, jj < a.n_init || jj >= nb - a.n_local);
   }
-  int rank = 0;
-  for (int i = 0; i < n; ++i) rank += readlane_u64(key, i) > key ? 1 : 0;
+  const int rank = count_larger(key, n);  // lanes >= n hold key 0
   // Agent-scope atomic stores: written through to the device-coherent level, so the
   // row's last workgroup can read them from any XCD without an L2 writeback.
   uint64_t* out = a.keys + ((size_t)(b * a.S + s) * kHeads + h) * a.Lk;
@@ -540,7 +611,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
   uint64_t mine;
   if (ns <= 64 && a.topk <= kPrunedMaxM) {
     uint64_t* scratch = lk + (size_t)a.S * stride + h * kPrunedScratch;
-    mine = merge_pruned(lk + h * a.Lk, ns, a.Lk, stride, m, lane, scratch, &s_count[h]);
+    mine = merge_pruned(lk + h * a.Lk, ns, a.Lk, stride, m, lane, scratch);
   } else {
     mine = merge_rounds(lk + h * a.Lk, ns, a.Lk, stride, m, lane);
   }
