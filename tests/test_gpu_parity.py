@@ -263,3 +263,40 @@ def test_decode_engines_agree_on_exact_data(msa):
         ids, sc = msa.msa_indexer_decode(q, k, bt, lens, engine=engine)
         assert np.array_equal(ids.cpu().numpy(), want_ids)
         assert np.array_equal(sc.cpu().numpy().astype(np.float64), want_sc)
+
+
+@pytest.mark.parametrize("B", [1, 2, 4, 8, 15, 16, 32])
+def test_split_width_sweep(msa, B):
+    # The grid of TensorRT-LLM PR #17008 (Accuracy): scores identical at every split width
+    # and the selected blocks identical, over batch x context length, with consecutive
+    # decode lengths (8700 and 8701) in the grid.
+    for kv in (256, 1000, 4096, 8700, 8701, 16384):
+        nbk = -(-kv // 128)
+        inp = synth.paged_case(1000 + B * 31 + kv, [kv] * B, nbk, poison=False, permute=True)
+        q, k, bt, lens = to_device(inp)
+        ref = oracle.block_scores(inp.q, inp.k_cache, inp.block_table, inp.seq_lens)
+        base_s, base_ids = None, None
+        for ns in sorted({0, 1, 2, 3, 4, 7, nbk // 2, nbk}):
+            try:
+                msa.plan(B, nbk, 16, ns)
+            except msa.MsaError:  # more than 64 blocks per split: refused by design
+                continue
+            s = msa.msa_indexer_block_scores(q, k, bt, lens, num_splits=ns).cpu().numpy()
+            ids, sc = msa.msa_indexer_decode(q, k, bt, lens, num_splits=ns)
+            ids, sc = ids.cpu().numpy(), sc.cpu().numpy()
+            if base_s is None:
+                base_s, base_ids = s, ids
+                check_scores(s, ref)
+                check_selection_exact_given_scores(ids, sc, s, inp.seq_lens, 16, 1, 2)
+                check_selection_vs_oracle(ids, ref, inp.seq_lens, 16, 1, 2)
+            assert np.array_equal(s, base_s), (B, kv, ns)
+            assert np.array_equal(ids, base_ids), (B, kv, ns)
+
+
+def test_heads_disagree_cfg2(msa):
+    inp, _, _, _ = cfg(2)
+    q, k, bt, lens = to_device(inp)
+    ids, _ = msa.msa_indexer_decode(q, k, bt, lens)
+    ids = ids.cpu().numpy()
+    differ = [len({tuple(sorted(ids[b, h])) for h in range(4)}) == 4 for b in range(inp.batch)]
+    assert np.mean(differ) >= 0.9
