@@ -361,7 +361,7 @@ __device__ __forceinline__ uint64_t merge_rounds(const uint64_t* lk, int ns, int
 // for all lanes (broadcast), 16 reads in flight, rather than a chain of readlanes.
 // cand: kPrunedScratch keys of LDS private to this wave.
 constexpr int kPrunedMaxM = 16;
-constexpr int kPrunedScratch = 64 + kPrunedMaxM * (kPrunedMaxM + 1) / 2 + 16;
+constexpr int kPrunedScratch = 64 + kPrunedMaxM * (kPrunedMaxM + 1) / 2 + 16 + 64;
 
 // Number of keys among a[0 .. n) (LDS, read by every lane at the same address, so the
 // reads broadcast) that are larger than x; 16 reads in flight per step. a must hold at
@@ -411,43 +411,53 @@ __device__ __forceinline__ uint64_t merge_pruned(const uint64_t* lk, int ns, int
   const uint64_t t0 = at_m ? readlane_u64(head, __builtin_ctzll(at_m)) : 1;  // fewer than m lists: no cut
   // This lane's survivors: a prefix of its list (at most kPrunedMaxM keys, read at once).
   const int lim = (lane < ns && head != 0 && r < m) ? min(Lk, m - r) : 0;
+  // Read kPrunedMaxM keys from the start of this lane's list whatever lim is: they lie in
+  // the lane's staged row group or the next one (stride >= 4 Lk + 1 keys, rows up to S),
+  // so they are in bounds, and the count below masks the ones past lim.
+  const uint64_t* mylist = lk + (lane < ns ? lane : 0) * stride;
   uint64_t v[kPrunedMaxM];
   int c = 0;
-  if (lim > 0) {
 #pragma unroll
-    for (int i = 0; i < kPrunedMaxM; ++i) v[i] = i < Lk ? lk[lane * stride + i] : 0;
+  for (int i = 0; i < kPrunedMaxM; ++i) {
+    v[i] = mylist[i];
+    c += (i < lim && v[i] >= t0) ? 1 : 0;
   }
-#pragma unroll
-  for (int i = 0; i < kPrunedMaxM; ++i) c += (i < lim && v[i] >= t0) ? 1 : 0;
   const int off = wave_prefix_small(c, lane);
   const int nc = __builtin_amdgcn_readfirstlane(wave_sum_small(c));
-  uint64_t* sv = cand + 64;  // survivors, after the heads
+  uint64_t* sv = cand + 64;                      // survivors, after the heads
+  uint64_t* sink = cand + kPrunedScratch - 64;   // one discard slot per lane
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // heads read before sv overwrites
 #pragma unroll
-  for (int i = 0; i < kPrunedMaxM; ++i)
-    if (i < c) sv[off + i] = v[i];
+  for (int i = 0; i < kPrunedMaxM; ++i) *(i < c ? sv + off + i : sink + lane) = v[i];
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   // Rank each survivor by counting the survivors above it; winners land at their rank.
   uint64_t* winners = cand;  // the heads are no longer needed
-  uint64_t x[3];
+  if (nc <= 64) {  // the usual case: one survivor per lane
+    const uint64_t x = lane < nc ? sv[lane] : 0;
+    const int rank = count_larger_lds(sv, nc, x);
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    if (lane < nc && rank < m) winners[rank] = x;
+  } else {
+    uint64_t x[3];
 #pragma unroll
-  for (int t = 0; t < 3; ++t) x[t] = lane + 64 * t < nc ? sv[lane + 64 * t] : 0;
-  int rank[3] = {0, 0, 0};
-  for (int j0 = 0; j0 < nc; j0 += 16) {
-    uint64_t w[16];
+    for (int t = 0; t < 3; ++t) x[t] = lane + 64 * t < nc ? sv[lane + 64 * t] : 0;
+    int rank[3] = {0, 0, 0};
+    for (int j0 = 0; j0 < nc; j0 += 16) {
+      uint64_t w[16];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) w[u] = sv[j0 + u];
+      for (int u = 0; u < 16; ++u) w[u] = sv[j0 + u];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const bool in = j0 + u < nc;
+      for (int u = 0; u < 16; ++u) {
+        const bool in = j0 + u < nc;
 #pragma unroll
-      for (int t = 0; t < 3; ++t) rank[t] += (in && w[u] > x[t]) ? 1 : 0;
+        for (int t = 0; t < 3; ++t) rank[t] += (in && w[u] > x[t]) ? 1 : 0;
+      }
     }
-  }
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 #pragma unroll
-  for (int t = 0; t < 3; ++t)
-    if (lane + 64 * t < nc && rank[t] < m) winners[rank[t]] = x[t];
+    for (int t = 0; t < 3; ++t)
+      if (lane + 64 * t < nc && rank[t] < m) winners[rank[t]] = x[t];
+  }
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   return lane < m ? winners[lane] : 0;
 }
