@@ -32,6 +32,8 @@ class Oracle:
         lib.msa_oracle_block_scores.restype = ctypes.c_int
         lib.msa_oracle_select.argtypes = [P, P, i32, i32, i32, i32, i32, P, P]
         lib.msa_oracle_select.restype = ctypes.c_int
+        lib.msa_oracle_expand_pages.argtypes = [P, P, P, i32, i32, i32, i32, P, P]
+        lib.msa_oracle_expand_pages.restype = ctypes.c_int
         lib.msa_oracle_num_threads.argtypes = []
         lib.msa_oracle_num_threads.restype = ctypes.c_int
         self.lib = lib
@@ -70,6 +72,21 @@ class Oracle:
             raise ValueError(f"oracle select failed with code {rc}")
         return ids, out
 
+    def expand_pages(self, ids, block_table, seq_lens):
+        """16-token page tables of selections ids [B,4,topk]: (pages [B,4,8*topk], tokens [B,4])."""
+        ids = np.ascontiguousarray(ids, dtype=np.int32)
+        block_table = np.ascontiguousarray(block_table, dtype=np.int32)
+        seq_lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+        B, H, topk = ids.shape
+        W = block_table.shape[1]
+        pages = np.empty((B, HEADS, 8 * topk), dtype=np.int32)
+        tokens = np.empty((B, HEADS), dtype=np.int32)
+        rc = self.lib.msa_oracle_expand_pages(_ptr(ids), _ptr(block_table), _ptr(seq_lens), B, W, W,
+                                              topk, _ptr(pages), _ptr(tokens))
+        if rc != 0:
+            raise ValueError(f"oracle expand_pages failed with code {rc}")
+        return pages, tokens
+
     def decode(self, inp):
         """Whole pass on a synth.Inputs: (ids, selected scores, block scores)."""
         s = self.block_scores(inp.q, inp.k_cache, inp.block_table, inp.seq_lens)
@@ -104,3 +121,7 @@ def select(scores, seq_lens, topk: int, n_init: int, n_local: int):
 
 def decode(inp):
     return default().decode(inp)
+
+
+def expand_pages(ids, block_table, seq_lens):
+    return default().expand_pages(ids, block_table, seq_lens)

@@ -43,6 +43,15 @@
  *         broken by ascending id); scores compare numerically, so -0 == +0;
  *       - slots m .. topk-1 hold id -1 and score -inf; an empty row has none.
  *
+ *   page table    for a sparse-attention consumer that reads 16-token pages (vLLM blog
+ *                 "Following the Bottleneck", section 3 and Figure 5: each selected
+ *                 128-token block resolves to its physical block, whose eight 16-token
+ *                 pages make eight entries of a compact page table; the cache itself is
+ *                 not copied). Per (b, h): the selected blocks in ascending logical order;
+ *                 the i-th gives entries 8i .. 8i+7 = 8 * block_table[b][j] + t; entries
+ *                 past the selected blocks are -1; the table's token count is the sum of
+ *                 the selected blocks' valid tokens.
+ *
  * bf16 inputs are widened exactly (bits << 16 is the fp32 value; fp32 -> fp64
  * is exact), products of two bf16 values are exact in fp64, and the 128-term
  * sums are accumulated in fp64.
@@ -215,4 +224,42 @@ int msa_oracle_decode(const uint16_t *q, const uint16_t *k_cache,
     if (rc != OR_OK) return rc;
     return msa_oracle_select(scratch_scores, seq_lens, batch, max_blocks, topk, n_init,
                              n_local, out_ids, out_scores);
+}
+
+static int cmp_int(const void *pa, const void *pb)
+{
+    int32_t a = *(const int32_t *)pa, b = *(const int32_t *)pb;
+    return (a > b) - (a < b);
+}
+
+/*
+ * 16-token page tables from selections ids[b][h][i] (i < topk, -1 = none):
+ * pages[b][h][8*topk], tokens[b][h].
+ */
+int msa_oracle_expand_pages(const int32_t *ids, const int32_t *block_table, const int32_t *seq_lens,
+                            int32_t batch, int32_t max_blocks, int32_t bt_stride, int32_t topk,
+                            int32_t *pages, int32_t *tokens)
+{
+    if (batch < 0 || max_blocks < 0 || bt_stride < max_blocks || topk < 1) return OR_ERR_ARG;
+    for (int64_t bh = 0; bh < (int64_t)batch * OR_HEADS; ++bh) {
+        int32_t b = (int32_t)(bh / OR_HEADS);
+        int64_t L = row_len(seq_lens, b, max_blocks);
+        int32_t sel[256];
+        int n = 0;
+        for (int i = 0; i < topk && i < 256; ++i)
+            if (ids[bh * topk + i] >= 0) sel[n++] = ids[bh * topk + i];
+        qsort(sel, (size_t)n, sizeof(int32_t), cmp_int);
+        int32_t *row = pages + bh * topk * 8;
+        for (int64_t e = 0; e < (int64_t)topk * 8; ++e) row[e] = -1;
+        int64_t count = 0;
+        for (int i = 0; i < n; ++i) {
+            int32_t j = sel[i];
+            int64_t page = block_table[(int64_t)b * bt_stride + j];
+            for (int t = 0; t < 8; ++t) row[i * 8 + t] = (int32_t)(page * 8 + t);
+            int64_t valid = L - (int64_t)j * OR_BLOCK;
+            count += valid > OR_BLOCK ? OR_BLOCK : valid;
+        }
+        tokens[bh] = (int32_t)count;
+    }
+    return OR_OK;
 }

@@ -23,8 +23,8 @@ MUTANTS = {
     "head_index": ("q + ((int64_t)b * OR_HEADS + h) * OR_DIM",
                    "q + ((int64_t)b * OR_HEADS + (OR_HEADS - 1 - h)) * OR_DIM"),
     "tail_unmasked": ("if (valid > OR_BLOCK) valid = OR_BLOCK;", "valid = OR_BLOCK;"),
-    "logical_order": ("block_table[(int64_t)b * bt_stride + j]",
-                      "block_table[(int64_t)b * bt_stride + (nb - 1 - j)]"),
+    "logical_order": ("block_table[(int64_t)b * bt_stride + j];\n            if (page < 0",
+                      "block_table[(int64_t)b * bt_stride + (nb - 1 - j)];\n            if (page < 0"),
     "max_seeded_zero": ("for (int h = 0; h < OR_HEADS; ++h) best[h] = -INFINITY;",
                         "for (int h = 0; h < OR_HEADS; ++h) best[h] = 0.0;"),
     "recent_pin_off_by_one": ("(j >= nb - n_local)", "(j > nb - n_local)"),
@@ -38,6 +38,9 @@ MUTANTS = {
                     "out_ids[bh * topk + i] = i < m ? c[i].id : 0;"),
     "short_row_truncated": ("int64_t m = nb < topk ? nb : topk;",
                             "int64_t m = nb < topk ? nb - 1 : topk;"),
+    "pages_not_sorted": ("qsort(sel, (size_t)n, sizeof(int32_t), cmp_int);", ""),
+    "page_offset": ("row[i * 8 + t] = (int32_t)(page * 8 + t);", "row[i * 8 + t] = (int32_t)(page * 8 + t + 1);"),
+    "tokens_full_blocks": ("count += valid > OR_BLOCK ? OR_BLOCK : valid;", "count += OR_BLOCK;"),
 }
 
 

@@ -385,3 +385,46 @@ def pin_page_figures(orc):
 @pytest.mark.parametrize("check", PINS, ids=lambda f: f.__name__[4:])
 def test_oracle_pin(check):
     check(oracle.default())
+
+
+# ---------------------------------------------------------------------------
+# The 16-token page table (vLLM blog "Following the Bottleneck", section 3).
+
+@pin
+def pin_expand_pages_hand_built(orc):
+    # Row 0: 300 tokens in 3 blocks on pages 7, 2, 9; selection order (2, 0, 1) comes out in
+    # ascending block order: pages 7, 2, 9 -> entries 56..63, 16..23, 72..79; tokens
+    # 128 + 128 + 44 = 300. Row 1: empty.
+    ids = np.full((2, 4, 4), -1, np.int32)
+    ids[0, :, :3] = [2, 0, 1]
+    ids[0, 1, :3] = [1, 2, 0]               # a different selection order, same table
+    bt = np.array([[7, 2, 9], [0, 0, 0]], np.int32)
+    lens = np.array([300, 0], np.int32)
+    pages, tokens = orc.expand_pages(ids, bt, lens)
+    want = list(range(56, 64)) + list(range(16, 24)) + list(range(72, 80)) + [-1] * 8
+    for h in range(4):
+        assert list(pages[0, h]) == want
+        assert tokens[0, h] == 300
+    assert np.all(pages[1] == -1) and np.all(tokens[1] == 0)
+    # Only the full blocks 0 and 1 selected: 256 tokens.
+    ids2 = np.full((1, 4, 4), -1, np.int32)
+    ids2[0, :, :2] = [1, 0]
+    p2, t2 = orc.expand_pages(ids2, bt[:1], lens[:1])
+    assert list(p2[0, 0, :16]) == list(range(56, 64)) + list(range(16, 24)) and np.all(t2 == 256)
+
+
+@pin
+def pin_expand_pages_invariants(orc):
+    inp = synth.paged_case(51, [128 * 40 + 17, 128 * 9, 5, 0], 41)
+    ids, _, _ = orc.decode(inp)
+    pages, tokens = orc.expand_pages(ids, inp.block_table, inp.seq_lens)
+    for b in range(4):
+        L = int(inp.seq_lens[b])
+        for h in range(4):
+            sel = sorted(j for j in ids[b, h] if j >= 0)
+            got = pages[b, h].reshape(-1, 8)
+            for i, j in enumerate(sel):
+                p = int(inp.block_table[b, j])
+                assert list(got[i]) == [8 * p + t for t in range(8)]
+            assert np.all(got[len(sel):] == -1)
+            assert tokens[b, h] == sum(min(128, L - 128 * j) for j in sel)
