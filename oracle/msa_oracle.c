@@ -233,21 +233,26 @@ static int cmp_int(const void *pa, const void *pb)
 }
 
 /*
- * 16-token page tables from selections ids[b][h][i] (i < topk, -1 = none):
- * pages[b][h][8*topk], tokens[b][h].
+ * 16-token page tables from selections ids[b][h][i] (i < topk): pages[b][h][8*topk],
+ * tokens[b][h]. An id outside [0, nb) stands for no block (-1 pads a short selection);
+ * a repeated id is expanded each time it appears. The entry is 8 * page + t modulo 2^32.
  */
 int msa_oracle_expand_pages(const int32_t *ids, const int32_t *block_table, const int32_t *seq_lens,
                             int32_t batch, int32_t max_blocks, int32_t bt_stride, int32_t topk,
                             int32_t *pages, int32_t *tokens)
 {
-    if (batch < 0 || max_blocks < 0 || bt_stride < max_blocks || topk < 1) return OR_ERR_ARG;
+    if (batch < 0 || max_blocks < 0 || bt_stride < max_blocks || topk < 1 || topk > 256)
+        return OR_ERR_ARG;
     for (int64_t bh = 0; bh < (int64_t)batch * OR_HEADS; ++bh) {
         int32_t b = (int32_t)(bh / OR_HEADS);
         int64_t L = row_len(seq_lens, b, max_blocks);
+        int64_t nb = (L + OR_BLOCK - 1) / OR_BLOCK;
         int32_t sel[256];
         int n = 0;
-        for (int i = 0; i < topk && i < 256; ++i)
-            if (ids[bh * topk + i] >= 0) sel[n++] = ids[bh * topk + i];
+        for (int i = 0; i < topk; ++i) {
+            int32_t j = ids[bh * topk + i];
+            if (j >= 0 && j < nb) sel[n++] = j;
+        }
         qsort(sel, (size_t)n, sizeof(int32_t), cmp_int);
         int32_t *row = pages + bh * topk * 8;
         for (int64_t e = 0; e < (int64_t)topk * 8; ++e) row[e] = -1;
@@ -255,7 +260,7 @@ int msa_oracle_expand_pages(const int32_t *ids, const int32_t *block_table, cons
         for (int i = 0; i < n; ++i) {
             int32_t j = sel[i];
             int64_t page = block_table[(int64_t)b * bt_stride + j];
-            for (int t = 0; t < 8; ++t) row[i * 8 + t] = (int32_t)(page * 8 + t);
+            for (int t = 0; t < 8; ++t) row[i * 8 + t] = (int32_t)(uint32_t)(page * 8 + t);
             int64_t valid = L - (int64_t)j * OR_BLOCK;
             count += valid > OR_BLOCK ? OR_BLOCK : valid;
         }

@@ -39,7 +39,11 @@ MUTANTS = {
     "short_row_truncated": ("int64_t m = nb < topk ? nb : topk;",
                             "int64_t m = nb < topk ? nb - 1 : topk;"),
     "pages_not_sorted": ("qsort(sel, (size_t)n, sizeof(int32_t), cmp_int);", ""),
-    "page_offset": ("row[i * 8 + t] = (int32_t)(page * 8 + t);", "row[i * 8 + t] = (int32_t)(page * 8 + t + 1);"),
+    "page_offset": ("row[i * 8 + t] = (int32_t)(uint32_t)(page * 8 + t);",
+                    "row[i * 8 + t] = (int32_t)(uint32_t)(page * 8 + t + 1);"),
+    "ids_past_row_kept": ("if (j >= 0 && j < nb) sel[n++] = j;", "if (j >= 0 && j < max_blocks) sel[n++] = j;"),
+    "repeats_dropped": ("if (j >= 0 && j < nb) sel[n++] = j;",
+                        "if (j >= 0 && j < nb && (n == 0 || sel[n - 1] != j)) sel[n++] = j;"),
     "tokens_full_blocks": ("count += valid > OR_BLOCK ? OR_BLOCK : valid;", "count += OR_BLOCK;"),
 }
 

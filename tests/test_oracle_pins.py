@@ -411,6 +411,17 @@ def pin_expand_pages_hand_built(orc):
     ids2[0, :, :2] = [1, 0]
     p2, t2 = orc.expand_pages(ids2, bt[:1], lens[:1])
     assert list(p2[0, 0, :16]) == list(range(56, 64)) + list(range(16, 24)) and np.all(t2 == 256)
+    # A 4-wide table whose row ends in block 2: id 3 (inside the table, past the row) and
+    # id -7 stand for no block; a repeated id is expanded twice; page 2^29 wraps mod 2^32.
+    bt3 = np.array([[1 << 29, 2, 9, 4]], np.int32)
+    ids3 = np.array([[[3, 2, -7, 2], [0, 3, 3, 3], [-1, -1, -1, -1], [1, 0, 2, 3]]], np.int32)
+    p3, t3 = orc.expand_pages(ids3, bt3, lens[:1])
+    wrap = [int(np.int32(np.uint32((8 << 29) % (1 << 32)) + t)) for t in range(8)]
+    assert list(p3[0, 0]) == list(range(72, 80)) * 2 + [-1] * 16 and t3[0, 0] == 88
+    assert list(p3[0, 1]) == wrap + [-1] * 24 and t3[0, 1] == 128
+    assert np.all(p3[0, 2] == -1) and t3[0, 2] == 0
+    assert list(p3[0, 3]) == wrap + list(range(16, 24)) + list(range(72, 80)) + [-1] * 8
+    assert t3[0, 3] == 300
 
 
 @pin
