@@ -99,10 +99,10 @@ int32_t msa_indexer_plan(int32_t batch, int32_t max_blocks_per_seq, int32_t topk
 
 /*
  * Workspace bytes a call with these arguments needs (0 on invalid arguments).
- * Layout: a 256-byte header whose first uint32 is the device error word and whose next
- * `batch` uint32 (spilling past 256 bytes for large batches) are per-row counters of
- * finished splits, padded to a 256-byte boundary; then the per-split candidate keys,
- * uint64 [batch][S][4][Lk]. The whole workspace must be zero before its first use (e.g.
+ * Layout: a 256-byte header whose first uint32 is the device error word; then one 256-byte
+ * line per row whose first uint32 counts the row's finished splits (uint32 [batch][64]);
+ * then the per-split candidate keys, uint64 [batch][S][4][Lk]. The whole workspace must be
+ * zero before its first use (e.g.
  * hipMemset once after allocation). The library leaves the counters at zero at the end of
  * every call, so the same workspace can be reused, and replayed in a graph, without
  * clearing it again; the error word only ever gains bits (msa_indexer_read_error clears it).
@@ -156,6 +156,50 @@ int32_t msa_indexer_decode_engine(const void *q, const void *k_cache, const int3
                                   int32_t topk, int32_t n_init, int32_t n_local, int32_t *out_ids,
                                   float *out_scores, void *workspace, size_t workspace_bytes,
                                   int32_t num_splits, int32_t engine, void *stream);
+
+/*
+ * msa_indexer_decode that also writes the selection as a 16-token page table, for a
+ * sparse-attention kernel that pages KV in 16-token pages while the indexer selects
+ * 128-token blocks (vLLM blog "Following the Bottleneck", section 3 and Figure 5: each
+ * selected block becomes the eight 16-token page entries of its physical block, and only
+ * this table is built; the KV cache is not copied or moved).
+ *   out_pages    int32 [batch][4][8*topk], 16-byte aligned. For (b, h), the selected blocks
+ *                in ascending logical block order; the i-th, block j, gives entries
+ *                8i .. 8i+7 = 8 * block_table[b*bt_stride + j] + t (t = 0..7). Entries past
+ *                8 * m are -1.
+ *   out_tokens   int32 [batch][4], 4-byte aligned: tokens in that table, the sum over the
+ *                selected blocks of min(128, len_b - 128 j). Only the last block of a row can
+ *                be partial, and it comes last when selected, so the table's first
+ *                out_tokens entries' tokens are exactly the selected context.
+ * Both must be non-null when batch > 0. num_pages must be at most 2^28 (so a 16-token page
+ * id fits int32; MSA_ERR_UNSUPPORTED otherwise). `engine` as in msa_indexer_decode_engine;
+ * every other argument as in msa_indexer_decode. The table is written by the same launch
+ * that writes out_ids (the merging workgroup of each row), not by an extra pass.
+ */
+int32_t msa_indexer_decode_pages(const void *q, const void *k_cache, const int32_t *block_table,
+                                 const int32_t *seq_lens, int32_t batch,
+                                 int32_t max_blocks_per_seq, int32_t bt_stride, int64_t num_pages,
+                                 int32_t topk, int32_t n_init, int32_t n_local, int32_t *out_ids,
+                                 float *out_scores, int32_t *out_pages, int32_t *out_tokens,
+                                 void *workspace, size_t workspace_bytes, int32_t num_splits,
+                                 int32_t engine, void *stream);
+
+/*
+ * The page table of msa_indexer_decode_pages from given selections (vLLM blog "Following the
+ * Bottleneck", section 3), e.g. a selection a previous layer made and later layers reuse.
+ *   ids          int32 [batch][4][topk], 4-byte aligned: per (b, h), block ids in any order.
+ *                An id outside [0, nb_b) stands for no block (so -1 padding is skipped) and
+ *                is never looked up; a repeated id is expanded each time it appears.
+ *   block_table, seq_lens, batch, max_blocks_per_seq, bt_stride as in msa_indexer_decode
+ *                (block_table entries of selected blocks are copied, not range-checked).
+ *   topk in [1, MSA_MAX_TOPK]; out_pages int32 [batch][4][8*topk] (16-byte aligned) and
+ *   out_tokens int32 [batch][4] as in msa_indexer_decode_pages, counting each expanded id.
+ * One launch of `batch` workgroups; no workspace. Entries are 8 * page + t modulo 2^32.
+ */
+int32_t msa_indexer_expand_pages(const int32_t *ids, const int32_t *block_table,
+                                 const int32_t *seq_lens, int32_t batch,
+                                 int32_t max_blocks_per_seq, int32_t bt_stride, int32_t topk,
+                                 int32_t *out_pages, int32_t *out_tokens, void *stream);
 
 /*
  * Stage 1 of msa_indexer_decode alone (never fused): one workgroup per (row, split) scores its blocks

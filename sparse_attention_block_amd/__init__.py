@@ -12,6 +12,8 @@ from ._lib import (  # noqa: F401
     load,
     msa_indexer_block_scores,
     msa_indexer_decode,
+    msa_indexer_decode_pages,
+    msa_indexer_expand_pages,
     msa_indexer_merge,
     msa_indexer_read_error,
     msa_indexer_split_topk,

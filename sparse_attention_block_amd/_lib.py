@@ -43,6 +43,9 @@ _SIGNATURES = {
                             _SZ, _I32, _P], _I32),
     "msa_indexer_decode_engine": ([_P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32, _I32, _P, _P,
                                    _P, _SZ, _I32, _I32, _P], _I32),
+    "msa_indexer_decode_pages": ([_P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32, _I32, _P, _P,
+                                  _P, _P, _P, _SZ, _I32, _I32, _P], _I32),
+    "msa_indexer_expand_pages": ([_P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _P], _I32),
     "msa_indexer_split_topk": ([_P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32, _I32, _P, _SZ,
                                 _I32, _I32, _P], _I32),
     "msa_indexer_merge": ([_P, _I32, _I32, _I32, _P, _P, _P, _SZ, _I32, _P], _I32),
@@ -191,6 +194,57 @@ def msa_indexer_decode(q, k_cache, block_table, seq_lens, topk=16, n_init=1, n_l
         rc = load().msa_indexer_decode_engine(*args, engine, _stream(stream))
         _check("msa_indexer_decode_engine", rc)
     return out_ids, out_scores
+
+
+def msa_indexer_decode_pages(q, k_cache, block_table, seq_lens, topk=16, n_init=1, n_local=2,
+                             out_ids=None, out_scores=None, out_pages=None, out_tokens=None,
+                             workspace=None, num_splits=0, engine=ENGINE_DEFAULT, stream=None):
+    """The decode pass plus its 16-token page table. Returns (out_ids, out_scores,
+    out_pages int32 [B,4,8*topk], out_tokens int32 [B,4])."""
+    torch = _torch()
+    (pq, pk, pbt, pl), B, W, stride, pages = _inputs(q, k_cache, block_table, seq_lens)
+    dev = q.device
+    out_ids = torch.empty((B, HEADS, topk), dtype=torch.int32, device=dev) if out_ids is None else out_ids
+    if out_scores is None:
+        out_scores = torch.empty((B, HEADS, topk), dtype=torch.float32, device=dev)
+    if out_pages is None:
+        out_pages = torch.empty((B, HEADS, 8 * topk), dtype=torch.int32, device=dev)
+    if out_tokens is None:
+        out_tokens = torch.empty((B, HEADS), dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = new_workspace(B, W, topk, num_splits, dev)
+    rc = load().msa_indexer_decode_pages(
+        pq, pk, pbt, pl, B, W, stride, pages, topk, n_init, n_local,
+        _dev(out_ids, "out_ids", torch.int32, (B, HEADS, topk)),
+        _dev(out_scores, "out_scores", torch.float32, (B, HEADS, topk)),
+        _dev(out_pages, "out_pages", torch.int32, (B, HEADS, 8 * topk)),
+        _dev(out_tokens, "out_tokens", torch.int32, (B, HEADS)),
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(), num_splits, engine,
+        _stream(stream))
+    _check("msa_indexer_decode_pages", rc)
+    return out_ids, out_scores, out_pages, out_tokens
+
+
+def msa_indexer_expand_pages(ids, block_table, seq_lens, out_pages=None, out_tokens=None,
+                             stream=None):
+    """16-token page table of given selections ids int32 [B,4,topk]: (out_pages, out_tokens)."""
+    torch = _torch()
+    if ids.dim() != 3 or ids.shape[1] != HEADS:
+        raise ValueError("ids: expected [batch, 4, topk]")
+    B, topk = ids.shape[0], ids.shape[2]
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table: expected [batch, max_blocks]")
+    if out_pages is None:
+        out_pages = torch.empty((B, HEADS, 8 * topk), dtype=torch.int32, device=ids.device)
+    if out_tokens is None:
+        out_tokens = torch.empty((B, HEADS), dtype=torch.int32, device=ids.device)
+    rc = load().msa_indexer_expand_pages(
+        _dev(ids, "ids", torch.int32), _dev(block_table, "block_table", torch.int32),
+        _dev(seq_lens, "seq_lens", torch.int32, (B,)), B, block_table.shape[1],
+        block_table.stride(0), topk, _dev(out_pages, "out_pages", torch.int32, (B, HEADS, 8 * topk)),
+        _dev(out_tokens, "out_tokens", torch.int32, (B, HEADS)), _stream(stream))
+    _check("msa_indexer_expand_pages", rc)
+    return out_pages, out_tokens
 
 
 def msa_indexer_split_topk(q, k_cache, block_table, seq_lens, workspace, topk=16, n_init=1,

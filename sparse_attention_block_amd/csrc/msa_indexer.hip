@@ -471,6 +471,46 @@ __device__ __forceinline__ void write_selection(uint64_t mine, int m, int topk, 
 }
 
 // ---------------------------------------------------------------------------------------
+// 16-token page table of one (row, head), for a sparse-attention consumer that pages KV in
+// 16-token pages (vLLM blog "Following the Bottleneck", section 3, Figure 5: each selected
+// 128-token block stands for its physical block's eight 16-token pages; only the table is
+// built, the cache stays in place). Lane i < topk holds block id `id`, `valid` when it names
+// a block of the row. The valid blocks go out in ascending logical order, block i of that
+// order as entries 8i .. 8i+7 = 8 * page + t (modulo 2^32); the remaining entries up to
+// 8 topk are -1. *tokens = the valid blocks' tokens. All 64 lanes must be active.
+
+__device__ __forceinline__ void emit_pages(int id, bool valid, int topk, int lane,
+                                           const int32_t* __restrict__ btrow, int L,
+                                           int32_t* __restrict__ pages, int32_t* __restrict__ tokens) {
+  // Slot of a valid lane: the valid lanes with a smaller (id, lane) before it, so repeated
+  // ids keep one slot each. Invalid lanes below topk fill the slots after the valid ones.
+  const uint64_t ord = valid ? ~(((uint64_t)(uint32_t)id << 6) | (uint64_t)lane) : 0;
+  const int pos = count_larger(ord, topk);
+  const uint64_t vmask = __ballot(valid);
+  const int n = __popcll(vmask);
+  const int valid_below = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(vmask >> 32),
+                                                         __builtin_amdgcn_mbcnt_lo((uint32_t)vmask, 0u));
+  const int slot = valid ? pos : n + (lane - valid_below);
+  if (lane < topk) {
+    int4 lo = make_int4(-1, -1, -1, -1), hi = lo;
+    if (valid) {
+      const uint32_t p = (uint32_t)btrow[id] * 8u;
+      lo = make_int4((int)p, (int)(p + 1), (int)(p + 2), (int)(p + 3));
+      hi = make_int4((int)(p + 4), (int)(p + 5), (int)(p + 6), (int)(p + 7));
+    }
+    int4* dst = reinterpret_cast<int4*>(pages + (size_t)slot * 8);
+    dst[0] = lo;
+    dst[1] = hi;
+  }
+  // Each lane's count is at most 128: sum it bit by bit over the wave.
+  const int cnt = valid ? min(kBlock, L - id * kBlock) : 0;
+  int total = 0;
+#pragma unroll
+  for (int bit = 0; bit < 8; ++bit) total += __popcll(__ballot((cnt >> bit) & 1)) << bit;
+  if (lane == 0) *tokens = total;
+}
+
+// ---------------------------------------------------------------------------------------
 // Stage 1.
 //
 // Row b gets ns = ceil(nb / C) workgroups; workgroup s owns the contiguous blocks
@@ -494,6 +534,8 @@ struct SplitArgs {
   uint32_t* counters;   // [batch][kCounterStride]: [0] workgroups finished; zero between calls
   int32_t* out_ids;     // [batch][4][topk] (fused mode)
   float* out_scores;    // [batch][4][topk] (fused mode)
+  int32_t* out_pages;   // [batch][4][8 topk] 16-token page table (fused mode; may be null)
+  int32_t* out_tokens;  // [batch][4] tokens in that table (with out_pages)
   float* scores;        // [batch][4][W] (block-score mode)
 };
 
@@ -558,10 +600,17 @@ __global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
   const int j1 = min(j0 + a.C, nb);
   if (s >= ns) {
     // An empty row has no workgroup to merge it: its first workgroup writes the padding.
-    if (MODE == kFused && nb == 0 && s == 0 && threadIdx.x < kHeads * a.topk) {
-      const size_t o = (size_t)b * kHeads * a.topk + threadIdx.x;
-      a.out_ids[o] = -1;
-      a.out_scores[o] = -__builtin_inff();
+    if (MODE == kFused && nb == 0 && s == 0) {
+      if (threadIdx.x < kHeads * a.topk) {
+        const size_t o = (size_t)b * kHeads * a.topk + threadIdx.x;
+        a.out_ids[o] = -1;
+        a.out_scores[o] = -__builtin_inff();
+      }
+      if (a.out_pages != nullptr) {
+        for (int e = threadIdx.x; e < kHeads * a.topk * 8; e += kThreads)
+          a.out_pages[(size_t)b * kHeads * a.topk * 8 + e] = -1;
+        if (threadIdx.x < kHeads) a.out_tokens[(size_t)b * kHeads + threadIdx.x] = 0;
+      }
     }
     return;
   }
@@ -627,6 +676,9 @@ __global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
   }
   const size_t o = ((size_t)b * kHeads + h) * a.topk;
   write_selection(mine, m, a.topk, lane, a.out_ids + o, a.out_scores + o);
+  if (a.out_pages != nullptr)
+    emit_pages(key_id(mine), lane < m, a.topk, lane, btrow, L, a.out_pages + o * 8,
+               a.out_tokens + (size_t)b * kHeads + h);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -638,6 +690,10 @@ struct MergeArgs {
   const uint64_t* keys;
   int32_t* out_ids;
   float* out_scores;
+  const int32_t* bt;    // with out_pages: the block table and its row stride
+  int32_t bt_stride;
+  int32_t* out_pages;   // may be null
+  int32_t* out_tokens;
 };
 
 __global__ __launch_bounds__(64) void merge_kernel(MergeArgs a) {
@@ -655,6 +711,32 @@ __global__ __launch_bounds__(64) void merge_kernel(MergeArgs a) {
   const uint64_t mine = merge_rounds(lk, ns, a.Lk, a.Lk, m, lane);
   const size_t o = ((size_t)b * kHeads + h) * a.topk;
   write_selection(mine, m, a.topk, lane, a.out_ids + o, a.out_scores + o);
+  if (a.out_pages != nullptr)
+    emit_pages(key_id(mine), lane < m, a.topk, lane, a.bt + (size_t)b * a.bt_stride, L,
+               a.out_pages + o * 8, a.out_tokens + (size_t)b * kHeads + h);
+}
+
+// ---------------------------------------------------------------------------------------
+// Page tables of given selections: one workgroup per row, wave h for head h.
+
+struct ExpandArgs {
+  const int32_t* ids;   // [batch][4][topk]
+  const int32_t* bt;
+  const int32_t* lens;
+  int32_t W, bt_stride, topk;
+  int32_t* out_pages;   // [batch][4][8 topk]
+  int32_t* out_tokens;  // [batch][4]
+};
+
+__global__ __launch_bounds__(kThreads) void expand_kernel(ExpandArgs a) {
+  const int b = blockIdx.x;
+  const int h = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int L = row_tokens(a.lens, b, a.W);
+  const int nb = (L + kBlock - 1) / kBlock;
+  const size_t bh = (size_t)b * kHeads + h;
+  const int id = lane < a.topk ? a.ids[bh * a.topk + lane] : -1;
+  emit_pages(id, id >= 0 && id < nb, a.topk, lane, a.bt + (size_t)b * a.bt_stride, L,
+             a.out_pages + bh * a.topk * 8, a.out_tokens + bh);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -774,6 +856,8 @@ SplitArgs make_split_args(const void* q, const void* k, const int32_t* bt, const
   a.keys = w ? reinterpret_cast<uint64_t*>(w + keys_offset(batch)) : nullptr;
   a.out_ids = nullptr;
   a.out_scores = nullptr;
+  a.out_pages = nullptr;
+  a.out_tokens = nullptr;
   a.scores = nullptr;
   return a;
 }
@@ -793,9 +877,22 @@ int32_t check_call(const void* q, const void* k, const int32_t* bt, const int32_
   return MSA_OK;
 }
 
+// Page-table outputs (both or neither): 16-byte aligned table, 4-byte aligned counts; the
+// block table must be there to read pages from, and 8 * page must fit 32 bits.
+int32_t check_pages(const int32_t* out_pages, const int32_t* out_tokens, const int32_t* bt,
+                    int32_t W, int64_t num_pages) {
+  if (!out_pages && !out_tokens) return MSA_OK;
+  if (!out_pages || !out_tokens || !aligned(out_pages, 16) || !aligned(out_tokens, 4))
+    return MSA_ERR_INVALID_ARG;
+  if (W > 0 && !bt) return MSA_ERR_INVALID_ARG;
+  if (num_pages > ((int64_t)1 << 28)) return MSA_ERR_UNSUPPORTED;
+  return MSA_OK;
+}
+
 int32_t merge_impl(const int32_t* lens, int32_t batch, int32_t W, int32_t topk, int32_t* out_ids,
                    float* out_scores, const void* ws, size_t ws_size, int32_t num_splits,
-                   hipStream_t st) {
+                   hipStream_t st, const int32_t* bt = nullptr, int32_t bt_stride = 0,
+                   int32_t* out_pages = nullptr, int32_t* out_tokens = nullptr) {
   if (batch < 0 || W < 0) return MSA_ERR_INVALID_ARG;
   if (topk < 1 || topk > MSA_MAX_TOPK) return MSA_ERR_INVALID_ARG;
   Plan p;
@@ -816,9 +913,45 @@ int32_t merge_impl(const int32_t* lens, int32_t batch, int32_t W, int32_t topk, 
   a.keys = reinterpret_cast<const uint64_t*>(static_cast<const char*>(ws) + keys_offset(batch));
   a.out_ids = out_ids;
   a.out_scores = out_scores;
+  a.bt = bt;
+  a.bt_stride = bt_stride;
+  a.out_pages = out_pages;
+  a.out_tokens = out_tokens;
   const size_t lds = (size_t)p.S * p.Lk * sizeof(uint64_t);
   hipLaunchKernelGGL(merge_kernel, dim3(kHeads, batch), dim3(64), lds, st, a);
   return hipGetLastError() == hipSuccess ? MSA_OK : MSA_ERR_HIP;
+}
+
+
+int32_t decode_impl(const void* q, const void* k_cache, const int32_t* block_table,
+                    const int32_t* seq_lens, int32_t batch, int32_t W, int32_t bt_stride,
+                    int64_t num_pages, int32_t topk, int32_t n_init, int32_t n_local,
+                    int32_t* out_ids, float* out_scores, int32_t* out_pages, int32_t* out_tokens,
+                    void* workspace, size_t workspace_bytes, int32_t num_splits, int32_t engine,
+                    hipStream_t st) {
+  // Check everything (outputs included) before the first launch.
+  if (batch > 0 && (!out_ids || !out_scores || !aligned(out_ids, 4) || !aligned(out_scores, 4)))
+    return MSA_ERR_INVALID_ARG;
+  if (engine < MSA_ENGINE_DEFAULT || engine > MSA_ENGINE_MFMA) return MSA_ERR_INVALID_ARG;
+  Plan p;
+  int32_t rc = check_call(q, k_cache, block_table, seq_lens, batch, W, bt_stride, num_pages, topk,
+                          n_init, n_local, workspace, workspace_bytes, num_splits, &p);
+  if (rc != MSA_OK) return rc;
+  if (batch > 0 && (rc = check_pages(out_pages, out_tokens, block_table, W, num_pages)) != MSA_OK)
+    return rc;
+  if (batch == 0) return MSA_OK;
+  SplitArgs a = make_split_args(q, k_cache, block_table, seq_lens, W, bt_stride, num_pages, p, topk,
+                                n_init, n_local, workspace, batch);
+  if (p.fused) {
+    a.out_ids = out_ids;
+    a.out_scores = out_scores;
+    a.out_pages = out_pages;
+    a.out_tokens = out_tokens;
+    return launch_split<kFused>(a, batch, engine, fused_lds_bytes(p), st);
+  }
+  if ((rc = launch_split<kSplit>(a, batch, engine, 0, st)) != MSA_OK) return rc;
+  return merge_impl(seq_lens, batch, W, topk, out_ids, out_scores, workspace, workspace_bytes,
+                    num_splits, st, block_table, bt_stride, out_pages, out_tokens);
 }
 
 }  // namespace
@@ -888,6 +1021,7 @@ int32_t msa_indexer_merge(const int32_t* seq_lens, int32_t batch, int32_t max_bl
                     workspace_bytes, num_splits, static_cast<hipStream_t>(stream));
 }
 
+
 int32_t msa_indexer_decode_engine(const void* q, const void* k_cache, const int32_t* block_table,
                                   const int32_t* seq_lens, int32_t batch,
                                   int32_t max_blocks_per_seq, int32_t bt_stride,
@@ -895,25 +1029,9 @@ int32_t msa_indexer_decode_engine(const void* q, const void* k_cache, const int3
                                   int32_t n_local, int32_t* out_ids, float* out_scores,
                                   void* workspace, size_t workspace_bytes, int32_t num_splits,
                                   int32_t engine, void* stream) {
-  // Check everything (outputs included) before the first launch.
-  if (batch > 0 && (!out_ids || !out_scores || !aligned(out_ids, 4) || !aligned(out_scores, 4)))
-    return MSA_ERR_INVALID_ARG;
-  if (engine < MSA_ENGINE_DEFAULT || engine > MSA_ENGINE_MFMA) return MSA_ERR_INVALID_ARG;
-  Plan p;
-  int32_t rc = check_call(q, k_cache, block_table, seq_lens, batch, max_blocks_per_seq, bt_stride,
-                          num_pages, topk, n_init, n_local, workspace, workspace_bytes, num_splits, &p);
-  if (rc != MSA_OK || batch == 0) return rc;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  SplitArgs a = make_split_args(q, k_cache, block_table, seq_lens, max_blocks_per_seq, bt_stride,
-                                num_pages, p, topk, n_init, n_local, workspace, batch);
-  if (p.fused) {
-    a.out_ids = out_ids;
-    a.out_scores = out_scores;
-    return launch_split<kFused>(a, batch, engine, fused_lds_bytes(p), st);
-  }
-  if ((rc = launch_split<kSplit>(a, batch, engine, 0, st)) != MSA_OK) return rc;
-  return merge_impl(seq_lens, batch, max_blocks_per_seq, topk, out_ids, out_scores, workspace,
-                    workspace_bytes, num_splits, st);
+  return decode_impl(q, k_cache, block_table, seq_lens, batch, max_blocks_per_seq, bt_stride,
+                     num_pages, topk, n_init, n_local, out_ids, out_scores, nullptr, nullptr,
+                     workspace, workspace_bytes, num_splits, engine, static_cast<hipStream_t>(stream));
 }
 
 int32_t msa_indexer_decode(const void* q, const void* k_cache, const int32_t* block_table,
@@ -921,9 +1039,49 @@ int32_t msa_indexer_decode(const void* q, const void* k_cache, const int32_t* bl
                            int32_t bt_stride, int64_t num_pages, int32_t topk, int32_t n_init,
                            int32_t n_local, int32_t* out_ids, float* out_scores, void* workspace,
                            size_t workspace_bytes, int32_t num_splits, void* stream) {
-  return msa_indexer_decode_engine(q, k_cache, block_table, seq_lens, batch, max_blocks_per_seq,
-                                   bt_stride, num_pages, topk, n_init, n_local, out_ids, out_scores,
-                                   workspace, workspace_bytes, num_splits, MSA_ENGINE_DEFAULT, stream);
+  return decode_impl(q, k_cache, block_table, seq_lens, batch, max_blocks_per_seq, bt_stride,
+                     num_pages, topk, n_init, n_local, out_ids, out_scores, nullptr, nullptr,
+                     workspace, workspace_bytes, num_splits, MSA_ENGINE_DEFAULT,
+                     static_cast<hipStream_t>(stream));
+}
+
+int32_t msa_indexer_decode_pages(const void* q, const void* k_cache, const int32_t* block_table,
+                                 const int32_t* seq_lens, int32_t batch,
+                                 int32_t max_blocks_per_seq, int32_t bt_stride, int64_t num_pages,
+                                 int32_t topk, int32_t n_init, int32_t n_local, int32_t* out_ids,
+                                 float* out_scores, int32_t* out_pages, int32_t* out_tokens,
+                                 void* workspace, size_t workspace_bytes, int32_t num_splits,
+                                 int32_t engine, void* stream) {
+  if (batch > 0 && (!out_pages || !out_tokens)) return MSA_ERR_INVALID_ARG;
+  return decode_impl(q, k_cache, block_table, seq_lens, batch, max_blocks_per_seq, bt_stride,
+                     num_pages, topk, n_init, n_local, out_ids, out_scores, out_pages, out_tokens,
+                     workspace, workspace_bytes, num_splits, engine, static_cast<hipStream_t>(stream));
+}
+
+int32_t msa_indexer_expand_pages(const int32_t* ids, const int32_t* block_table,
+                                 const int32_t* seq_lens, int32_t batch,
+                                 int32_t max_blocks_per_seq, int32_t bt_stride, int32_t topk,
+                                 int32_t* out_pages, int32_t* out_tokens, void* stream) {
+  if (batch < 0 || max_blocks_per_seq < 0 || bt_stride < max_blocks_per_seq) return MSA_ERR_INVALID_ARG;
+  if (topk < 1 || topk > MSA_MAX_TOPK) return MSA_ERR_INVALID_ARG;
+  if (max_blocks_per_seq > MSA_MAX_BLOCKS_PER_SEQ) return MSA_ERR_UNSUPPORTED;
+  if (batch == 0) return MSA_OK;
+  if (!ids || !seq_lens || !out_pages || !out_tokens || (!block_table && max_blocks_per_seq > 0))
+    return MSA_ERR_INVALID_ARG;
+  if (!aligned(ids, 4) || !aligned(seq_lens, 4) || !aligned(block_table, 4) ||
+      !aligned(out_pages, 16) || !aligned(out_tokens, 4))
+    return MSA_ERR_INVALID_ARG;
+  ExpandArgs a;
+  a.ids = ids;
+  a.bt = block_table;
+  a.lens = seq_lens;
+  a.W = max_blocks_per_seq;
+  a.bt_stride = bt_stride;
+  a.topk = topk;
+  a.out_pages = out_pages;
+  a.out_tokens = out_tokens;
+  hipLaunchKernelGGL(expand_kernel, dim3(batch), dim3(kThreads), 0, static_cast<hipStream_t>(stream), a);
+  return hipGetLastError() == hipSuccess ? MSA_OK : MSA_ERR_HIP;
 }
 
 int32_t msa_indexer_block_scores(const void* q, const void* k_cache, const int32_t* block_table,

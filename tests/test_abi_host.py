@@ -143,6 +143,69 @@ def test_stage_entry_points_reject_on_host(lib):
     assert lib.msa_indexer_read_error(None, ctypes.byref(ctypes.c_uint32()), None) == INVALID
 
 
+def _decode_pages(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, bt=FAKE, lens=FAKE, batch=2, W=8, stride=8, pages=16, topk=16,
+             n_init=1, n_local=2, ids=FAKE, scores=FAKE, pt=FAKE, tok=FAKE, ws=FAKE,
+             ws_bytes=1 << 20, splits=0, engine=0, stream=None)
+    a.update(kw)
+    return lib.msa_indexer_decode_pages(a["q"], a["k"], a["bt"], a["lens"], a["batch"], a["W"],
+                                        a["stride"], a["pages"], a["topk"], a["n_init"],
+                                        a["n_local"], a["ids"], a["scores"], a["pt"], a["tok"],
+                                        a["ws"], a["ws_bytes"], a["splits"], a["engine"],
+                                        a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(pt=None), INVALID),
+    (dict(tok=None), INVALID),
+    (dict(pt=FAKE + 4), INVALID),                # 16-byte alignment of the page table
+    (dict(tok=FAKE + 2), INVALID),
+    (dict(pages=(1 << 28) + 1), UNSUPPORTED),    # 8 * page would not fit int32
+    (dict(engine=3), INVALID),
+    (dict(ids=None), INVALID),
+    (dict(topk=65), INVALID),
+    (dict(ws_bytes=255), WS_SMALL),
+])
+def test_decode_pages_rejects_on_host(lib, kw, code):
+    assert _decode_pages(lib, **kw) == code
+
+
+def test_decode_pages_batch_zero_is_a_no_op(lib):
+    assert _decode_pages(lib, batch=0, q=None, k=None, bt=None, lens=None, ids=None, scores=None,
+                         pt=None, tok=None, ws=None, ws_bytes=0) == OK
+
+
+def _expand(lib, **kw):
+    a = dict(ids=FAKE, bt=FAKE, lens=FAKE, batch=2, W=8, stride=8, topk=16, pt=FAKE, tok=FAKE,
+             stream=None)
+    a.update(kw)
+    return lib.msa_indexer_expand_pages(a["ids"], a["bt"], a["lens"], a["batch"], a["W"],
+                                        a["stride"], a["topk"], a["pt"], a["tok"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ids=None), INVALID),
+    (dict(bt=None), INVALID),
+    (dict(lens=None), INVALID),
+    (dict(pt=None), INVALID),
+    (dict(tok=None), INVALID),
+    (dict(ids=FAKE + 2), INVALID),
+    (dict(pt=FAKE + 8), INVALID),
+    (dict(batch=-1), INVALID),
+    (dict(W=-1), INVALID),
+    (dict(stride=7), INVALID),
+    (dict(topk=0), INVALID),
+    (dict(topk=65), INVALID),
+    (dict(W=16385, stride=16385), UNSUPPORTED),
+])
+def test_expand_pages_rejects_on_host(lib, kw, code):
+    assert _expand(lib, **kw) == code
+
+
+def test_expand_pages_batch_zero_is_a_no_op(lib):
+    assert _expand(lib, batch=0, ids=None, bt=None, lens=None, pt=None, tok=None) == OK
+
+
 def test_binding_refuses_host_tensors():
     torch = pytest.importorskip("torch")
     from sparse_attention_block_amd import msa_indexer_decode

@@ -246,8 +246,11 @@ def test_workspace_reuse_and_counter_reset(msa):
         lens.copy_(torch.from_numpy(new_lens))
         ids, sc = msa.msa_indexer_decode(q, k, bt, lens, num_splits=ns, workspace=ws)
         torch.cuda.synchronize()
-        counters = ws[4:4 + 4 * 6].view(torch.int32).cpu().numpy()
-        assert np.all(counters == 0), (it, counters)
+        # error word in the 256-byte header, then one 256-byte counter line per row
+        header = ws[:256].view(torch.int32).cpu().numpy()
+        counters = ws[256:256 + 6 * 256].view(torch.int32).cpu().numpy().reshape(6, 64)
+        assert np.all(header == 0), (it, header[:4])
+        assert np.all(counters == 0), (it, counters[:, 0])
         cur = synth.Inputs("reuse", inp.q, inp.k_cache, inp.block_table, new_lens)
         ref = oracle.block_scores(cur.q, cur.k_cache, cur.block_table, cur.seq_lens)
         gpu_s = msa.msa_indexer_block_scores(q, k, bt, lens).cpu().numpy()
