@@ -69,6 +69,49 @@ def cpu_baseline(inp, repeats: int = 3):
     }
 
 
+def time_page_table(msa, torch, args, q, k, bt, lens, ids, ws, stream, topk, n_init, n_local,
+                    engine, B):
+    """The 16-token page table on the same workload: the decode step that also writes it
+    (msa_indexer_decode_pages, one launch), and the table alone from given selections
+    (msa_indexer_expand_pages). Both are timed like the main step."""
+    dev = q.device
+    sc = torch.empty((B, 4, topk), dtype=torch.float32, device=dev)
+    pages = torch.empty((B, 4, 8 * topk), dtype=torch.int32, device=dev)
+    tokens = torch.empty((B, 4), dtype=torch.int32, device=dev)
+
+    def dp():
+        msa.msa_indexer_decode_pages(q, k, bt, lens, topk, n_init, n_local, out_ids=ids,
+                                     out_scores=sc, out_pages=pages, out_tokens=tokens,
+                                     workspace=ws, engine=engine or 0)
+
+    def ex():
+        msa.msa_indexer_expand_pages(ids, bt, lens, out_pages=pages, out_tokens=tokens)
+
+    res = {}
+    for name, fn in (("decode_pages", dp), ("expand_pages", ex)):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        wall_us = (time.perf_counter() - t0) * 1e6 / args.steps
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        for e0, e1 in ev:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        res[name] = {"us_per_call": round(wall_us, 2),
+                     "kernel_us": round(statistics.mean(e0.elapsed_time(e1) for e0, e1 in ev) * 1e3, 2)}
+    # The table alone moves ids (read), table entries (gathered), pages and counts (written).
+    res["expand_pages"]["bytes_per_call"] = B * 4 * (topk * 4 + topk * 4 + topk * 32 + 4)
+    log(f"page table: {res}")
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -77,6 +120,10 @@ def main() -> int:
     ap.add_argument("--engine", type=int, default=0, help="0 default, 1 VALU dot2, 2 MFMA")
     ap.add_argument("--splits", type=int, default=0, help="0 = automatic split count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--step", choices=("decode", "decode_pages"), default="decode",
+                    help="the call timed as one step (decode_pages also writes the 16-token page table)")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip timing the page-table entry points")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a 1 GiB device copy (for scaling HBM counters)")
     args = ap.parse_args()
@@ -127,12 +174,20 @@ def main() -> int:
     stream = torch.cuda.current_stream()
     engine_arg = args.engine if args.engine else None
 
+    pt = torch.empty((B, 4, 8 * topk), dtype=torch.int32, device=dev)
+    ptok = torch.empty((B, 4), dtype=torch.int32, device=dev)
+
     def step(ev0=None, ev1=None):
         # A fused plan is one kernel launch per step (the last split of each row merges
         # it); otherwise stage 1 is timed alone and stage 2 follows it.
         if ev0 is not None:
             ev0.record(stream)
-        if plan["fused"]:
+        if plan["fused"] and args.step == "decode_pages":
+            msa.msa_indexer_decode_pages(q, k, bt, lens, topk, n_init, n_local, out_ids=ids,
+                                         out_scores=sc, out_pages=pt, out_tokens=ptok,
+                                         workspace=ws, num_splits=args.splits,
+                                         engine=args.engine)
+        elif plan["fused"]:
             msa.msa_indexer_decode(q, k, bt, lens, topk, n_init, n_local, out_ids=ids, out_scores=sc,
                                    workspace=ws, num_splits=args.splits, engine=engine_arg)
         else:
@@ -170,6 +225,11 @@ def main() -> int:
         log("device error flag set")
         return 1
 
+    extra = {}
+    if plan["fused"] and not args.no_extra:
+        extra = time_page_table(msa, torch, args, q, k, bt, lens, ids, ws, stream, topk, n_init,
+                                n_local, engine_arg, B)
+
     ms_per_step = elapsed * 1e3 / args.steps
     us_per_step = ms_per_step * 1e3
     gbs = nbytes / (ms_per_step * 1e-3) / 1e9
@@ -200,6 +260,8 @@ def main() -> int:
             "block_tokens": 128, "topk": topk, "n_init": n_init, "n_local": n_local,
             "num_splits": splits, "blocks_per_split": plan["blocks_per_split"],
             "fused_merge": plan["fused"], "engine": engine, "index_k_bytes": nbytes,
+            "step_call": "msa_indexer_decode_pages" if args.step == "decode_pages" and plan["fused"]
+                         else "msa_indexer_decode",
         },
         "roofline": {
             "kernel": ("split_kernel, fused: block scores + per-split top-16 + merge by each row's "
@@ -215,6 +277,8 @@ def main() -> int:
             "algorithmic_bytes_per_launch": nbytes,
         },
     }
+    if extra:
+        out["page_table"] = extra
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on the same workload")
         out["cpu_baseline"] = cpu_baseline(inp)
