@@ -34,6 +34,9 @@ class Oracle:
         lib.msa_oracle_select.restype = ctypes.c_int
         lib.msa_oracle_expand_pages.argtypes = [P, P, P, i32, i32, i32, i32, P, P]
         lib.msa_oracle_expand_pages.restype = ctypes.c_int
+        lib.msa_oracle_decode_multi.argtypes = [P, P, P, P, i32, i32, i32, i64, i32, i32, i32, i32,
+                                                 P, P, P]
+        lib.msa_oracle_decode_multi.restype = ctypes.c_int
         lib.msa_oracle_num_threads.argtypes = []
         lib.msa_oracle_num_threads.restype = ctypes.c_int
         self.lib = lib
@@ -87,8 +90,32 @@ class Oracle:
             raise ValueError(f"oracle expand_pages failed with code {rc}")
         return pages, tokens
 
+    def decode_multi(self, q, k_cache, block_table, seq_lens, topk: int, n_init: int, n_local: int):
+        """Multi-token decode, q [B, Q, 4, 128]: (ids int32 [B,Q,4,topk], selected scores fp64
+        [B,Q,4,topk], block scores fp64 [B,Q,4,W])."""
+        q = np.ascontiguousarray(q, dtype=np.uint16)
+        k_cache = np.ascontiguousarray(k_cache, dtype=np.uint16)
+        block_table = np.ascontiguousarray(block_table, dtype=np.int32)
+        seq_lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+        B, W = block_table.shape
+        assert q.ndim == 4 and q.shape[0] == B and q.shape[2:] == (HEADS, 128)
+        Q = q.shape[1]
+        blocks = np.empty((B, Q, HEADS, W), dtype=np.float64)
+        ids = np.empty((B, Q, HEADS, topk), dtype=np.int32)
+        sc = np.empty((B, Q, HEADS, topk), dtype=np.float64)
+        rc = self.lib.msa_oracle_decode_multi(_ptr(q), _ptr(k_cache), _ptr(block_table),
+                                              _ptr(seq_lens), B, W, W, k_cache.shape[0], Q, topk,
+                                              n_init, n_local, _ptr(blocks), _ptr(ids), _ptr(sc))
+        if rc != 0:
+            raise ValueError(f"oracle decode_multi failed with code {rc}")
+        return ids, sc, blocks
+
     def decode(self, inp):
-        """Whole pass on a synth.Inputs: (ids, selected scores, block scores)."""
+        """Whole pass on a synth.Inputs: (ids, selected scores, block scores). Inputs with
+        several query positions (q [B, Q, 4, 128]) go through decode_multi."""
+        if inp.q.ndim == 4:
+            return self.decode_multi(inp.q, inp.k_cache, inp.block_table, inp.seq_lens, inp.topk,
+                                     inp.n_init, inp.n_local)
         s = self.block_scores(inp.q, inp.k_cache, inp.block_table, inp.seq_lens)
         ids, sc = self.select(s, inp.seq_lens, inp.topk, inp.n_init, inp.n_local)
         return ids, sc, s
@@ -125,3 +152,7 @@ def decode(inp):
 
 def expand_pages(ids, block_table, seq_lens):
     return default().expand_pages(ids, block_table, seq_lens)
+
+
+def decode_multi(q, k_cache, block_table, seq_lens, topk: int, n_init: int, n_local: int):
+    return default().decode_multi(q, k_cache, block_table, seq_lens, topk, n_init, n_local)

@@ -52,6 +52,15 @@
  *                 past the selected blocks are -1; the table's token count is the sum of
  *                 the selected blocks' valid tokens.
  *
+ *   multi-token   a row that verifies Q draft tokens (speculative decoding) carries Q query
+ *   decode        positions q[b][p], p < Q, the last Q tokens of its context (vLLM blog
+ *                 "Following the Bottleneck", section 2: one workgroup per request scores all
+ *                 draft positions; vLLM PR #57832, Test Plan: query_len 4 verifies). Under the
+ *                 causal clamp min(q_end + offset_q, kv_len) of TensorRT-LLM PR #17008
+ *                 ("Description"), position p sees the first L_p = L - (Q - 1 - p) tokens,
+ *                 L the row's clamped length (L_p floored at 0). Each (b, p, h) is exactly the
+ *                 single-token pass above with q[b][p] and length L_p.
+ *
  * bf16 inputs are widened exactly (bits << 16 is the fp32 value; fp32 -> fp64
  * is exact), products of two bf16 values are exact in fp64, and the 128-term
  * sums are accumulated in fp64.
@@ -267,4 +276,54 @@ int msa_oracle_expand_pages(const int32_t *ids, const int32_t *block_table, cons
         tokens[bh] = (int32_t)count;
     }
     return OR_OK;
+}
+
+/*
+ * Multi-token decode: q[b][p][h][d] for p < qlen; block scores out_blocks[b][p][h][j]
+ * (j < max_blocks), selections out_ids / out_scores [b][p][h][topk]. Each position is run
+ * through msa_oracle_decode with its own query and causal length.
+ */
+int msa_oracle_decode_multi(const uint16_t *q, const uint16_t *k_cache,
+                            const int32_t *block_table, const int32_t *seq_lens,
+                            int32_t batch, int32_t max_blocks, int32_t bt_stride,
+                            int64_t num_pages, int32_t qlen, int32_t topk, int32_t n_init,
+                            int32_t n_local, double *out_blocks, int32_t *out_ids,
+                            double *out_scores)
+{
+    if (batch < 0 || max_blocks < 0 || qlen < 1 || topk < 1) return OR_ERR_ARG;
+    size_t nb_q = (size_t)batch * OR_HEADS * OR_DIM;
+    size_t nb_s = (size_t)batch * OR_HEADS * (size_t)max_blocks;
+    size_t nb_k = (size_t)batch * OR_HEADS * (size_t)topk;
+    uint16_t *qp = (uint16_t *)malloc((nb_q ? nb_q : 1) * sizeof(uint16_t));
+    int32_t *lens_p = (int32_t *)malloc((batch ? batch : 1) * sizeof(int32_t));
+    double *sc = (double *)malloc((nb_s ? nb_s : 1) * sizeof(double));
+    int32_t *ids = (int32_t *)malloc((nb_k ? nb_k : 1) * sizeof(int32_t));
+    double *sel = (double *)malloc((nb_k ? nb_k : 1) * sizeof(double));
+    int rc = (qp && lens_p && sc && ids && sel) ? OR_OK : OR_ERR_ARG;
+    for (int32_t p = 0; p < qlen && rc == OR_OK; ++p) {
+        for (int32_t b = 0; b < batch; ++b) {
+            int64_t L = row_len(seq_lens, b, max_blocks) - (qlen - 1 - p);
+            lens_p[b] = (int32_t)(L > 0 ? L : 0);
+            memcpy(qp + (size_t)b * OR_HEADS * OR_DIM,
+                   q + ((size_t)b * qlen + p) * OR_HEADS * OR_DIM,
+                   OR_HEADS * OR_DIM * sizeof(uint16_t));
+        }
+        rc = msa_oracle_decode(qp, k_cache, block_table, lens_p, batch, max_blocks, bt_stride,
+                               num_pages, topk, n_init, n_local, sc, ids, sel);
+        for (int32_t b = 0; b < batch && rc == OR_OK; ++b) {
+            size_t o = (size_t)b * qlen + p;
+            memcpy(out_blocks + o * OR_HEADS * max_blocks, sc + (size_t)b * OR_HEADS * max_blocks,
+                   (size_t)OR_HEADS * max_blocks * sizeof(double));
+            memcpy(out_ids + o * OR_HEADS * topk, ids + (size_t)b * OR_HEADS * topk,
+                   (size_t)OR_HEADS * topk * sizeof(int32_t));
+            memcpy(out_scores + o * OR_HEADS * topk, sel + (size_t)b * OR_HEADS * topk,
+                   (size_t)OR_HEADS * topk * sizeof(double));
+        }
+    }
+    free(qp);
+    free(lens_p);
+    free(sc);
+    free(ids);
+    free(sel);
+    return rc;
 }

@@ -6,6 +6,8 @@ CPU oracle can both consume exactly the same bf16 bits from it.
 
 Layouts (row-major, as both sides read them):
   q            uint16 [B, 4, 128]        bf16 bit patterns, one decode token per row
+               uint16 [B, Q, 4, 128]     or Q query positions per row (multi-token decode:
+                                         the row's last Q context tokens are draft tokens)
   k_cache      uint16 [P, 128, 128]      bf16 bit patterns, page-major, token-major
   block_table  int32  [B, W]             logical block j of row b -> physical page
   seq_lens     int32  [B]                tokens in row b's context (0 .. W*128)
@@ -82,6 +84,11 @@ class Inputs:
         return int(self.q.shape[0])
 
     @property
+    def qlen(self) -> int:
+        """Query positions per row (1 for single-token decode)."""
+        return 1 if self.q.ndim == 3 else int(self.q.shape[1])
+
+    @property
     def max_blocks(self) -> int:
         return int(self.block_table.shape[1])
 
@@ -149,6 +156,85 @@ def paged_case(seed: int, seq_lens, max_blocks: int, *, permute: bool = True,
     return Inputs(name or f"paged(seed={seed},B={B},W={W})", q, k, bt, lens,
                   topk=topk, n_init=n_init, n_local=n_local,
                   meta={"poison_page": poison_page if poison else None})
+
+
+def multi_case(seed: int, seq_lens, max_blocks: int, qlen: int, **kw) -> Inputs:
+    """paged_case with qlen query positions per row: q ~N(0,1) bf16 [B, qlen, 4, 128]."""
+    inp = paged_case(seed, seq_lens, max_blocks, **kw)
+    inp.q = normal_bf16(seed, 4, (inp.batch, qlen, HEADS, DIM))
+    inp.name = kw.get("name") or f"multi(seed={seed},B={inp.batch},W={inp.max_blocks},Q={qlen})"
+    return inp
+
+
+def multi_planted(qlen: int = 4) -> Inputs:
+    """Batch 16, 8576..8704 tokens (68-block table), qlen draft positions, exact integer scores.
+
+    q[b,p,h,:] is +-1 and background index-K entries are uniform in {-1, 0, +1}, so every
+    score is an exact integer. Planted, for each row:
+      * for each (position p, head h), a run of 16 blocks at a seeded start whose token slot
+        4p+h holds q[b,p,h,:] with all but its first T entries zeroed (score exactly T for
+        (p, h); T in 100..115, ties included);
+      * the draft tokens themselves: the token at absolute index L-qlen+i holds q[b,0,i%4,:]
+        in full (score 128 for position 0, head i%4), so position 0 must see it only for
+        i = 0 (causally, position p sees the first L-(qlen-1-p) tokens);
+      * rows 3 and 11: q[b,qlen-1,h,:] in the invalid tail slots of the partial last block.
+    Lengths put the boundary between positions' block counts in every place: some rows have
+    position 0 one block short of the others.
+    """
+    B, W = 16, 68
+    seed = 6
+    lens = np.array([8700, 8704, 128 * 67 + 1, 128 * 67 + 2, 128 * 67 + 3, 128 * 67 + 4,
+                     8699, 8577, 8578, 8579, 8600, 8650, 8701, 8702, 8703, 8576], dtype=np.int32)
+    sgn = _child(seed, 0).standard_normal((B, qlen, HEADS, DIM))
+    qf = np.where(sgn >= 0, 1.0, -1.0).astype(np.float32)
+    nb = _nblocks(lens)
+    n_pages = int(nb.sum()) + 1
+    kf = _child(seed, 1).integers(-1, 2, size=(n_pages, BLOCK, DIM)).astype(np.float32)
+    order = _child(seed, 2).permutation(n_pages).astype(np.int32)
+    spare = int(order[-1])
+    bt = np.full((B, W), spare, dtype=np.int32)
+    pos = 0
+    for b in range(B):
+        bt[b, :nb[b]] = order[pos:pos + nb[b]]
+        pos += int(nb[b])
+    rng = _child(seed, 3)
+    planted = {}
+    for b in range(B):
+        L = int(lens[b])
+        for p in range(qlen):
+            for h in range(HEADS):
+                w0 = int(rng.integers(0, nb[b] - 2 - 16 + 1))
+                kind = int(rng.integers(0, 3))
+                if kind == 0:
+                    targets = [100] * 16
+                elif kind == 1:
+                    targets = list(range(115, 99, -1))
+                else:
+                    targets = [100 + int(t) for t in rng.integers(0, 4, size=16)]
+                for i, t in enumerate(targets):
+                    tok = qf[b, p, h].copy()
+                    tok[t:] = 0.0
+                    kf[bt[b, w0 + i], 4 * p + h] = tok
+                    planted[(b, p, h, w0 + i)] = t
+        for i in range(qlen):
+            a = L - qlen + i
+            if a >= 0:
+                kf[bt[b, a // BLOCK], a % BLOCK] = qf[b, 0, i % HEADS]
+        if b in (3, 11):
+            last = (L - 1) // BLOCK
+            for t in range(L - last * BLOCK, BLOCK):
+                kf[bt[b, last], t] = qf[b, qlen - 1, t % HEADS]
+    return Inputs(f"multi planted B=16 Q={qlen}", bf16_bits(qf), bf16_bits(kf), bt, lens,
+                  meta={"planted": planted})
+
+
+def multi_config(qlen: int = 4) -> Inputs:
+    """The benchmark shape with qlen draft positions per row: batch 32 x 131072 tokens (1024
+    blocks, 1 GiB of index-K, the same cache as config3), q ~N(0,1) [32, qlen, 4, 128]."""
+    inp = config3()
+    inp.q = normal_bf16(3, 5, (inp.batch, qlen, HEADS, DIM))
+    inp.name = f"B=32 x 131072, Q={qlen}"
+    return inp
 
 
 # ---------------------------------------------------------------------------

@@ -44,6 +44,12 @@ MUTANTS = {
     "ids_past_row_kept": ("if (j >= 0 && j < nb) sel[n++] = j;", "if (j >= 0 && j < max_blocks) sel[n++] = j;"),
     "repeats_dropped": ("if (j >= 0 && j < nb) sel[n++] = j;",
                         "if (j >= 0 && j < nb && (n == 0 || sel[n - 1] != j)) sel[n++] = j;"),
+    "causal_reversed": ("int64_t L = row_len(seq_lens, b, max_blocks) - (qlen - 1 - p);",
+                        "int64_t L = row_len(seq_lens, b, max_blocks) - p;"),
+    "causal_off_by_one": ("int64_t L = row_len(seq_lens, b, max_blocks) - (qlen - 1 - p);",
+                          "int64_t L = row_len(seq_lens, b, max_blocks) - (qlen - p);"),
+    "positions_swapped": ("q + ((size_t)b * qlen + p) * OR_HEADS * OR_DIM",
+                          "q + ((size_t)b * qlen + (qlen - 1 - p)) * OR_HEADS * OR_DIM"),
     "tokens_full_blocks": ("count += valid > OR_BLOCK ? OR_BLOCK : valid;", "count += OR_BLOCK;"),
 }
 

@@ -439,3 +439,126 @@ def pin_expand_pages_invariants(orc):
                 assert list(got[i]) == [8 * p + t for t in range(8)]
             assert np.all(got[len(sel):] == -1)
             assert tokens[b, h] == sum(min(128, L - 128 * j) for j in sel)
+
+
+# ---------------------------------------------------------------------------
+# Multi-token decode (vLLM blog "Following the Bottleneck", section 2; TensorRT-LLM PR
+# #17008, Description: the causal clamp).
+
+def brute_scores_causal(inp: synth.Inputs) -> np.ndarray:
+    """Block scores of every (row, position, head) from an attention mask over absolute token
+    positions: the row's context is tokens 0 .. L-1 and its Q query positions are the last Q
+    of them, at absolute positions L-Q .. L-1; query position a sees the tokens t <= a."""
+    qf = synth.bf16_to_f32(inp.q).astype(np.float64)       # [B, Q, 4, 128]
+    kf = synth.bf16_to_f32(inp.k_cache).astype(np.float64)
+    B, W = inp.block_table.shape
+    Q = qf.shape[1]
+    out = np.full((B, Q, 4, W), -np.inf)
+    for b in range(B):
+        L = int(min(max(inp.seq_lens[b], 0), W * 128))
+        if L == 0:
+            continue
+        nb = -(-L // 128)
+        pages = inp.block_table[b, :nb]
+        ctx = kf[pages].reshape(nb * 128, 128)               # token t of the row at row t
+        s = np.einsum("phd,td->pht", qf[b], ctx)             # [Q, 4, nb*128]
+        t = np.arange(nb * 128)
+        for p in range(Q):
+            a = L - Q + p                                    # absolute position of query p
+            masked = np.where(t[None, :] <= a, s[p], -np.inf)  # [4, nb*128]
+            blk = masked.reshape(4, nb, 128).max(axis=2)
+            out[b, p, :, :nb] = blk
+    return out
+
+
+def multi_small_cases():
+    return [
+        synth.multi_case(21, [300, 128, 1, 0, 1000, 257, 3, 129, 130], 8, 4),
+        synth.multi_case(22, [128 * 5, 77, 2], 5, 3, permute=False),
+        synth.multi_case(23, [4000, 3000, 129, 4], 32, 2, extra_pages=7),
+    ]
+
+
+@pin
+def pin_multi_block_scores_match_causal_brute_force(orc):
+    # Each query position's block scores equal the attention-mask formulation, including rows
+    # shorter than Q (early positions see nothing) and block edges between positions.
+    for inp in multi_small_cases():
+        _, _, got = orc.decode(inp)
+        want = brute_scores_causal(inp)
+        assert np.array_equal(np.isinf(got), np.isinf(want))
+        fin = np.isfinite(want)
+        np.testing.assert_allclose(got[fin], want[fin], rtol=0, atol=1e-9)
+
+
+@pin
+def pin_multi_selection_follows_each_positions_blocks(orc):
+    # Position p's selection covers exactly the blocks with a visible token (from the brute
+    # force's mask), its own first / last blocks are pinned, and with nothing pinned it is
+    # np.lexsort of the brute-force scores.
+    for inp in multi_small_cases():
+        want = brute_scores_causal(inp)
+        ids, sc, _ = orc.decode(inp)
+        inp0 = synth.Inputs(inp.name, inp.q, inp.k_cache, inp.block_table, inp.seq_lens,
+                            topk=inp.topk, n_init=0, n_local=0)
+        ids0, _, _ = orc.decode(inp0)
+        B, Q = inp.q.shape[:2]
+        for b in range(B):
+            for p in range(Q):
+                for h in range(4):
+                    vis = np.flatnonzero(np.isfinite(want[b, p, h]))
+                    nbp = len(vis)
+                    assert np.array_equal(vis, np.arange(nbp))
+                    m = min(inp.topk, nbp)
+                    got = ids[b, p, h]
+                    assert np.all(got[m:] == -1) and len(set(got[:m])) == m
+                    pins = set(range(min(inp.n_init, nbp))) | set(range(max(nbp - inp.n_local, 0), nbp))
+                    assert pins <= set(got[:m].tolist())
+                    order = np.lexsort((np.arange(nbp), -want[b, p, h, :nbp]))[:m]
+                    assert list(ids0[b, p, h, :m]) == list(order)
+
+
+@pin
+def pin_multi_one_position_is_single_token(orc):
+    inp = synth.paged_case(24, [300, 1000, 0, 128], 8)
+    ids1, sc1, s1 = orc.decode(inp)
+    multi = synth.Inputs(inp.name, inp.q[:, None], inp.k_cache, inp.block_table, inp.seq_lens)
+    ids, sc, s = orc.decode(multi)
+    assert np.array_equal(ids[:, 0], ids1) and np.array_equal(sc[:, 0], sc1)
+    assert np.array_equal(s[:, 0], s1)
+
+
+@pin
+def pin_multi_planted(orc):
+    # Exact integer scores. Closed forms: (1) the draft token at absolute position L-Q holds
+    # q[b,0,0], so position 0, head 0 scores exactly 128 on its block; the draft tokens after it
+    # hold q[b,0,i%4] but lie past position 0's causal end, so they never reach 128 for
+    # position 0. (2) Rows 3 and 11 hold q[b,Q-1,h] in the masked tail of their last block,
+    # which must not score. (3) Outside the pinned blocks, position p / head h selects its
+    # planted run's best blocks: targets descending, ids ascending among ties.
+    inp = synth.multi_planted()
+    ids, sc, s = orc.decode(inp)
+    Q = inp.qlen
+    planted = inp.meta["planted"]
+    for b in range(inp.batch):
+        L = int(inp.seq_lens[b])
+        assert s[b, 0, 0, (L - Q) // 128] == 128.0
+        for i in range(1, Q):
+            j = (L - Q + i) // 128
+            if i % 4 != 0:
+                assert s[b, 0, i % 4, j] < 100.0
+        if b in (3, 11):
+            for h in range(4):
+                assert s[b, Q - 1, h, (L - 1) // 128] < 100.0
+        for p in range(Q):
+            Lp = L - (Q - 1 - p)
+            nbp = -(-Lp // 128)
+            pins = {0, nbp - 2, nbp - 1}
+            for h in range(4):
+                got = ids[b, p, h]
+                assert set(got[:3].tolist()) == pins
+                runs = sorted(((t, j) for (bb, pp, hh, j), t in planted.items()
+                               if (bb, pp, hh) == (b, p, h) and j not in pins),
+                              key=lambda x: (-x[0], x[1]))
+                assert [j for _, j in runs[:13]] == list(got[3:16])
+                assert [float(t) for t, _ in runs[:13]] == list(sc[b, p, h, 3:16])
