@@ -63,8 +63,9 @@ def cpu_baseline(inp, repeats: int = 3):
         "unit": "GB/s",
         "cores": oracle.num_threads(),
         "kind": "oracle",
-        "sample": f"the whole workload (all {inp.batch} rows x {inp.max_blocks} blocks), "
-                  f"median of {repeats} passes of scores + selection, fp64, {t * 1e3:.1f} ms/pass",
+        "sample": f"the whole workload (all {inp.batch} rows x {inp.max_blocks} blocks"
+                  f"{' x %d positions' % inp.qlen if inp.qlen > 1 else ''}), median of {repeats} "
+                  f"passes of scores + selection, fp64, {t * 1e3:.1f} ms/pass",
         "ms_per_step": round(t * 1e3, 3),
     }
 
@@ -112,6 +113,97 @@ def time_page_table(msa, torch, args, q, k, bt, lens, ids, ws, stream, topk, n_i
     return res
 
 
+def bench_multi(args, msa, synth, np, torch) -> int:
+    """Multi-token decode step (qlen draft positions per row) over the benchmark's cache."""
+    Q = args.qlen
+    log(f"generating the batch 32 x 131072 workload with {Q} query positions per row")
+    inp = synth.multi_config(Q)
+    B, W, topk, n_init, n_local = inp.batch, inp.max_blocks, inp.topk, inp.n_init, inp.n_local
+    nbytes = inp.index_k_bytes
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    q = torch.from_numpy(inp.q.view(np.int16)).to(dev).view(torch.bfloat16)
+    k = torch.from_numpy(inp.k_cache.view(np.int16)).to(dev).view(torch.bfloat16)
+    bt = torch.from_numpy(inp.block_table).to(dev)
+    lens = torch.from_numpy(inp.seq_lens).to(dev)
+    plan = msa.plan(B, W, topk, args.splits)
+    ws = torch.zeros(msa.workspace_bytes_multi(B, W, Q, topk, args.splits), dtype=torch.uint8,
+                     device=dev)
+    ids = torch.empty((B, Q, 4, topk), dtype=torch.int32, device=dev)
+    sc = torch.empty((B, Q, 4, topk), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    log(f"inputs resident in HBM; plan {plan}")
+
+    def step():
+        msa.msa_indexer_decode_multi(q, k, bt, lens, topk, n_init, n_local, out_ids=ids,
+                                     out_scores=sc, workspace=ws, num_splits=args.splits)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    k_ms = statistics.mean(e0.elapsed_time(e1) for e0, e1 in ev)
+    if msa.msa_indexer_read_error(ws) != 0:
+        log("device error flag set")
+        return 1
+    ms_per_step = elapsed * 1e3 / args.steps
+    gbs = nbytes / (ms_per_step * 1e-3) / 1e9
+    k_gbs = nbytes / (k_ms * 1e-3) / 1e9
+    out = {
+        "metric": f"µs/verify step ({Q} draft positions per row) + index-K GB/s (% of 8 TB/s) "
+                  "at batch 32 × 128K ctx",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 q and index-K, shuffled page table)",
+        "config": {
+            "workload": f"batch 32 x 131072-token rows, {Q} query positions each (causal), 1024 "
+                        "blocks of 128 tokens, 4 index heads x 128, top-16, 1 initial + 2 recent "
+                        "blocks pinned",
+            "batch": B, "qlen": Q, "seq_len": int(inp.seq_lens[0]), "topk": topk,
+            "num_splits": plan["splits"], "blocks_per_split": plan["blocks_per_split"],
+            "index_k_bytes": nbytes, "step_call": "msa_indexer_decode_multi",
+        },
+        "roofline": {
+            "kernel": "verify_kernel + verify_merge_kernel (the whole step, timed together)",
+            "bound": "hbm",
+            "achieved": round(k_gbs, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(k_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel_us": round(k_ms * 1e3, 2),
+            "algorithmic_bytes_per_launch": nbytes,
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on the same workload")
+        out["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -122,6 +214,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--step", choices=("decode", "decode_pages"), default="decode",
                     help="the call timed as one step (decode_pages also writes the 16-token page table)")
+    ap.add_argument("--qlen", type=int, default=1,
+                    help="query positions per row; above 1 the step is a multi-token (draft verify) "
+                         "decode of the same cache, msa_indexer_decode_multi")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip timing the page-table entry points")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -150,6 +245,8 @@ def main() -> int:
     from sparse_attention_block_amd import synth
 
     lib = msa.load()  # raises if the HIP library is not built
+    if args.qlen != 1:
+        return bench_multi(args, msa, synth, np, torch)
     log("generating the batch 32 x 131072 workload (1 GiB of bf16 index-K)")
     t0 = time.time()
     inp = synth.config3()

@@ -65,6 +65,7 @@ extern "C" {
 /* Limits of this build. */
 #define MSA_MAX_TOPK 64
 #define MSA_MAX_BLOCKS_PER_SEQ 16384     /* 2M tokens per row */
+#define MSA_MAX_QUERY_LEN 4              /* query positions per row in the multi-token calls */
 
 /* Block-scoring engines (msa_indexer_split_topk / msa_indexer_block_scores). */
 #define MSA_ENGINE_DEFAULT 0                /* the VALU engine */
@@ -200,6 +201,53 @@ int32_t msa_indexer_expand_pages(const int32_t *ids, const int32_t *block_table,
                                  const int32_t *seq_lens, int32_t batch,
                                  int32_t max_blocks_per_seq, int32_t bt_stride, int32_t topk,
                                  int32_t *out_pages, int32_t *out_tokens, void *stream);
+
+/*
+ * Workspace bytes of msa_indexer_decode_multi (0 on invalid arguments): the layout of
+ * msa_indexer_workspace_bytes with keys uint64 [batch][S][qlen*4][Lk]. Zeroed once before
+ * its first use, like the single-token workspace.
+ */
+size_t msa_indexer_workspace_bytes_multi(int32_t batch, int32_t max_blocks_per_seq, int32_t qlen,
+                                         int32_t topk, int32_t num_splits);
+
+/*
+ * Multi-token decode: a row that verifies qlen draft tokens (speculative decoding) carries
+ * qlen query positions, the last qlen tokens of its context (vLLM PR #57832, Test Plan:
+ * query_len 4 verifies; vLLM blog "Following the Bottleneck", section 2: one workgroup per
+ * request scores all draft positions from one read of the keys).
+ *   q            bf16 [batch][qlen][4][128], contiguous, 16-byte aligned.
+ *   qlen         1 .. MSA_MAX_QUERY_LEN.
+ *   seq_lens     context tokens of row b, the qlen draft tokens included; clamped to
+ *                [0, max_blocks_per_seq*128] first. Position p then sees the first
+ *                L_p = max(0, len_b - (qlen-1-p)) tokens (the causal clamp
+ *                min(q_end + offset_q, kv_len) of TensorRT-LLM PR #17008, Description).
+ *   out_ids, out_scores  int32 / fp32 [batch][qlen][4][topk]: for every (b, p, h), exactly
+ *                what msa_indexer_decode returns for query q[b][p] and length L_p (its own
+ *                block count, pinned blocks and padding).
+ *   workspace    at least msa_indexer_workspace_bytes_multi(...) bytes, 256-byte aligned.
+ * Every other argument as in msa_indexer_decode. Each page is read once for all positions
+ * and heads (MFMA: 4 positions x 4 heads fill the 16 rows of v_mfma_f32_16x16x32_bf16).
+ * Two launches: per-split top-k of every (position, head), then one wave per (b, p, h)
+ * merging the splits' lists.
+ */
+int32_t msa_indexer_decode_multi(const void *q, const void *k_cache, const int32_t *block_table,
+                                 const int32_t *seq_lens, int32_t batch,
+                                 int32_t max_blocks_per_seq, int32_t bt_stride, int64_t num_pages,
+                                 int32_t qlen, int32_t topk, int32_t n_init, int32_t n_local,
+                                 int32_t *out_ids, float *out_scores, void *workspace,
+                                 size_t workspace_bytes, int32_t num_splits, void *stream);
+
+/*
+ * Test and debugging aid for the multi-token pass: fp32 block scores
+ * out[b][p][h][j], [batch][qlen][4][max_blocks_per_seq], -inf for blocks position p does not
+ * see (j >= ceil(L_p / 128)) and for pages out of range. Same scoring code as
+ * msa_indexer_decode_multi.
+ */
+int32_t msa_indexer_block_scores_multi(const void *q, const void *k_cache,
+                                       const int32_t *block_table, const int32_t *seq_lens,
+                                       int32_t batch, int32_t max_blocks_per_seq,
+                                       int32_t bt_stride, int64_t num_pages, int32_t qlen,
+                                       float *out, int32_t num_splits, void *stream);
 
 /*
  * Stage 1 of msa_indexer_decode alone (never fused): one workgroup per (row, split) scores its blocks

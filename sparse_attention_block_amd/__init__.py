@@ -11,7 +11,9 @@ from ._lib import (  # noqa: F401
     MsaError,
     load,
     msa_indexer_block_scores,
+    msa_indexer_block_scores_multi,
     msa_indexer_decode,
+    msa_indexer_decode_multi,
     msa_indexer_decode_pages,
     msa_indexer_expand_pages,
     msa_indexer_merge,
@@ -22,4 +24,5 @@ from ._lib import (  # noqa: F401
     plan,
     status_string,
     workspace_bytes,
+    workspace_bytes_multi,
 )

@@ -46,6 +46,11 @@ _SIGNATURES = {
     "msa_indexer_decode_pages": ([_P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32, _I32, _P, _P,
                                   _P, _P, _P, _SZ, _I32, _I32, _P], _I32),
     "msa_indexer_expand_pages": ([_P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _P], _I32),
+    "msa_indexer_workspace_bytes_multi": ([_I32, _I32, _I32, _I32, _I32], _SZ),
+    "msa_indexer_decode_multi": ([_P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32, _I32, _I32, _P,
+                                  _P, _P, _SZ, _I32, _P], _I32),
+    "msa_indexer_block_scores_multi": ([_P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _P, _I32, _P],
+                                       _I32),
     "msa_indexer_split_topk": ([_P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32, _I32, _P, _SZ,
                                 _I32, _I32, _P], _I32),
     "msa_indexer_merge": ([_P, _I32, _I32, _I32, _P, _P, _P, _SZ, _I32, _P], _I32),
@@ -245,6 +250,64 @@ def msa_indexer_expand_pages(ids, block_table, seq_lens, out_pages=None, out_tok
         _dev(out_tokens, "out_tokens", torch.int32, (B, HEADS)), _stream(stream))
     _check("msa_indexer_expand_pages", rc)
     return out_pages, out_tokens
+
+
+def workspace_bytes_multi(batch: int, max_blocks: int, qlen: int, topk: int, splits: int = 0) -> int:
+    return int(load().msa_indexer_workspace_bytes_multi(batch, max_blocks, qlen, topk, splits))
+
+
+def _inputs_multi(q, k_cache, block_table, seq_lens):
+    torch = _torch()
+    if q.dim() != 4 or tuple(q.shape[2:]) != (HEADS, DIM):
+        raise ValueError("q: expected [batch, qlen, 4, 128]")
+    B, Q = q.shape[0], q.shape[1]
+    if k_cache.dim() != 3 or tuple(k_cache.shape[1:]) != (BLOCK, DIM):
+        raise ValueError("k_cache: expected [pages, 128, 128]")
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table: expected [batch, max_blocks]")
+    ptrs = (_dev(q, "q", torch.bfloat16), _dev(k_cache, "k_cache", torch.bfloat16),
+            _dev(block_table, "block_table", torch.int32),
+            _dev(seq_lens, "seq_lens", torch.int32, (B,)))
+    return ptrs, B, Q, block_table.shape[1], block_table.stride(0), k_cache.shape[0]
+
+
+def msa_indexer_decode_multi(q, k_cache, block_table, seq_lens, topk=16, n_init=1, n_local=2,
+                             out_ids=None, out_scores=None, workspace=None, num_splits=0,
+                             stream=None):
+    """Multi-token decode, q [B, Q, 4, 128]: (out_ids int32 [B,Q,4,topk], out_scores fp32)."""
+    torch = _torch()
+    (pq, pk, pbt, pl), B, Q, W, stride, pages = _inputs_multi(q, k_cache, block_table, seq_lens)
+    dev = q.device
+    if out_ids is None:
+        out_ids = torch.empty((B, Q, HEADS, topk), dtype=torch.int32, device=dev)
+    if out_scores is None:
+        out_scores = torch.empty((B, Q, HEADS, topk), dtype=torch.float32, device=dev)
+    if workspace is None:
+        n = workspace_bytes_multi(B, W, Q, topk, num_splits)
+        if n == 0:
+            raise ValueError("invalid arguments for a workspace")
+        workspace = torch.zeros(n, dtype=torch.uint8, device=dev)
+    rc = load().msa_indexer_decode_multi(
+        pq, pk, pbt, pl, B, W, stride, pages, Q, topk, n_init, n_local,
+        _dev(out_ids, "out_ids", torch.int32, (B, Q, HEADS, topk)),
+        _dev(out_scores, "out_scores", torch.float32, (B, Q, HEADS, topk)),
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(), num_splits, _stream(stream))
+    _check("msa_indexer_decode_multi", rc)
+    return out_ids, out_scores
+
+
+def msa_indexer_block_scores_multi(q, k_cache, block_table, seq_lens, num_splits=0, out=None,
+                                   stream=None):
+    """fp32 block scores [B, Q, 4, W] of the multi-token pass; -inf where a position sees no block."""
+    torch = _torch()
+    (pq, pk, pbt, pl), B, Q, W, stride, pages = _inputs_multi(q, k_cache, block_table, seq_lens)
+    if out is None:
+        out = torch.empty((B, Q, HEADS, W), dtype=torch.float32, device=q.device)
+    rc = load().msa_indexer_block_scores_multi(pq, pk, pbt, pl, B, W, stride, pages, Q,
+                                               _dev(out, "out", torch.float32, (B, Q, HEADS, W)),
+                                               num_splits, _stream(stream))
+    _check("msa_indexer_block_scores_multi", rc)
+    return out
 
 
 def msa_indexer_split_topk(q, k_cache, block_table, seq_lens, workspace, topk=16, n_init=1,

@@ -740,6 +740,198 @@ __global__ __launch_bounds__(kThreads) void expand_kernel(ExpandArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
+// Multi-token decode: a row verifying Q <= 4 draft tokens carries Q query positions, the
+// last Q tokens of its context. All Q x 4 (position, head) query rows are scored from one
+// read of each page (vLLM blog "Following the Bottleneck", section 2: one workgroup per
+// request for all draft positions, reusing the key loads). Under the causal clamp of
+// TensorRT-LLM PR #17008 (Description), position p sees the first L - (Q-1-p) tokens.
+//
+// The 16 query rows are exactly the A operand of v_mfma_f32_16x16x32_bf16: row m = 4p + h
+// (rows from 4Q on are zero). The result puts token column l%16 in lane l with rows
+// 4(l/16) .. +3, so lane group g = l/16 holds position g's four heads: the causal mask is a
+// per-lane token bound.
+
+struct QMulti {
+  bf16x8_t a[4];  // per k-step, as QMfma
+};
+
+__device__ __forceinline__ void load_q_multi(const uint16_t* __restrict__ q, int b, int Q, int lane,
+                                             QMulti& r) {
+  const int m = lane & 15, g = lane >> 4;
+  const int p = m >> 2, h = m & 3;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (p < Q)
+      v = *reinterpret_cast<const uint4*>(q + ((size_t)((b * Q + p) * kHeads + h) * kDim + s * 32 + g * 8));
+    r.a[s] = __builtin_bit_cast(bf16x8_t, v);
+  }
+}
+
+// Block maxima of one page for every position: lanes of group g get position g's four
+// heads in m[0..3]. full: every position sees all 128 tokens. Otherwise valid_g is the
+// number of tokens of this block position g sees (<= 0: none, the maxima stay -inf) and
+// vmax the largest over the positions (wave-uniform).
+__device__ __forceinline__ void score_block_multi(const uint16_t* __restrict__ page, bool full,
+                                                  int valid_g, int vmax, const QMulti& qr, int lane,
+                                                  float (&m)[kHeads]) {
+  const int n = lane & 15, g = lane >> 4;
+  const uint4* p = reinterpret_cast<const uint4*>(page) + n * 16 + g;
+#pragma unroll
+  for (int h = 0; h < kHeads; ++h) m[h] = -__builtin_inff();
+  if (full) {
+    uint4 kv[8][4];
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) kv[t][s] = p[t * 256 + s * 4];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qr.a[s], __builtin_bit_cast(bf16x8_t, kv[t][s]), acc, 0, 0, 0);
+#pragma unroll
+      for (int h = 0; h < kHeads; ++h) m[h] = fmaxf(m[h], acc[h]);
+    }
+  } else {
+    for (int t = 0; 16 * t < vmax; ++t) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const uint4 kv = p[t * 256 + s * 4];
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qr.a[s], __builtin_bit_cast(bf16x8_t, kv), acc, 0, 0, 0);
+      }
+      const bool ok = 16 * t + n < valid_g;
+#pragma unroll
+      for (int h = 0; h < kHeads; ++h) m[h] = ok ? fmaxf(m[h], acc[h]) : m[h];
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < kHeads; ++h) m[h] = row_max16(m[h]);
+}
+
+struct VerifyArgs {
+  const uint16_t* q;    // [batch][Q][4][128]
+  const uint16_t* k;
+  const int32_t* bt;
+  const int32_t* lens;
+  int32_t W, bt_stride;
+  int64_t num_pages;
+  int32_t Q, S, C, Lk, topk, n_init, n_local;
+  uint64_t* keys;       // [batch][S][Q*4][Lk]
+  uint32_t* err;        // device error word (may be null)
+  float* scores;        // [batch][Q][4][W] (block-score mode)
+};
+
+// Tokens position p of a row of L tokens sees.
+__device__ __forceinline__ int causal_len(int L, int Q, int p) { return max(0, L - (Q - 1 - p)); }
+
+// Grid (S, batch), 4 waves; split s of row b owns blocks [s*C, min((s+1)*C, nb)), nb the
+// last position's block count. kScores: block scores out. kSplit: per (position, head) the
+// split's top Lk keys, best first, zero padded.
+template <int MODE>
+__global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a) {
+  __shared__ float sc[kMaxSplitBlocks][16];
+  const int s = blockIdx.x;
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4;
+  const int L = row_tokens(a.lens, b, a.W);
+  const int nb = (L + kBlock - 1) / kBlock;
+  const int Lg = g < a.Q ? causal_len(L, a.Q, g) : 0;
+  const int L0 = causal_len(L, a.Q, 0);
+  const int32_t* btrow = a.bt + (size_t)b * a.bt_stride;
+  const int j0 = s * a.C, j1 = min(j0 + a.C, nb);
+
+  if (MODE == kScores) {  // blocks past the row's end: -inf for every position
+    const int e0 = max(j0, nb), e1 = min(j0 + a.C, a.W), ne = e1 - e0;
+    for (int idx = threadIdx.x; idx < ne * a.Q * kHeads; idx += kThreads) {
+      const int r = idx / ne, j = e0 + idx % ne;
+      a.scores[((size_t)b * a.Q * kHeads + r) * a.W + j] = -__builtin_inff();
+    }
+  }
+  if (j0 >= nb) return;
+  QMulti qr;
+  load_q_multi(a.q, b, a.Q, lane, qr);
+  for (int j = j0 + wave; j < j1; j += kWaves) {
+    float m[kHeads];
+    const int page = btrow[j];
+    if (page < 0 || (int64_t)page >= a.num_pages) {
+#pragma unroll
+      for (int h = 0; h < kHeads; ++h) m[h] = -__builtin_inff();
+      if (a.err != nullptr && lane == 0) atomicOr(a.err, (uint32_t)MSA_DEVERR_PAGE_OUT_OF_RANGE);
+    } else {
+      const bool full = (j + 1) * kBlock <= L0;
+      const int vmax = min(kBlock, L - j * kBlock);
+      score_block_multi(a.k + (size_t)page * kPageElems, full, min(kBlock, Lg - j * kBlock), vmax, qr,
+                        lane, m);
+    }
+    if ((lane & 15) == 0 && g < a.Q) {
+      if (MODE == kScores) {
+#pragma unroll
+        for (int h = 0; h < kHeads; ++h) a.scores[((size_t)(b * a.Q + g) * kHeads + h) * a.W + j] = m[h];
+      } else {
+#pragma unroll
+        for (int h = 0; h < kHeads; ++h) sc[j - j0][4 * g + h] = m[h];
+      }
+    }
+  }
+  if (MODE == kScores) return;
+  __syncthreads();
+
+  // Wave h ranks head h of every position. A block past position p's end has no key (0).
+  const int n = j1 - j0;
+  const int h = wave;
+  for (int p = 0; p < a.Q; ++p) {
+    const int nbp = (causal_len(L, a.Q, p) + kBlock - 1) / kBlock;
+    const int jj = j0 + lane;
+    const bool real = lane < n && jj < nbp;
+    const uint64_t key = real ? make_key(sc[lane][4 * p + h], jj, jj < a.n_init || jj >= nbp - a.n_local) : 0;
+    const int rank = count_larger(key, n);
+    const int cnt = __popcll(__ballot(real));
+    uint64_t* out = a.keys + ((size_t)(b * a.S + s) * a.Q * kHeads + 4 * p + h) * a.Lk;
+    if (real && rank < a.Lk) out[rank] = key;
+    if (lane >= cnt && lane < a.Lk) out[lane] = 0;
+  }
+}
+
+struct VerifyMergeArgs {
+  const int32_t* lens;
+  int32_t W, Q, S, C, Lk, topk;
+  const uint64_t* keys;
+  int32_t* out_ids;     // [batch][Q][4][topk]
+  float* out_scores;
+};
+
+// One wave per (row, position-head task): the exact top-min(topk, nb_p) of the splits'
+// lists (the merge of the single-token pass, per position).
+__global__ __launch_bounds__(64) void verify_merge_kernel(VerifyMergeArgs a) {
+  extern __shared__ uint64_t lk[];  // [ns][Lk + 1] lists, 16 keys of slack, pruned scratch
+  const int task = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+  const int p = task >> 2;
+  const int L = row_tokens(a.lens, b, a.W);
+  const int nb = (L + kBlock - 1) / kBlock;
+  const int nbp = (causal_len(L, a.Q, p) + kBlock - 1) / kBlock;
+  const int m = min(a.topk, nbp);
+  const int ns = (nb + a.C - 1) / a.C;
+  const int Lk = a.Lk, stride = Lk + 1, QH = a.Q * kHeads;
+  const uint64_t* src = a.keys + ((size_t)b * a.S * QH + task) * Lk;
+  stage_keys(src, lk, ns * Lk, lane, 64, [Lk, QH](int e) { return (e / Lk) * QH * Lk + e % Lk; },
+             [Lk, stride](int e) { return (e / Lk) * stride + e % Lk; });
+  for (int e = lane; e < 16; e += 64) lk[ns * stride + e] = 0;
+  __syncthreads();
+  uint64_t mine;
+  if (ns <= 64 && a.topk <= kPrunedMaxM)
+    mine = merge_pruned(lk, ns, Lk, stride, m, lane, lk + (size_t)a.S * stride + 16);
+  else
+    mine = merge_rounds(lk, ns, Lk, stride, m, lane);
+  const size_t o = ((size_t)b * QH + task) * a.topk;
+  write_selection(mine, m, a.topk, lane, a.out_ids + o, a.out_scores + o);
+}
+
+// ---------------------------------------------------------------------------------------
 // Host side.
 
 struct Plan {
@@ -922,6 +1114,35 @@ int32_t merge_impl(const int32_t* lens, int32_t batch, int32_t W, int32_t topk, 
   return hipGetLastError() == hipSuccess ? MSA_OK : MSA_ERR_HIP;
 }
 
+
+size_t ws_bytes_multi(int32_t batch, int32_t Q, const Plan& p) {
+  return keys_offset(batch) + (size_t)batch * p.S * Q * kHeads * p.Lk * sizeof(uint64_t);
+}
+
+VerifyArgs make_verify_args(const void* q, const void* k, const int32_t* bt, const int32_t* lens,
+                            int32_t W, int32_t bt_stride, int64_t num_pages, int32_t Q, const Plan& p,
+                            int32_t topk, int32_t n_init, int32_t n_local, void* ws, int32_t batch) {
+  VerifyArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.bt = bt;
+  a.lens = lens;
+  a.W = W;
+  a.bt_stride = bt_stride;
+  a.num_pages = num_pages;
+  a.Q = Q;
+  a.S = p.S;
+  a.C = p.C;
+  a.Lk = p.Lk;
+  a.topk = topk;
+  a.n_init = n_init;
+  a.n_local = n_local;
+  char* w = static_cast<char*>(ws);
+  a.err = w ? reinterpret_cast<uint32_t*>(w) : nullptr;
+  a.keys = w ? reinterpret_cast<uint64_t*>(w + keys_offset(batch)) : nullptr;
+  a.scores = nullptr;
+  return a;
+}
 
 int32_t decode_impl(const void* q, const void* k_cache, const int32_t* block_table,
                     const int32_t* seq_lens, int32_t batch, int32_t W, int32_t bt_stride,
@@ -1110,6 +1331,74 @@ int32_t msa_indexer_read_error(void* workspace, uint32_t* host_flags, void* stre
     return MSA_ERR_HIP;
   if (hipMemset(workspace, 0, sizeof(uint32_t)) != hipSuccess) return MSA_ERR_HIP;
   return MSA_OK;
+}
+
+size_t msa_indexer_workspace_bytes_multi(int32_t batch, int32_t max_blocks_per_seq, int32_t qlen,
+                                         int32_t topk, int32_t num_splits) {
+  Plan p;
+  if (qlen < 1 || qlen > MSA_MAX_QUERY_LEN) return 0;
+  if (make_plan(batch, max_blocks_per_seq, topk, num_splits, &p) != MSA_OK) return 0;
+  return ws_bytes_multi(batch, qlen, p);
+}
+
+int32_t msa_indexer_decode_multi(const void* q, const void* k_cache, const int32_t* block_table,
+                                 const int32_t* seq_lens, int32_t batch,
+                                 int32_t max_blocks_per_seq, int32_t bt_stride, int64_t num_pages,
+                                 int32_t qlen, int32_t topk, int32_t n_init, int32_t n_local,
+                                 int32_t* out_ids, float* out_scores, void* workspace,
+                                 size_t workspace_bytes, int32_t num_splits, void* stream) {
+  if (qlen < 1 || qlen > MSA_MAX_QUERY_LEN) return MSA_ERR_INVALID_ARG;
+  int32_t rc = check_inputs(q, k_cache, block_table, seq_lens, batch, max_blocks_per_seq, bt_stride,
+                            num_pages);
+  if (rc != MSA_OK) return rc;
+  if ((rc = check_select(topk, n_init, n_local)) != MSA_OK) return rc;
+  Plan p;
+  if ((rc = make_plan(batch, max_blocks_per_seq, topk, num_splits, &p)) != MSA_OK) return rc;
+  if (batch == 0) return MSA_OK;
+  if (!out_ids || !out_scores || !aligned(out_ids, 4) || !aligned(out_scores, 4)) return MSA_ERR_INVALID_ARG;
+  if (!workspace || !aligned(workspace, kAlign)) return MSA_ERR_INVALID_ARG;
+  if (workspace_bytes < ws_bytes_multi(batch, qlen, p)) return MSA_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const VerifyArgs a = make_verify_args(q, k_cache, block_table, seq_lens, max_blocks_per_seq,
+                                        bt_stride, num_pages, qlen, p, topk, n_init, n_local,
+                                        workspace, batch);
+  hipLaunchKernelGGL(verify_kernel<kSplit>, dim3(p.S, batch), dim3(kThreads), 0, st, a);
+  if (hipGetLastError() != hipSuccess) return MSA_ERR_HIP;
+  VerifyMergeArgs mg;
+  mg.lens = seq_lens;
+  mg.W = max_blocks_per_seq;
+  mg.Q = qlen;
+  mg.S = p.S;
+  mg.C = p.C;
+  mg.Lk = p.Lk;
+  mg.topk = topk;
+  mg.keys = a.keys;
+  mg.out_ids = out_ids;
+  mg.out_scores = out_scores;
+  const size_t lds = ((size_t)p.S * (p.Lk + 1) + 16 + kPrunedScratch) * sizeof(uint64_t);
+  hipLaunchKernelGGL(verify_merge_kernel, dim3(qlen * kHeads, batch), dim3(64), lds, st, mg);
+  return hipGetLastError() == hipSuccess ? MSA_OK : MSA_ERR_HIP;
+}
+
+int32_t msa_indexer_block_scores_multi(const void* q, const void* k_cache, const int32_t* block_table,
+                                       const int32_t* seq_lens, int32_t batch,
+                                       int32_t max_blocks_per_seq, int32_t bt_stride,
+                                       int64_t num_pages, int32_t qlen, float* out,
+                                       int32_t num_splits, void* stream) {
+  if (qlen < 1 || qlen > MSA_MAX_QUERY_LEN) return MSA_ERR_INVALID_ARG;
+  int32_t rc = check_inputs(q, k_cache, block_table, seq_lens, batch, max_blocks_per_seq, bt_stride,
+                            num_pages);
+  if (rc != MSA_OK) return rc;
+  Plan p;
+  if ((rc = make_plan(batch, max_blocks_per_seq, 16, num_splits, &p)) != MSA_OK) return rc;
+  if (batch == 0 || max_blocks_per_seq == 0) return MSA_OK;
+  if (!out || !aligned(out, 4)) return MSA_ERR_INVALID_ARG;
+  VerifyArgs a = make_verify_args(q, k_cache, block_table, seq_lens, max_blocks_per_seq, bt_stride,
+                                  num_pages, qlen, p, 16, 0, 0, nullptr, batch);
+  a.scores = out;
+  hipLaunchKernelGGL(verify_kernel<kScores>, dim3(p.S, batch), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), a);
+  return hipGetLastError() == hipSuccess ? MSA_OK : MSA_ERR_HIP;
 }
 
 }  // extern "C"

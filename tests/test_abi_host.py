@@ -206,6 +206,51 @@ def test_expand_pages_batch_zero_is_a_no_op(lib):
     assert _expand(lib, batch=0, ids=None, bt=None, lens=None, pt=None, tok=None) == OK
 
 
+def _decode_multi(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, bt=FAKE, lens=FAKE, batch=2, W=8, stride=8, pages=16, qlen=4,
+             topk=16, n_init=1, n_local=2, ids=FAKE, scores=FAKE, ws=FAKE, ws_bytes=1 << 20,
+             splits=0, stream=None)
+    a.update(kw)
+    return lib.msa_indexer_decode_multi(a["q"], a["k"], a["bt"], a["lens"], a["batch"], a["W"],
+                                        a["stride"], a["pages"], a["qlen"], a["topk"], a["n_init"],
+                                        a["n_local"], a["ids"], a["scores"], a["ws"], a["ws_bytes"],
+                                        a["splits"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(qlen=0), INVALID),
+    (dict(qlen=5), INVALID),
+    (dict(q=None), INVALID),
+    (dict(q=FAKE + 8), INVALID),
+    (dict(ids=None), INVALID),
+    (dict(scores=FAKE + 1), INVALID),
+    (dict(ws=None), INVALID),
+    (dict(ws=FAKE + 128), INVALID),
+    (dict(stride=7), INVALID),
+    (dict(topk=65), INVALID),
+    (dict(n_init=9, n_local=8), INVALID),
+    (dict(W=16385, stride=16385), UNSUPPORTED),
+    (dict(ws_bytes=256 + 2 * 256 + 2 * 2 * 16 * 4 * 8 - 1), WS_SMALL),
+])
+def test_decode_multi_rejects_on_host(lib, kw, code):
+    assert _decode_multi(lib, **kw) == code
+
+
+def test_decode_multi_workspace_and_no_op(lib):
+    ws = lib.msa_indexer_workspace_bytes_multi
+    # header, counter lines, then keys [batch][S][qlen*4][Lk]: 8 blocks -> 2 splits of 4, Lk 4
+    assert ws(2, 8, 4, 16, 0) == 256 + 2 * 256 + 2 * 2 * 16 * 4 * 8
+    assert ws(32, 1024, 4, 16, 0) == 256 + 32 * 256 + 32 * 32 * 16 * 16 * 8
+    assert ws(2, 8, 0, 16, 0) == 0 and ws(2, 8, 5, 16, 0) == 0
+    assert _decode_multi(lib, ws_bytes=ws(2, 8, 4, 16, 0) - 1) == WS_SMALL
+    assert _decode_multi(lib, batch=0, q=None, k=None, bt=None, lens=None, ids=None, scores=None,
+                         ws=None, ws_bytes=0) == OK
+    bs = lib.msa_indexer_block_scores_multi
+    assert bs(FAKE, FAKE, FAKE, FAKE, 2, 8, 8, 16, 4, None, 0, None) == INVALID
+    assert bs(FAKE, FAKE, FAKE, FAKE, 2, 8, 8, 16, 5, FAKE, 0, None) == INVALID
+    assert bs(None, None, None, None, 0, 8, 8, 16, 4, None, 0, None) == OK
+
+
 def test_binding_refuses_host_tensors():
     torch = pytest.importorskip("torch")
     from sparse_attention_block_amd import msa_indexer_decode
