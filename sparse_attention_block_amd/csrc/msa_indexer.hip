@@ -768,47 +768,54 @@ __device__ __forceinline__ void load_q_multi(const uint16_t* __restrict__ q, int
   }
 }
 
-// Block maxima of one page for every position: lanes of group g get position g's four
-// heads in m[0..3]. full: every position sees all 128 tokens. Otherwise valid_g is the
-// number of tokens of this block position g sees (<= 0: none, the maxima stay -inf) and
-// vmax the largest over the positions (wave-uniform).
-__device__ __forceinline__ void score_block_multi(const uint16_t* __restrict__ page, bool full,
-                                                  int valid_g, int vmax, const QMulti& qr, int lane,
-                                                  float (&m)[kHeads]) {
-  const int n = lane & 15, g = lane >> 4;
-  const uint4* p = reinterpret_cast<const uint4*>(page) + n * 16 + g;
+// Streaming form for the verify kernel. The MFMA operand layout reads half of sixteen
+// 128-byte lines per load instruction, which streams poorly. Here each wave instead reads
+// its pages with the coalesced pattern of the VALU engine (load i: 1 KiB = tokens 4i .. 4i+3,
+// lane l: token 4i + l/16, dims 8(l%16) .. +7, non-temporal), 32 tokens (8 loads) at a time,
+// one chunk ahead, and passes each chunk through a private 8 KiB LDS region to reach the
+// operand layout. 16-byte slot c of token t is stored at position c ^ (t % 16) of the token's
+// 256-byte row, so neither the row-wise writes nor the column-wise operand reads (16 tokens,
+// one slot each) put two lanes of a pass on the same banks.
+constexpr int kChunkTokens = 32;
+constexpr int kChunkLoads = kChunkTokens / 4;                 // 1 KiB wave loads per chunk
+constexpr int kChunkSlots = kChunkTokens * (kDim * 2 / 16);   // 16-byte slots per chunk
+
+__device__ __forceinline__ void chunk_load(const uint16_t* __restrict__ page, int c, int lane,
+                                           uint4 (&kv)[kChunkLoads]) {
+  const uint4* p = reinterpret_cast<const uint4*>(page) + c * kChunkSlots + lane;
 #pragma unroll
-  for (int h = 0; h < kHeads; ++h) m[h] = -__builtin_inff();
-  if (full) {
-    uint4 kv[8][4];
+  for (int i = 0; i < kChunkLoads; ++i) kv[i] = load_stream(p + i * 64);
+}
+
+__device__ __forceinline__ void chunk_to_lds(uint4* region, const uint4 (&kv)[kChunkLoads], int lane) {
+  const int r = lane >> 4, c = lane & 15;
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) kv[t][s] = p[t * 256 + s * 4];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qr.a[s], __builtin_bit_cast(bf16x8_t, kv[t][s]), acc, 0, 0, 0);
-#pragma unroll
-      for (int h = 0; h < kHeads; ++h) m[h] = fmaxf(m[h], acc[h]);
-    }
-  } else {
-    for (int t = 0; 16 * t < vmax; ++t) {
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const uint4 kv = p[t * 256 + s * 4];
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qr.a[s], __builtin_bit_cast(bf16x8_t, kv), acc, 0, 0, 0);
-      }
-      const bool ok = 16 * t + n < valid_g;
-#pragma unroll
-      for (int h = 0; h < kHeads; ++h) m[h] = ok ? fmaxf(m[h], acc[h]) : m[h];
-    }
+  for (int i = 0; i < kChunkLoads; ++i) {
+    const int t = 4 * i + r;
+    region[t * 16 + (c ^ (t & 15))] = kv[i];
   }
+}
+
+// Running maxima over one chunk: lane group g accumulates position g's four heads; token
+// 16 tg + l%16 of the chunk is column l%16 of MFMA tg. ok_g: tokens of the chunk position g
+// sees (>= 32: all).
+__device__ __forceinline__ void chunk_mfma(const uint4* region, int ok_g, const QMulti& qr, int lane,
+                                           float (&m)[kHeads]) {
+  const int n = lane & 15, g = lane >> 4;
 #pragma unroll
-  for (int h = 0; h < kHeads; ++h) m[h] = row_max16(m[h]);
+  for (int tg = 0; tg < 2; ++tg) {
+    const int t = 16 * tg + n;
+    uint4 b[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) b[s] = region[t * 16 + ((4 * s + g) ^ n)];
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qr.a[s], __builtin_bit_cast(bf16x8_t, b[s]), acc, 0, 0, 0);
+    const bool ok = t < ok_g;
+#pragma unroll
+    for (int h = 0; h < kHeads; ++h) m[h] = ok ? fmaxf(m[h], acc[h]) : m[h];
+  }
 }
 
 struct VerifyArgs {
@@ -831,8 +838,9 @@ __device__ __forceinline__ int causal_len(int L, int Q, int p) { return max(0, L
 // last position's block count. kScores: block scores out. kSplit: per (position, head) the
 // split's top Lk keys, best first, zero padded.
 template <int MODE>
-__global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void verify_kernel(VerifyArgs a) {
   __shared__ float sc[kMaxSplitBlocks][16];
+  __shared__ uint4 stage[kWaves * kChunkSlots];  // one 8 KiB chunk region per wave
   const int s = blockIdx.x;
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63;
@@ -841,7 +849,6 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a) {
   const int L = row_tokens(a.lens, b, a.W);
   const int nb = (L + kBlock - 1) / kBlock;
   const int Lg = g < a.Q ? causal_len(L, a.Q, g) : 0;
-  const int L0 = causal_len(L, a.Q, 0);
   const int32_t* btrow = a.bt + (size_t)b * a.bt_stride;
   const int j0 = s * a.C, j1 = min(j0 + a.C, nb);
 
@@ -855,19 +862,12 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a) {
   if (j0 >= nb) return;
   QMulti qr;
   load_q_multi(a.q, b, a.Q, lane, qr);
-  for (int j = j0 + wave; j < j1; j += kWaves) {
-    float m[kHeads];
-    const int page = btrow[j];
-    if (page < 0 || (int64_t)page >= a.num_pages) {
-#pragma unroll
-      for (int h = 0; h < kHeads; ++h) m[h] = -__builtin_inff();
-      if (a.err != nullptr && lane == 0) atomicOr(a.err, (uint32_t)MSA_DEVERR_PAGE_OUT_OF_RANGE);
-    } else {
-      const bool full = (j + 1) * kBlock <= L0;
-      const int vmax = min(kBlock, L - j * kBlock);
-      score_block_multi(a.k + (size_t)page * kPageElems, full, min(kBlock, Lg - j * kBlock), vmax, qr,
-                        lane, m);
-    }
+  uint4* region = stage + wave * kChunkSlots;
+
+  // The wave's blocks j0 + wave, j0 + wave + 4, ... as one stream of 32-token chunks: chunk
+  // c of block j holds tokens 32c .. 32c+31; a block has ceil(vmax / 32) chunks, vmax the
+  // tokens the last position sees. Blocks whose page is out of range score -inf, unread.
+  auto emit = [&](int j, float (&m)[kHeads]) {
     if ((lane & 15) == 0 && g < a.Q) {
       if (MODE == kScores) {
 #pragma unroll
@@ -876,6 +876,61 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a) {
 #pragma unroll
         for (int h = 0; h < kHeads; ++h) sc[j - j0][4 * g + h] = m[h];
       }
+    }
+  };
+  // First block at or after j with a page in range (out-of-range ones are emitted as -inf).
+  auto next_block = [&](int j, const uint16_t*& pg) {
+    for (; j < j1; j += kWaves) {
+      const int page = btrow[j];
+      if (page >= 0 && (int64_t)page < a.num_pages) {
+        pg = a.k + (size_t)page * kPageElems;
+        return j;
+      }
+      if (a.err != nullptr && lane == 0) atomicOr(a.err, (uint32_t)MSA_DEVERR_PAGE_OUT_OF_RANGE);
+      float m[kHeads];
+#pragma unroll
+      for (int h = 0; h < kHeads; ++h) m[h] = -__builtin_inff();
+      emit(j, m);
+    }
+    return j;
+  };
+  auto chunks_of = [&](int j) { return (min(kBlock, L - j * kBlock) + kChunkTokens - 1) / kChunkTokens; };
+
+  const uint16_t* pg = nullptr;
+  int j = next_block(j0 + wave, pg);
+  if (j < j1) {
+    int c = 0, nch = chunks_of(j);
+    float m[kHeads];
+#pragma unroll
+    for (int h = 0; h < kHeads; ++h) m[h] = -__builtin_inff();
+    uint4 kv[kChunkLoads];
+    chunk_load(pg, 0, lane, kv);
+    while (true) {
+      // Next chunk: the rest of this block, else the first chunk of the wave's next block.
+      int nj = j, nc = c + 1;
+      const uint16_t* npg = pg;
+      if (nc == nch) {
+        nj = next_block(j + kWaves, npg);
+        nc = 0;
+      }
+      uint4 nx[kChunkLoads];
+      if (nj < j1) chunk_load(npg, nc, lane, nx);
+      chunk_to_lds(region, kv, lane);
+      chunk_mfma(region, Lg - j * kBlock - c * kChunkTokens, qr, lane, m);
+      if (c + 1 == nch) {
+#pragma unroll
+        for (int h = 0; h < kHeads; ++h) m[h] = row_max16(m[h]);
+        emit(j, m);
+#pragma unroll
+        for (int h = 0; h < kHeads; ++h) m[h] = -__builtin_inff();
+      }
+      if (nj >= j1) break;
+      if (nj != j) nch = chunks_of(nj);
+      j = nj;
+      c = nc;
+      pg = npg;
+#pragma unroll
+      for (int i = 0; i < kChunkLoads; ++i) kv[i] = nx[i];
     }
   }
   if (MODE == kScores) return;
