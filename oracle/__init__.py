@@ -37,6 +37,12 @@ class Oracle:
         lib.msa_oracle_decode_multi.argtypes = [P, P, P, P, i32, i32, i32, i64, i32, i32, i32, i32,
                                                  P, P, P]
         lib.msa_oracle_decode_multi.restype = ctypes.c_int
+        f64 = ctypes.c_double
+        lib.msa_oracle_block_scores_fp8.argtypes = [P, P, f64, P, P, i32, i32, i32, i64, P]
+        lib.msa_oracle_block_scores_fp8.restype = ctypes.c_int
+        lib.msa_oracle_decode_multi_fp8.argtypes = [P, P, f64, P, P, i32, i32, i32, i64, i32, i32,
+                                                    i32, i32, P, P, P]
+        lib.msa_oracle_decode_multi_fp8.restype = ctypes.c_int
         lib.msa_oracle_num_threads.argtypes = []
         lib.msa_oracle_num_threads.restype = ctypes.c_int
         self.lib = lib
@@ -110,9 +116,51 @@ class Oracle:
             raise ValueError(f"oracle decode_multi failed with code {rc}")
         return ids, sc, blocks
 
+    def block_scores_fp8(self, q, k_codes, k_scale: float, block_table, seq_lens) -> np.ndarray:
+        """fp64 block scores [B, 4, W] over an FP8 E4M3 cache (uint8 codes) with scale k_scale."""
+        q = np.ascontiguousarray(q, dtype=np.uint16)
+        k_codes = np.ascontiguousarray(k_codes, dtype=np.uint8)
+        block_table = np.ascontiguousarray(block_table, dtype=np.int32)
+        seq_lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+        B, W = block_table.shape
+        assert q.shape == (B, HEADS, 128) and k_codes.shape[1:] == (128, 128)
+        out = np.empty((B, HEADS, W), dtype=np.float64)
+        rc = self.lib.msa_oracle_block_scores_fp8(_ptr(q), _ptr(k_codes), float(k_scale),
+                                                  _ptr(block_table), _ptr(seq_lens), B, W, W,
+                                                  k_codes.shape[0], _ptr(out))
+        if rc != 0:
+            raise ValueError(f"oracle block_scores_fp8 failed with code {rc}")
+        return out
+
+    def decode_multi_fp8(self, q, k_codes, k_scale: float, block_table, seq_lens, topk: int,
+                         n_init: int, n_local: int):
+        """decode_multi over an FP8 E4M3 cache (uint8 codes) with scale k_scale."""
+        q = np.ascontiguousarray(q, dtype=np.uint16)
+        k_codes = np.ascontiguousarray(k_codes, dtype=np.uint8)
+        block_table = np.ascontiguousarray(block_table, dtype=np.int32)
+        seq_lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+        B, W = block_table.shape
+        assert q.ndim == 4 and q.shape[0] == B and q.shape[2:] == (HEADS, 128)
+        Q = q.shape[1]
+        blocks = np.empty((B, Q, HEADS, W), dtype=np.float64)
+        ids = np.empty((B, Q, HEADS, topk), dtype=np.int32)
+        sc = np.empty((B, Q, HEADS, topk), dtype=np.float64)
+        rc = self.lib.msa_oracle_decode_multi_fp8(_ptr(q), _ptr(k_codes), float(k_scale),
+                                                  _ptr(block_table), _ptr(seq_lens), B, W, W,
+                                                  k_codes.shape[0], Q, topk, n_init, n_local,
+                                                  _ptr(blocks), _ptr(ids), _ptr(sc))
+        if rc != 0:
+            raise ValueError(f"oracle decode_multi_fp8 failed with code {rc}")
+        return ids, sc, blocks
+
     def decode(self, inp):
         """Whole pass on a synth.Inputs: (ids, selected scores, block scores). Inputs with
-        several query positions (q [B, Q, 4, 128]) go through decode_multi."""
+        several query positions (q [B, Q, 4, 128]) go through decode_multi; an FP8 cache
+        (uint8 codes, inp.k_scale) through decode_multi_fp8, with [B, Q, ...] results."""
+        if inp.k_cache.dtype == np.uint8:
+            q = inp.q if inp.q.ndim == 4 else inp.q[:, None]
+            return self.decode_multi_fp8(q, inp.k_cache, inp.k_scale, inp.block_table,
+                                         inp.seq_lens, inp.topk, inp.n_init, inp.n_local)
         if inp.q.ndim == 4:
             return self.decode_multi(inp.q, inp.k_cache, inp.block_table, inp.seq_lens, inp.topk,
                                      inp.n_init, inp.n_local)

@@ -61,6 +61,14 @@
  *                 L the row's clamped length (L_p floored at 0). Each (b, p, h) is exactly the
  *                 single-token pass above with q[b][p] and length L_p.
  *
+ *   fp8 cache     the index-K cache may hold FP8 E4M3 codes instead of bf16 (SGLang PR #41488,
+ *                 Accuracy and Speed Tests: BF16 queries with an FP8 E4M3 index cache). The
+ *                 pages fix no scale; the reading taken here: OCP E4M3 (the MI355X format:
+ *                 exponent bias 7, three mantissa bits, subnormals, no infinities, S.1111.111
+ *                 is NaN and outside the contract), one positive scale per cache, so the key
+ *                 is k_scale * value(code). A positive scale cannot reorder blocks (vLLM blog,
+ *                 section 2), so the selection does not depend on it.
+ *
  * bf16 inputs are widened exactly (bits << 16 is the fp32 value; fp32 -> fp64
  * is exact), products of two bf16 values are exact in fp64, and the 128-term
  * sums are accumulated in fp64.
@@ -90,6 +98,16 @@ static double widen_bf16(uint16_t bits)
     return (double)f;
 }
 
+/* OCP FP8 E4M3: sign, 4 exponent bits (bias 7), 3 mantissa bits; exponent 0 is subnormal. */
+static double widen_e4m3(uint8_t code)
+{
+    int sign = code >> 7;
+    int e = (code >> 3) & 15;
+    int m = code & 7;
+    double mag = e == 0 ? ldexp((double)m, -9) : ldexp(8.0 + m, e - 10);
+    return sign ? -mag : mag;
+}
+
 static int64_t row_len(const int32_t *seq_lens, int32_t b, int32_t max_blocks)
 {
     int64_t L = seq_lens[b];
@@ -113,10 +131,10 @@ int msa_oracle_num_threads(void)
  * row's end hold -inf. Returns OR_ERR_PAGE if a block the row needs maps to a
  * page outside [0, num_pages).
  */
-int msa_oracle_block_scores(const uint16_t *q, const uint16_t *k_cache,
-                            const int32_t *block_table, const int32_t *seq_lens,
-                            int32_t batch, int32_t max_blocks, int32_t bt_stride,
-                            int64_t num_pages, double *out)
+static int block_scores_impl(const uint16_t *q, const void *k_cache, int kv_fp8, double k_scale,
+                             const int32_t *block_table, const int32_t *seq_lens,
+                             int32_t batch, int32_t max_blocks, int32_t bt_stride,
+                             int64_t num_pages, double *out)
 {
     if (batch < 0 || max_blocks < 0 || bt_stride < max_blocks) return OR_ERR_ARG;
     int64_t total = (int64_t)batch * max_blocks;
@@ -140,9 +158,15 @@ int msa_oracle_block_scores(const uint16_t *q, const uint16_t *k_cache,
                 int64_t valid = L - (int64_t)j * OR_BLOCK;
                 if (valid > OR_BLOCK) valid = OR_BLOCK;
                 for (int64_t t = 0; t < valid; ++t) {
-                    const uint16_t *tok = k_cache + (page * OR_BLOCK + t) * OR_DIM;
+                    int64_t tok = (page * OR_BLOCK + t) * OR_DIM;
                     double kt[OR_DIM];
-                    for (int d = 0; d < OR_DIM; ++d) kt[d] = widen_bf16(tok[d]);
+                    if (kv_fp8) {
+                        const uint8_t *k8 = (const uint8_t *)k_cache + tok;
+                        for (int d = 0; d < OR_DIM; ++d) kt[d] = k_scale * widen_e4m3(k8[d]);
+                    } else {
+                        const uint16_t *k16 = (const uint16_t *)k_cache + tok;
+                        for (int d = 0; d < OR_DIM; ++d) kt[d] = widen_bf16(k16[d]);
+                    }
                     for (int h = 0; h < OR_HEADS; ++h) {
                         const uint16_t *qh = q + ((int64_t)b * OR_HEADS + h) * OR_DIM;
                         double s = 0.0;
@@ -162,6 +186,26 @@ int msa_oracle_block_scores(const uint16_t *q, const uint16_t *k_cache,
             out[((int64_t)b * OR_HEADS + h) * max_blocks + j] = best[h];
     }
     return status;
+}
+
+int msa_oracle_block_scores(const uint16_t *q, const uint16_t *k_cache,
+                            const int32_t *block_table, const int32_t *seq_lens,
+                            int32_t batch, int32_t max_blocks, int32_t bt_stride,
+                            int64_t num_pages, double *out)
+{
+    return block_scores_impl(q, k_cache, 0, 1.0, block_table, seq_lens, batch, max_blocks,
+                             bt_stride, num_pages, out);
+}
+
+/* Block scores over an FP8 E4M3 cache k_cache[page][token][dim] (one byte per element). */
+int msa_oracle_block_scores_fp8(const uint16_t *q, const uint8_t *k_cache, double k_scale,
+                                const int32_t *block_table, const int32_t *seq_lens,
+                                int32_t batch, int32_t max_blocks, int32_t bt_stride,
+                                int64_t num_pages, double *out)
+{
+    if (!(k_scale > 0.0) || !isfinite(k_scale)) return OR_ERR_ARG;
+    return block_scores_impl(q, k_cache, 1, k_scale, block_table, seq_lens, batch, max_blocks,
+                             bt_stride, num_pages, out);
 }
 
 typedef struct {
@@ -283,12 +327,12 @@ int msa_oracle_expand_pages(const int32_t *ids, const int32_t *block_table, cons
  * (j < max_blocks), selections out_ids / out_scores [b][p][h][topk]. Each position is run
  * through msa_oracle_decode with its own query and causal length.
  */
-int msa_oracle_decode_multi(const uint16_t *q, const uint16_t *k_cache,
-                            const int32_t *block_table, const int32_t *seq_lens,
-                            int32_t batch, int32_t max_blocks, int32_t bt_stride,
-                            int64_t num_pages, int32_t qlen, int32_t topk, int32_t n_init,
-                            int32_t n_local, double *out_blocks, int32_t *out_ids,
-                            double *out_scores)
+static int decode_multi_impl(const uint16_t *q, const void *k_cache, int kv_fp8, double k_scale,
+                             const int32_t *block_table, const int32_t *seq_lens,
+                             int32_t batch, int32_t max_blocks, int32_t bt_stride,
+                             int64_t num_pages, int32_t qlen, int32_t topk, int32_t n_init,
+                             int32_t n_local, double *out_blocks, int32_t *out_ids,
+                             double *out_scores)
 {
     if (batch < 0 || max_blocks < 0 || qlen < 1 || topk < 1) return OR_ERR_ARG;
     size_t nb_q = (size_t)batch * OR_HEADS * OR_DIM;
@@ -308,8 +352,10 @@ int msa_oracle_decode_multi(const uint16_t *q, const uint16_t *k_cache,
                    q + ((size_t)b * qlen + p) * OR_HEADS * OR_DIM,
                    OR_HEADS * OR_DIM * sizeof(uint16_t));
         }
-        rc = msa_oracle_decode(qp, k_cache, block_table, lens_p, batch, max_blocks, bt_stride,
-                               num_pages, topk, n_init, n_local, sc, ids, sel);
+        rc = block_scores_impl(qp, k_cache, kv_fp8, k_scale, block_table, lens_p, batch,
+                               max_blocks, bt_stride, num_pages, sc);
+        if (rc == OR_OK)
+            rc = msa_oracle_select(sc, lens_p, batch, max_blocks, topk, n_init, n_local, ids, sel);
         for (int32_t b = 0; b < batch && rc == OR_OK; ++b) {
             size_t o = (size_t)b * qlen + p;
             memcpy(out_blocks + o * OR_HEADS * max_blocks, sc + (size_t)b * OR_HEADS * max_blocks,
@@ -326,4 +372,30 @@ int msa_oracle_decode_multi(const uint16_t *q, const uint16_t *k_cache,
     free(ids);
     free(sel);
     return rc;
+}
+
+int msa_oracle_decode_multi(const uint16_t *q, const uint16_t *k_cache,
+                            const int32_t *block_table, const int32_t *seq_lens,
+                            int32_t batch, int32_t max_blocks, int32_t bt_stride,
+                            int64_t num_pages, int32_t qlen, int32_t topk, int32_t n_init,
+                            int32_t n_local, double *out_blocks, int32_t *out_ids,
+                            double *out_scores)
+{
+    return decode_multi_impl(q, k_cache, 0, 1.0, block_table, seq_lens, batch, max_blocks,
+                             bt_stride, num_pages, qlen, topk, n_init, n_local, out_blocks,
+                             out_ids, out_scores);
+}
+
+/* Multi-token decode (qlen >= 1) over an FP8 E4M3 cache with scale k_scale > 0. */
+int msa_oracle_decode_multi_fp8(const uint16_t *q, const uint8_t *k_cache, double k_scale,
+                                const int32_t *block_table, const int32_t *seq_lens,
+                                int32_t batch, int32_t max_blocks, int32_t bt_stride,
+                                int64_t num_pages, int32_t qlen, int32_t topk, int32_t n_init,
+                                int32_t n_local, double *out_blocks, int32_t *out_ids,
+                                double *out_scores)
+{
+    if (!(k_scale > 0.0) || !isfinite(k_scale)) return OR_ERR_ARG;
+    return decode_multi_impl(q, k_cache, 1, k_scale, block_table, seq_lens, batch, max_blocks,
+                             bt_stride, num_pages, qlen, topk, n_init, n_local, out_blocks,
+                             out_ids, out_scores);
 }

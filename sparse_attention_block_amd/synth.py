@@ -9,6 +9,7 @@ Layouts (row-major, as both sides read them):
                uint16 [B, Q, 4, 128]     or Q query positions per row (multi-token decode:
                                          the row's last Q context tokens are draft tokens)
   k_cache      uint16 [P, 128, 128]      bf16 bit patterns, page-major, token-major
+               uint8  [P, 128, 128]      or FP8 E4M3 codes (OCP), keys = k_scale * value
   block_table  int32  [B, W]             logical block j of row b -> physical page
   seq_lens     int32  [B]                tokens in row b's context (0 .. W*128)
 
@@ -78,6 +79,11 @@ class Inputs:
     n_init: int = 1
     n_local: int = 2
     meta: dict = field(default_factory=dict)
+    k_scale: float = 1.0  # FP8 caches only
+
+    @property
+    def fp8(self) -> bool:
+        return self.k_cache.dtype == np.uint8
 
     @property
     def batch(self) -> int:
@@ -98,8 +104,9 @@ class Inputs:
 
     @property
     def index_k_bytes(self) -> int:
-        """Index-K bytes the pass must read: sum of seq_len * 128 dims * 2 B."""
-        return int(np.asarray(self.seq_lens, dtype=np.int64).clip(min=0).sum()) * DIM * 2
+        """Index-K bytes the pass must read: sum of seq_len * 128 dims * (2 B bf16, 1 B fp8)."""
+        elem = 1 if self.fp8 else 2
+        return int(np.asarray(self.seq_lens, dtype=np.int64).clip(min=0).sum()) * DIM * elem
 
 
 def _nblocks(lens: np.ndarray) -> np.ndarray:
@@ -235,6 +242,51 @@ def multi_config(qlen: int = 4) -> Inputs:
     inp.q = normal_bf16(3, 5, (inp.batch, qlen, HEADS, DIM))
     inp.name = f"B=32 x 131072, Q={qlen}"
     return inp
+
+
+def e4m3_codes(x: np.ndarray) -> np.ndarray:
+    """fp32 values -> OCP FP8 E4M3 codes (uint8), round to nearest even, saturated to +-448
+    (so no NaN code is produced). Converted in chunks through torch's float8_e4m3fn."""
+    import torch
+    a = np.clip(np.asarray(x, dtype=np.float32), -448.0, 448.0).reshape(-1)
+    out = np.empty(a.shape, dtype=np.uint8)
+    for lo in range(0, a.size, _CHUNK_ELEMS):
+        hi = min(a.size, lo + _CHUNK_ELEMS)
+        out[lo:hi] = torch.from_numpy(a[lo:hi]).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return out.reshape(np.shape(x))
+
+
+def to_fp8(inp: Inputs, k_scale: float = 1.0, amp: float = 1.0) -> Inputs:
+    """The same input with its bf16 index-K cache re-encoded as E4M3 codes of amp * value
+    (amp = 1 keeps small integers exact: -1, 0, 1 and the +-64 poison are E4M3 values), and
+    q shaped [B, Q, 4, 128]."""
+    vals = bf16_to_f32(inp.k_cache) if amp == 1.0 else bf16_to_f32(inp.k_cache) * np.float32(amp)
+    q = inp.q if inp.q.ndim == 4 else inp.q[:, None].copy()
+    return Inputs(inp.name + f" fp8(scale={k_scale})", q, e4m3_codes(vals), inp.block_table,
+                  inp.seq_lens, topk=inp.topk, n_init=inp.n_init, n_local=inp.n_local,
+                  meta=dict(inp.meta), k_scale=float(k_scale))
+
+
+def fp8_case(seed: int, seq_lens, max_blocks: int, qlen: int = 1, k_scale: float = 1.0,
+             amp: float = 4.0, **kw) -> Inputs:
+    """multi_case with the index-K cache as E4M3 codes of amp * N(0,1) (poison pages and
+    tails stay +-64 * amp, inside the E4M3 range for amp <= 7)."""
+    return to_fp8(multi_case(seed, seq_lens, max_blocks, qlen, **kw), k_scale, amp)
+
+
+def fp8_config(qlen: int = 1, k_scale: float = 1.0) -> Inputs:
+    """The benchmark shape with an FP8 cache: batch 32 x 131072 tokens (1024 blocks, 512 MiB of
+    E4M3 codes of 4 * N(0,1)), shuffled pages, q ~N(0,1) bf16 [32, qlen, 4, 128]."""
+    B, L, W = 32, 131072, 1024
+    n = B * W * BLOCK * DIM
+    codes = np.empty(n, dtype=np.uint8)
+    for c, lo in enumerate(range(0, n, _CHUNK_ELEMS)):
+        hi = min(n, lo + _CHUNK_ELEMS)
+        codes[lo:hi] = e4m3_codes(4.0 * _child(7, 1, c).standard_normal(hi - lo, dtype=np.float32))
+    q = normal_bf16(7, 0, (B, qlen, HEADS, DIM))
+    bt = _child(7, 2).permutation(B * W).astype(np.int32).reshape(B, W)
+    return Inputs(f"fp8 B=32 x 131072, Q={qlen}", q, codes.reshape(B * W, BLOCK, DIM), bt,
+                  np.full(B, L, dtype=np.int32), k_scale=float(k_scale))
 
 
 # ---------------------------------------------------------------------------

@@ -18,8 +18,8 @@ from test_oracle_pins import PINS
 MUTANTS = {
     "dropped_dim": ("for (int d = 0; d < OR_DIM; ++d) s +=", "for (int d = 1; d < OR_DIM; ++d) s +="),
     "wrong_sign": ("s += widen_bf16(qh[d]) * kt[d];", "s -= widen_bf16(qh[d]) * kt[d];"),
-    "transposed_page": ("kt[d] = widen_bf16(tok[d]);",
-                        "kt[d] = widen_bf16(k_cache[(page * OR_BLOCK + d) * OR_DIM + t]);"),
+    "transposed_page": ("kt[d] = widen_bf16(k16[d]);",
+                        "kt[d] = widen_bf16(((const uint16_t *)k_cache)[(page * OR_BLOCK + d) * OR_DIM + t]);"),
     "head_index": ("q + ((int64_t)b * OR_HEADS + h) * OR_DIM",
                    "q + ((int64_t)b * OR_HEADS + (OR_HEADS - 1 - h)) * OR_DIM"),
     "tail_unmasked": ("if (valid > OR_BLOCK) valid = OR_BLOCK;", "valid = OR_BLOCK;"),
@@ -50,6 +50,10 @@ MUTANTS = {
                           "int64_t L = row_len(seq_lens, b, max_blocks) - (qlen - p);"),
     "positions_swapped": ("q + ((size_t)b * qlen + p) * OR_HEADS * OR_DIM",
                           "q + ((size_t)b * qlen + (qlen - 1 - p)) * OR_HEADS * OR_DIM"),
+    "e4m3_bias": ("ldexp(8.0 + m, e - 10)", "ldexp(8.0 + m, e - 11)"),
+    "e4m3_subnormal": ("ldexp((double)m, -9)", "ldexp((double)m, -10)"),
+    "e4m3_sign_dropped": ("return sign ? -mag : mag;", "return mag;"),
+    "fp8_scale_dropped": ("kt[d] = k_scale * widen_e4m3(k8[d]);", "kt[d] = widen_e4m3(k8[d]);"),
     "tokens_full_blocks": ("count += valid > OR_BLOCK ? OR_BLOCK : valid;", "count += OR_BLOCK;"),
 }
 

@@ -14,6 +14,7 @@
 """
 import json
 import math
+import functools
 import os
 
 import numpy as np
@@ -471,6 +472,12 @@ def brute_scores_causal(inp: synth.Inputs) -> np.ndarray:
     return out
 
 
+@functools.lru_cache(maxsize=None)
+def planted_multi(qlen: int = 4):
+    """synth.multi_planted, generated once per process (the pins only read it)."""
+    return synth.multi_planted(qlen)
+
+
 def multi_small_cases():
     return [
         synth.multi_case(21, [300, 128, 1, 0, 1000, 257, 3, 129, 130], 8, 4),
@@ -536,7 +543,7 @@ def pin_multi_planted(orc):
     # position 0. (2) Rows 3 and 11 hold q[b,Q-1,h] in the masked tail of their last block,
     # which must not score. (3) Outside the pinned blocks, position p / head h selects its
     # planted run's best blocks: targets descending, ids ascending among ties.
-    inp = synth.multi_planted()
+    inp = planted_multi(4)
     ids, sc, s = orc.decode(inp)
     Q = inp.qlen
     planted = inp.meta["planted"]
@@ -562,3 +569,90 @@ def pin_multi_planted(orc):
                               key=lambda x: (-x[0], x[1]))
                 assert [j for _, j in runs[:13]] == list(got[3:16])
                 assert [float(t) for t, _ in runs[:13]] == list(sc[b, p, h, 3:16])
+
+
+# ---------------------------------------------------------------------------
+# FP8 E4M3 index cache (SGLang PR #41488, Accuracy Tests: FP8 E4M3 index caches).
+
+def _torch_e4m3_values(codes: np.ndarray) -> np.ndarray:
+    """E4M3 code -> value by torch's float8_e4m3fn (a library decoding, not the oracle's)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).view(torch.float8_e4m3fn)
+    return t.to(torch.float64).numpy()
+
+
+@pin
+def pin_fp8_every_code(orc):
+    # Row b holds one token whose dim 0 is code c_b (the rest 0); every head's q is e_0. The
+    # block score is then value(c_b) * k_scale for the 254 non-NaN codes.
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    B = len(codes)
+    k = np.zeros((B, 128, 128), dtype=np.uint8)
+    k[:, 0, 0] = codes
+    q = np.zeros((B, 4, 128), dtype=np.uint16)
+    q[:, :, 0] = synth.bf16_bits(np.float32(1.0))
+    bt = np.arange(B, dtype=np.int32).reshape(B, 1)
+    lens = np.ones(B, dtype=np.int32)
+    for scale in (1.0, 0.5, 3.0):
+        got = orc.block_scores_fp8(q, k, scale, bt, lens)[:, :, 0]
+        want = _torch_e4m3_values(codes) * scale
+        assert np.array_equal(got, np.repeat(want[:, None], 4, axis=1))
+    got = dict(zip(codes.tolist(), orc.block_scores_fp8(q, k, 1.0, bt, lens)[:, 0, 0].tolist()))
+    # closed forms of the format: 1.0, the largest value, the smallest normal and subnormal
+    assert got[0x38] == 1.0 and got[0xB8] == -1.0 and got[0x40] == 2.0
+    assert got[0x7E] == 448.0 and got[0xFE] == -448.0
+    assert got[0x08] == 2.0 ** -6 and got[0x01] == 2.0 ** -9 and got[0x07] == 7 * 2.0 ** -9
+    assert got[0x00] == 0.0 and got[0x80] == 0.0
+    pos = [got[c] for c in range(0x7F)]
+    assert all(a < b for a, b in zip(pos, pos[1:]))          # codes 0..126 increase
+
+
+def fp8_small_cases():
+    return [
+        synth.fp8_case(31, [300, 128, 1, 0, 1000, 257, 3], 8, 4, k_scale=0.5),
+        synth.fp8_case(32, [128 * 5, 77], 5, 1, k_scale=1.0, amp=6.0),
+        synth.fp8_case(33, [4000, 3000, 129], 32, 2, k_scale=0.037),
+    ]
+
+
+@pin
+def pin_fp8_block_scores_match_brute_force(orc):
+    for inp in fp8_small_cases():
+        kf = _torch_e4m3_values(inp.k_cache) * inp.k_scale
+        want = _brute_causal_values(inp.q, kf, inp.block_table, inp.seq_lens)
+        _, _, got = orc.decode(inp)
+        assert np.array_equal(np.isinf(got), np.isinf(want))
+        fin = np.isfinite(want)
+        np.testing.assert_allclose(got[fin], want[fin], rtol=1e-12, atol=1e-9)
+
+
+def _brute_causal_values(q_bits, kvals, block_table, seq_lens):
+    qf = synth.bf16_to_f32(q_bits).astype(np.float64)
+    B, W = block_table.shape
+    Q = qf.shape[1]
+    out = np.full((B, Q, 4, W), -np.inf)
+    for b in range(B):
+        L = int(min(max(seq_lens[b], 0), W * 128))
+        if L == 0:
+            continue
+        nb = -(-L // 128)
+        ctx = kvals[block_table[b, :nb]].reshape(nb * 128, 128)
+        s = np.einsum("phd,td->pht", qf[b], ctx)
+        t = np.arange(nb * 128)
+        for p in range(Q):
+            masked = np.where(t[None, :] <= L - Q + p, s[p], -np.inf)
+            out[b, p, :, :nb] = masked.reshape(4, nb, 128).max(axis=2)
+    return out
+
+
+@pin
+def pin_fp8_exact_values_match_bf16(orc):
+    # The planted workload's keys are -1, 0, 1: exact in E4M3, so the FP8 pass must select
+    # exactly what the bf16 pass selects, and a power-of-two scale scales the scores exactly.
+    inp = planted_multi(4)
+    ids, sc, s = orc.decode(inp)
+    for scale in (1.0, 0.25):
+        f = synth.to_fp8(inp, k_scale=scale)
+        ids8, sc8, s8 = orc.decode(f)
+        assert np.array_equal(ids8, ids)
+        assert np.array_equal(sc8, sc * scale) and np.array_equal(s8, s * scale)
