@@ -116,14 +116,18 @@ def time_page_table(msa, torch, args, q, k, bt, lens, ids, ws, stream, topk, n_i
 def bench_multi(args, msa, synth, np, torch) -> int:
     """Multi-token decode step (qlen draft positions per row) over the benchmark's cache."""
     Q = args.qlen
-    log(f"generating the batch 32 x 131072 workload with {Q} query positions per row")
-    inp = synth.multi_config(Q)
+    kind = "FP8 E4M3" if args.fp8 else "bf16"
+    log(f"generating the batch 32 x 131072 workload ({kind} cache) with {Q} query positions per row")
+    inp = synth.fp8_config(Q) if args.fp8 else synth.multi_config(Q)
     B, W, topk, n_init, n_local = inp.batch, inp.max_blocks, inp.topk, inp.n_init, inp.n_local
     nbytes = inp.index_k_bytes
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     q = torch.from_numpy(inp.q.view(np.int16)).to(dev).view(torch.bfloat16)
-    k = torch.from_numpy(inp.k_cache.view(np.int16)).to(dev).view(torch.bfloat16)
+    if args.fp8:
+        k = torch.from_numpy(inp.k_cache).to(dev)
+    else:
+        k = torch.from_numpy(inp.k_cache.view(np.int16)).to(dev).view(torch.bfloat16)
     bt = torch.from_numpy(inp.block_table).to(dev)
     lens = torch.from_numpy(inp.seq_lens).to(dev)
     plan = msa.plan(B, W, topk, args.splits)
@@ -136,8 +140,13 @@ def bench_multi(args, msa, synth, np, torch) -> int:
     log(f"inputs resident in HBM; plan {plan}")
 
     def step():
-        msa.msa_indexer_decode_multi(q, k, bt, lens, topk, n_init, n_local, out_ids=ids,
-                                     out_scores=sc, workspace=ws, num_splits=args.splits)
+        if args.fp8:
+            msa.msa_indexer_decode_fp8(q, k, inp.k_scale, bt, lens, topk, n_init, n_local,
+                                       out_ids=ids, out_scores=sc, workspace=ws,
+                                       num_splits=args.splits)
+        else:
+            msa.msa_indexer_decode_multi(q, k, bt, lens, topk, n_init, n_local, out_ids=ids,
+                                         out_scores=sc, workspace=ws, num_splits=args.splits)
 
     for _ in range(args.warmup):
         step()
@@ -162,8 +171,8 @@ def bench_multi(args, msa, synth, np, torch) -> int:
     gbs = nbytes / (ms_per_step * 1e-3) / 1e9
     k_gbs = nbytes / (k_ms * 1e-3) / 1e9
     out = {
-        "metric": f"µs/verify step ({Q} draft positions per row) + index-K GB/s (% of 8 TB/s) "
-                  "at batch 32 × 128K ctx",
+        "metric": (f"µs/verify step ({Q} draft positions per row)" if Q > 1 else "µs/decode step")
+                  + f" + index-K GB/s (% of 8 TB/s) at batch 32 × 128K ctx, {kind} index cache",
         "value": round(gbs, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -175,15 +184,18 @@ def bench_multi(args, msa, synth, np, torch) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) bf16 q and index-K, shuffled page table)",
+        "dtype": "fp8e4m3 x bf16" if args.fp8 else "bf16",
+        "data": ("synthetic (seeded N(0,1) bf16 q, E4M3 codes of 4 N(0,1) index-K, shuffled page "
+                 "table)") if args.fp8 else
+                "synthetic (seeded N(0,1) bf16 q and index-K, shuffled page table)",
         "config": {
-            "workload": f"batch 32 x 131072-token rows, {Q} query positions each (causal), 1024 "
+            "workload": f"batch 32 x 131072-token rows ({kind} index-K), {Q} query position(s) each (causal), 1024 "
                         "blocks of 128 tokens, 4 index heads x 128, top-16, 1 initial + 2 recent "
                         "blocks pinned",
             "batch": B, "qlen": Q, "seq_len": int(inp.seq_lens[0]), "topk": topk,
             "num_splits": plan["splits"], "blocks_per_split": plan["blocks_per_split"],
-            "index_k_bytes": nbytes, "step_call": "msa_indexer_decode_multi",
+            "index_k_bytes": nbytes,
+            "step_call": "msa_indexer_decode_fp8" if args.fp8 else "msa_indexer_decode_multi",
         },
         "roofline": {
             "kernel": "verify_kernel + verify_merge_kernel (the whole step, timed together)",
@@ -217,6 +229,8 @@ def main() -> int:
     ap.add_argument("--qlen", type=int, default=1,
                     help="query positions per row; above 1 the step is a multi-token (draft verify) "
                          "decode of the same cache, msa_indexer_decode_multi")
+    ap.add_argument("--fp8", action="store_true",
+                    help="an FP8 E4M3 index-K cache (msa_indexer_decode_fp8, 512 MiB at this shape)")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip timing the page-table entry points")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -245,7 +259,7 @@ def main() -> int:
     from sparse_attention_block_amd import synth
 
     lib = msa.load()  # raises if the HIP library is not built
-    if args.qlen != 1:
+    if args.qlen != 1 or args.fp8:
         return bench_multi(args, msa, synth, np, torch)
     log("generating the batch 32 x 131072 workload (1 GiB of bf16 index-K)")
     t0 = time.time()

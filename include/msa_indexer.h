@@ -250,6 +250,37 @@ int32_t msa_indexer_block_scores_multi(const void *q, const void *k_cache,
                                        float *out, int32_t num_splits, void *stream);
 
 /*
+ * msa_indexer_decode_multi over an FP8 E4M3 index-K cache (SGLang PR #41488, Accuracy and
+ * Speed Tests: BF16 queries, FP8 E4M3 index caches).
+ *   k_cache      uint8 [num_pages][128 tokens][128 dims], 16-byte aligned: OCP FP8 E4M3
+ *                codes (exponent bias 7, subnormals, no infinities; the NaN codes 0x7F and
+ *                0xFF are outside the contract). A page is 16 KiB.
+ *   k_scale      the cache's one positive scale: keys are k_scale * value(code). Must be
+ *                finite and > 0 (MSA_ERR_INVALID_ARG otherwise). A positive scale cannot
+ *                change the selection; it scales the reported scores.
+ * Every other argument, the outputs and the workspace (msa_indexer_workspace_bytes_multi)
+ * as in msa_indexer_decode_multi; qlen = 1 is the single-token pass over an FP8 cache (q
+ * [batch][1][4][128] is the same memory as [batch][4][128]). Scores are fp32 sums of the
+ * exact products q * value(code), times k_scale once per block maximum.
+ */
+int32_t msa_indexer_decode_fp8(const void *q, const void *k_cache, float k_scale,
+                               const int32_t *block_table, const int32_t *seq_lens, int32_t batch,
+                               int32_t max_blocks_per_seq, int32_t bt_stride, int64_t num_pages,
+                               int32_t qlen, int32_t topk, int32_t n_init, int32_t n_local,
+                               int32_t *out_ids, float *out_scores, void *workspace,
+                               size_t workspace_bytes, int32_t num_splits, void *stream);
+
+/*
+ * Test and debugging aid: msa_indexer_block_scores_multi over an FP8 E4M3 cache with scale
+ * k_scale (arguments as in msa_indexer_decode_fp8).
+ */
+int32_t msa_indexer_block_scores_fp8(const void *q, const void *k_cache, float k_scale,
+                                     const int32_t *block_table, const int32_t *seq_lens,
+                                     int32_t batch, int32_t max_blocks_per_seq, int32_t bt_stride,
+                                     int64_t num_pages, int32_t qlen, float *out, int32_t num_splits,
+                                     void *stream);
+
+/*
  * Stage 1 of msa_indexer_decode alone (never fused): one workgroup per (row, split) scores its blocks
  * for all 4 heads from a single read of each page and writes each head's top-Lk
  * (Lk = min(topk, C)) candidate keys of the split, best first, into the workspace. `engine` picks the scoring

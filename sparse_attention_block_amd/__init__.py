@@ -11,8 +11,10 @@ from ._lib import (  # noqa: F401
     MsaError,
     load,
     msa_indexer_block_scores,
+    msa_indexer_block_scores_fp8,
     msa_indexer_block_scores_multi,
     msa_indexer_decode,
+    msa_indexer_decode_fp8,
     msa_indexer_decode_multi,
     msa_indexer_decode_pages,
     msa_indexer_expand_pages,

@@ -33,6 +33,7 @@ _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
 _I64 = ctypes.c_int64
 _SZ = ctypes.c_size_t
+_F32 = ctypes.c_float
 
 _SIGNATURES = {
     "msa_status_string": ([_I32], ctypes.c_char_p),
@@ -51,6 +52,10 @@ _SIGNATURES = {
                                   _P, _P, _SZ, _I32, _P], _I32),
     "msa_indexer_block_scores_multi": ([_P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _P, _I32, _P],
                                        _I32),
+    "msa_indexer_decode_fp8": ([_P, _P, _F32, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32, _I32, _I32,
+                                _P, _P, _P, _SZ, _I32, _P], _I32),
+    "msa_indexer_block_scores_fp8": ([_P, _P, _F32, _P, _P, _I32, _I32, _I32, _I64, _I32, _P, _I32,
+                                      _P], _I32),
     "msa_indexer_split_topk": ([_P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32, _I32, _P, _SZ,
                                 _I32, _I32, _P], _I32),
     "msa_indexer_merge": ([_P, _I32, _I32, _I32, _P, _P, _P, _SZ, _I32, _P], _I32),
@@ -256,7 +261,7 @@ def workspace_bytes_multi(batch: int, max_blocks: int, qlen: int, topk: int, spl
     return int(load().msa_indexer_workspace_bytes_multi(batch, max_blocks, qlen, topk, splits))
 
 
-def _inputs_multi(q, k_cache, block_table, seq_lens):
+def _inputs_multi(q, k_cache, block_table, seq_lens, kv_dtype=None):
     torch = _torch()
     if q.dim() != 4 or tuple(q.shape[2:]) != (HEADS, DIM):
         raise ValueError("q: expected [batch, qlen, 4, 128]")
@@ -265,7 +270,7 @@ def _inputs_multi(q, k_cache, block_table, seq_lens):
         raise ValueError("k_cache: expected [pages, 128, 128]")
     if block_table.dim() != 2 or block_table.shape[0] != B:
         raise ValueError("block_table: expected [batch, max_blocks]")
-    ptrs = (_dev(q, "q", torch.bfloat16), _dev(k_cache, "k_cache", torch.bfloat16),
+    ptrs = (_dev(q, "q", torch.bfloat16), _dev(k_cache, "k_cache", kv_dtype or torch.bfloat16),
             _dev(block_table, "block_table", torch.int32),
             _dev(seq_lens, "seq_lens", torch.int32, (B,)))
     return ptrs, B, Q, block_table.shape[1], block_table.stride(0), k_cache.shape[0]
@@ -307,6 +312,48 @@ def msa_indexer_block_scores_multi(q, k_cache, block_table, seq_lens, num_splits
                                                _dev(out, "out", torch.float32, (B, Q, HEADS, W)),
                                                num_splits, _stream(stream))
     _check("msa_indexer_block_scores_multi", rc)
+    return out
+
+
+def msa_indexer_decode_fp8(q, k_cache, k_scale, block_table, seq_lens, topk=16, n_init=1,
+                           n_local=2, out_ids=None, out_scores=None, workspace=None, num_splits=0,
+                           stream=None):
+    """Decode over an FP8 E4M3 cache (uint8 codes [pages, 128, 128], scale k_scale), q
+    [B, Q, 4, 128]: (out_ids int32 [B,Q,4,topk], out_scores fp32 [B,Q,4,topk])."""
+    torch = _torch()
+    (pq, pk, pbt, pl), B, Q, W, stride, pages = _inputs_multi(q, k_cache, block_table, seq_lens,
+                                                              torch.uint8)
+    dev = q.device
+    if out_ids is None:
+        out_ids = torch.empty((B, Q, HEADS, topk), dtype=torch.int32, device=dev)
+    if out_scores is None:
+        out_scores = torch.empty((B, Q, HEADS, topk), dtype=torch.float32, device=dev)
+    if workspace is None:
+        n = workspace_bytes_multi(B, W, Q, topk, num_splits)
+        if n == 0:
+            raise ValueError("invalid arguments for a workspace")
+        workspace = torch.zeros(n, dtype=torch.uint8, device=dev)
+    rc = load().msa_indexer_decode_fp8(
+        pq, pk, float(k_scale), pbt, pl, B, W, stride, pages, Q, topk, n_init, n_local,
+        _dev(out_ids, "out_ids", torch.int32, (B, Q, HEADS, topk)),
+        _dev(out_scores, "out_scores", torch.float32, (B, Q, HEADS, topk)),
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(), num_splits, _stream(stream))
+    _check("msa_indexer_decode_fp8", rc)
+    return out_ids, out_scores
+
+
+def msa_indexer_block_scores_fp8(q, k_cache, k_scale, block_table, seq_lens, num_splits=0,
+                                 out=None, stream=None):
+    """fp32 block scores [B, Q, 4, W] over an FP8 E4M3 cache."""
+    torch = _torch()
+    (pq, pk, pbt, pl), B, Q, W, stride, pages = _inputs_multi(q, k_cache, block_table, seq_lens,
+                                                              torch.uint8)
+    if out is None:
+        out = torch.empty((B, Q, HEADS, W), dtype=torch.float32, device=q.device)
+    rc = load().msa_indexer_block_scores_fp8(pq, pk, float(k_scale), pbt, pl, B, W, stride, pages, Q,
+                                             _dev(out, "out", torch.float32, (B, Q, HEADS, W)),
+                                             num_splits, _stream(stream))
+    _check("msa_indexer_block_scores_fp8", rc)
     return out
 
 

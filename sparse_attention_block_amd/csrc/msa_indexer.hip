@@ -776,42 +776,77 @@ __device__ __forceinline__ void load_q_multi(const uint16_t* __restrict__ q, int
 // operand layout. 16-byte slot c of token t is stored at position c ^ (t % 16) of the token's
 // 256-byte row, so neither the row-wise writes nor the column-wise operand reads (16 tokens,
 // one slot each) put two lanes of a pass on the same banks.
-constexpr int kChunkTokens = 32;
-constexpr int kChunkLoads = kChunkTokens / 4;                 // 1 KiB wave loads per chunk
-constexpr int kChunkSlots = kChunkTokens * (kDim * 2 / 16);   // 16-byte slots per chunk
+// The same scheme serves FP8 E4M3 caches (one byte per element, 128-byte tokens, a 16 KiB
+// page): a chunk is then 64 tokens, still 8 KiB and 8 loads, and the operand read of each
+// lane is the 8 bytes of its 8 k-slots, widened to bf16 exactly (every E4M3 value is a bf16
+// value) by v_cvt_scalef32_pk_bf16_fp8 with scale 1.
+constexpr int kChunkLoads = 8;                 // 1 KiB wave loads per chunk
+constexpr int kChunkSlots = kChunkLoads * 64;  // 16-byte slots per chunk (8 KiB)
 
-__device__ __forceinline__ void chunk_load(const uint16_t* __restrict__ page, int c, int lane,
+template <bool FP8>
+struct KvGeom {
+  static constexpr int kTokenSlots = FP8 ? 8 : 16;              // 16-byte slots per token
+  static constexpr int kChunkTokens = kChunkSlots / kTokenSlots;  // 64 or 32
+  static constexpr int kTokensPerLoad = 64 / kTokenSlots;       // 8 or 4
+  static constexpr size_t kPageBytes = (size_t)kBlock * kDim * (FP8 ? 1 : 2);
+};
+
+__device__ __forceinline__ void chunk_load(const uint8_t* __restrict__ page, int c, int lane,
                                            uint4 (&kv)[kChunkLoads]) {
   const uint4* p = reinterpret_cast<const uint4*>(page) + c * kChunkSlots + lane;
 #pragma unroll
   for (int i = 0; i < kChunkLoads; ++i) kv[i] = load_stream(p + i * 64);
 }
 
+template <bool FP8>
 __device__ __forceinline__ void chunk_to_lds(uint4* region, const uint4 (&kv)[kChunkLoads], int lane) {
-  const int r = lane >> 4, c = lane & 15;
+  using G = KvGeom<FP8>;
+  const int r = lane / G::kTokenSlots, c = lane % G::kTokenSlots;
 #pragma unroll
   for (int i = 0; i < kChunkLoads; ++i) {
-    const int t = 4 * i + r;
-    region[t * 16 + (c ^ (t & 15))] = kv[i];
+    const int t = G::kTokensPerLoad * i + r;
+    region[t * G::kTokenSlots + (c ^ (t % G::kTokenSlots))] = kv[i];
+  }
+}
+
+// Four E4M3 codes (one dword) to bf16 pairs, exactly.
+__device__ __forceinline__ uint32_t e4m3_pair_lo(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, false));
+}
+__device__ __forceinline__ uint32_t e4m3_pair_hi(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, true));
+}
+
+// Operand of MFMA k-step s for the chunk token t in column l%16: the bf16 values of dims
+// 32 s + 8 g .. +7 (g = l/16).
+template <bool FP8>
+__device__ __forceinline__ bf16x8_t chunk_operand(const uint4* region, int t, int s, int g) {
+  if constexpr (FP8) {
+    const int c = 2 * s + (g >> 1);
+    const uint2 v = reinterpret_cast<const uint2*>(region)[(t * 8 + (c ^ (t & 7))) * 2 + (g & 1)];
+    const uint4 w = make_uint4(e4m3_pair_lo(v.x), e4m3_pair_hi(v.x), e4m3_pair_lo(v.y), e4m3_pair_hi(v.y));
+    return __builtin_bit_cast(bf16x8_t, w);
+  } else {
+    return __builtin_bit_cast(bf16x8_t, region[t * 16 + ((4 * s + g) ^ (t & 15))]);
   }
 }
 
 // Running maxima over one chunk: lane group g accumulates position g's four heads; token
 // 16 tg + l%16 of the chunk is column l%16 of MFMA tg. ok_g: tokens of the chunk position g
-// sees (>= 32: all).
+// sees (>= the chunk size: all).
+template <bool FP8>
 __device__ __forceinline__ void chunk_mfma(const uint4* region, int ok_g, const QMulti& qr, int lane,
                                            float (&m)[kHeads]) {
   const int n = lane & 15, g = lane >> 4;
 #pragma unroll
-  for (int tg = 0; tg < 2; ++tg) {
+  for (int tg = 0; tg < KvGeom<FP8>::kChunkTokens / 16; ++tg) {
     const int t = 16 * tg + n;
-    uint4 b[4];
+    bf16x8_t b[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) b[s] = region[t * 16 + ((4 * s + g) ^ n)];
+    for (int s = 0; s < 4; ++s) b[s] = chunk_operand<FP8>(region, t, s, g);
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qr.a[s], __builtin_bit_cast(bf16x8_t, b[s]), acc, 0, 0, 0);
+    for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qr.a[s], b[s], acc, 0, 0, 0);
     const bool ok = t < ok_g;
 #pragma unroll
     for (int h = 0; h < kHeads; ++h) m[h] = ok ? fmaxf(m[h], acc[h]) : m[h];
@@ -820,7 +855,8 @@ __device__ __forceinline__ void chunk_mfma(const uint4* region, int ok_g, const 
 
 struct VerifyArgs {
   const uint16_t* q;    // [batch][Q][4][128]
-  const uint16_t* k;
+  const uint8_t* k;     // bf16 or E4M3 pages
+  float k_scale;        // E4M3 caches: keys are k_scale * value
   const int32_t* bt;
   const int32_t* lens;
   int32_t W, bt_stride;
@@ -837,8 +873,9 @@ __device__ __forceinline__ int causal_len(int L, int Q, int p) { return max(0, L
 // Grid (S, batch), 4 waves; split s of row b owns blocks [s*C, min((s+1)*C, nb)), nb the
 // last position's block count. kScores: block scores out. kSplit: per (position, head) the
 // split's top Lk keys, best first, zero padded.
-template <int MODE>
+template <int MODE, bool FP8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void verify_kernel(VerifyArgs a) {
+  using G = KvGeom<FP8>;
   __shared__ float sc[kMaxSplitBlocks][16];
   __shared__ uint4 stage[kWaves * kChunkSlots];  // one 8 KiB chunk region per wave
   const int s = blockIdx.x;
@@ -868,6 +905,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   // c of block j holds tokens 32c .. 32c+31; a block has ceil(vmax / 32) chunks, vmax the
   // tokens the last position sees. Blocks whose page is out of range score -inf, unread.
   auto emit = [&](int j, float (&m)[kHeads]) {
+    if (FP8) {
+#pragma unroll
+      for (int h = 0; h < kHeads; ++h) m[h] *= a.k_scale;
+    }
     if ((lane & 15) == 0 && g < a.Q) {
       if (MODE == kScores) {
 #pragma unroll
@@ -879,11 +920,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     }
   };
   // First block at or after j with a page in range (out-of-range ones are emitted as -inf).
-  auto next_block = [&](int j, const uint16_t*& pg) {
+  auto next_block = [&](int j, const uint8_t*& pg) {
     for (; j < j1; j += kWaves) {
       const int page = btrow[j];
       if (page >= 0 && (int64_t)page < a.num_pages) {
-        pg = a.k + (size_t)page * kPageElems;
+        pg = a.k + (size_t)page * G::kPageBytes;
         return j;
       }
       if (a.err != nullptr && lane == 0) atomicOr(a.err, (uint32_t)MSA_DEVERR_PAGE_OUT_OF_RANGE);
@@ -894,9 +935,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     }
     return j;
   };
-  auto chunks_of = [&](int j) { return (min(kBlock, L - j * kBlock) + kChunkTokens - 1) / kChunkTokens; };
+  auto chunks_of = [&](int j) { return (min(kBlock, L - j * kBlock) + G::kChunkTokens - 1) / G::kChunkTokens; };
 
-  const uint16_t* pg = nullptr;
+  const uint8_t* pg = nullptr;
   int j = next_block(j0 + wave, pg);
   if (j < j1) {
     int c = 0, nch = chunks_of(j);
@@ -908,15 +949,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     while (true) {
       // Next chunk: the rest of this block, else the first chunk of the wave's next block.
       int nj = j, nc = c + 1;
-      const uint16_t* npg = pg;
+      const uint8_t* npg = pg;
       if (nc == nch) {
         nj = next_block(j + kWaves, npg);
         nc = 0;
       }
       uint4 nx[kChunkLoads];
       if (nj < j1) chunk_load(npg, nc, lane, nx);
-      chunk_to_lds(region, kv, lane);
-      chunk_mfma(region, Lg - j * kBlock - c * kChunkTokens, qr, lane, m);
+      chunk_to_lds<FP8>(region, kv, lane);
+      chunk_mfma<FP8>(region, Lg - j * kBlock - c * G::kChunkTokens, qr, lane, m);
       if (c + 1 == nch) {
 #pragma unroll
         for (int h = 0; h < kHeads; ++h) m[h] = row_max16(m[h]);
@@ -1176,10 +1217,12 @@ size_t ws_bytes_multi(int32_t batch, int32_t Q, const Plan& p) {
 
 VerifyArgs make_verify_args(const void* q, const void* k, const int32_t* bt, const int32_t* lens,
                             int32_t W, int32_t bt_stride, int64_t num_pages, int32_t Q, const Plan& p,
-                            int32_t topk, int32_t n_init, int32_t n_local, void* ws, int32_t batch) {
+                            int32_t topk, int32_t n_init, int32_t n_local, void* ws, int32_t batch,
+                            float k_scale = 1.0f) {
   VerifyArgs a;
   a.q = static_cast<const uint16_t*>(q);
-  a.k = static_cast<const uint16_t*>(k);
+  a.k = static_cast<const uint8_t*>(k);
+  a.k_scale = k_scale;
   a.bt = bt;
   a.lens = lens;
   a.W = W;
@@ -1197,6 +1240,70 @@ VerifyArgs make_verify_args(const void* q, const void* k, const int32_t* bt, con
   a.keys = w ? reinterpret_cast<uint64_t*>(w + keys_offset(batch)) : nullptr;
   a.scores = nullptr;
   return a;
+}
+
+bool valid_scale(float k_scale) { return k_scale > 0.0f && k_scale <= 3.402823466e38f; }
+
+template <int MODE>
+void launch_verify(const VerifyArgs& a, bool fp8, int32_t batch, hipStream_t st) {
+  if (fp8)
+    hipLaunchKernelGGL((verify_kernel<MODE, true>), dim3(a.S, batch), dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((verify_kernel<MODE, false>), dim3(a.S, batch), dim3(kThreads), 0, st, a);
+}
+
+int32_t verify_decode_impl(const void* q, const void* k_cache, bool fp8, float k_scale,
+                           const int32_t* block_table, const int32_t* seq_lens, int32_t batch,
+                           int32_t W, int32_t bt_stride, int64_t num_pages, int32_t qlen,
+                           int32_t topk, int32_t n_init, int32_t n_local, int32_t* out_ids,
+                           float* out_scores, void* workspace, size_t workspace_bytes,
+                           int32_t num_splits, hipStream_t st) {
+  if (qlen < 1 || qlen > MSA_MAX_QUERY_LEN || !valid_scale(k_scale)) return MSA_ERR_INVALID_ARG;
+  int32_t rc = check_inputs(q, k_cache, block_table, seq_lens, batch, W, bt_stride, num_pages);
+  if (rc != MSA_OK) return rc;
+  if ((rc = check_select(topk, n_init, n_local)) != MSA_OK) return rc;
+  Plan p;
+  if ((rc = make_plan(batch, W, topk, num_splits, &p)) != MSA_OK) return rc;
+  if (batch == 0) return MSA_OK;
+  if (!out_ids || !out_scores || !aligned(out_ids, 4) || !aligned(out_scores, 4)) return MSA_ERR_INVALID_ARG;
+  if (!workspace || !aligned(workspace, kAlign)) return MSA_ERR_INVALID_ARG;
+  if (workspace_bytes < ws_bytes_multi(batch, qlen, p)) return MSA_ERR_WORKSPACE_TOO_SMALL;
+  const VerifyArgs a = make_verify_args(q, k_cache, block_table, seq_lens, W, bt_stride, num_pages, qlen,
+                                        p, topk, n_init, n_local, workspace, batch, k_scale);
+  launch_verify<kSplit>(a, fp8, batch, st);
+  if (hipGetLastError() != hipSuccess) return MSA_ERR_HIP;
+  VerifyMergeArgs mg;
+  mg.lens = seq_lens;
+  mg.W = W;
+  mg.Q = qlen;
+  mg.S = p.S;
+  mg.C = p.C;
+  mg.Lk = p.Lk;
+  mg.topk = topk;
+  mg.keys = a.keys;
+  mg.out_ids = out_ids;
+  mg.out_scores = out_scores;
+  const size_t lds = ((size_t)p.S * (p.Lk + 1) + 16 + kPrunedScratch) * sizeof(uint64_t);
+  hipLaunchKernelGGL(verify_merge_kernel, dim3(qlen * kHeads, batch), dim3(64), lds, st, mg);
+  return hipGetLastError() == hipSuccess ? MSA_OK : MSA_ERR_HIP;
+}
+
+int32_t verify_scores_impl(const void* q, const void* k_cache, bool fp8, float k_scale,
+                           const int32_t* block_table, const int32_t* seq_lens, int32_t batch,
+                           int32_t W, int32_t bt_stride, int64_t num_pages, int32_t qlen, float* out,
+                           int32_t num_splits, hipStream_t st) {
+  if (qlen < 1 || qlen > MSA_MAX_QUERY_LEN || !valid_scale(k_scale)) return MSA_ERR_INVALID_ARG;
+  int32_t rc = check_inputs(q, k_cache, block_table, seq_lens, batch, W, bt_stride, num_pages);
+  if (rc != MSA_OK) return rc;
+  Plan p;
+  if ((rc = make_plan(batch, W, 16, num_splits, &p)) != MSA_OK) return rc;
+  if (batch == 0 || W == 0) return MSA_OK;
+  if (!out || !aligned(out, 4)) return MSA_ERR_INVALID_ARG;
+  VerifyArgs a = make_verify_args(q, k_cache, block_table, seq_lens, W, bt_stride, num_pages, qlen, p,
+                                  16, 0, 0, nullptr, batch, k_scale);
+  a.scores = out;
+  launch_verify<kScores>(a, fp8, batch, st);
+  return hipGetLastError() == hipSuccess ? MSA_OK : MSA_ERR_HIP;
 }
 
 int32_t decode_impl(const void* q, const void* k_cache, const int32_t* block_table,
@@ -1402,37 +1509,20 @@ int32_t msa_indexer_decode_multi(const void* q, const void* k_cache, const int32
                                  int32_t qlen, int32_t topk, int32_t n_init, int32_t n_local,
                                  int32_t* out_ids, float* out_scores, void* workspace,
                                  size_t workspace_bytes, int32_t num_splits, void* stream) {
-  if (qlen < 1 || qlen > MSA_MAX_QUERY_LEN) return MSA_ERR_INVALID_ARG;
-  int32_t rc = check_inputs(q, k_cache, block_table, seq_lens, batch, max_blocks_per_seq, bt_stride,
-                            num_pages);
-  if (rc != MSA_OK) return rc;
-  if ((rc = check_select(topk, n_init, n_local)) != MSA_OK) return rc;
-  Plan p;
-  if ((rc = make_plan(batch, max_blocks_per_seq, topk, num_splits, &p)) != MSA_OK) return rc;
-  if (batch == 0) return MSA_OK;
-  if (!out_ids || !out_scores || !aligned(out_ids, 4) || !aligned(out_scores, 4)) return MSA_ERR_INVALID_ARG;
-  if (!workspace || !aligned(workspace, kAlign)) return MSA_ERR_INVALID_ARG;
-  if (workspace_bytes < ws_bytes_multi(batch, qlen, p)) return MSA_ERR_WORKSPACE_TOO_SMALL;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  const VerifyArgs a = make_verify_args(q, k_cache, block_table, seq_lens, max_blocks_per_seq,
-                                        bt_stride, num_pages, qlen, p, topk, n_init, n_local,
-                                        workspace, batch);
-  hipLaunchKernelGGL(verify_kernel<kSplit>, dim3(p.S, batch), dim3(kThreads), 0, st, a);
-  if (hipGetLastError() != hipSuccess) return MSA_ERR_HIP;
-  VerifyMergeArgs mg;
-  mg.lens = seq_lens;
-  mg.W = max_blocks_per_seq;
-  mg.Q = qlen;
-  mg.S = p.S;
-  mg.C = p.C;
-  mg.Lk = p.Lk;
-  mg.topk = topk;
-  mg.keys = a.keys;
-  mg.out_ids = out_ids;
-  mg.out_scores = out_scores;
-  const size_t lds = ((size_t)p.S * (p.Lk + 1) + 16 + kPrunedScratch) * sizeof(uint64_t);
-  hipLaunchKernelGGL(verify_merge_kernel, dim3(qlen * kHeads, batch), dim3(64), lds, st, mg);
-  return hipGetLastError() == hipSuccess ? MSA_OK : MSA_ERR_HIP;
+  return verify_decode_impl(q, k_cache, false, 1.0f, block_table, seq_lens, batch, max_blocks_per_seq,
+                            bt_stride, num_pages, qlen, topk, n_init, n_local, out_ids, out_scores,
+                            workspace, workspace_bytes, num_splits, static_cast<hipStream_t>(stream));
+}
+
+int32_t msa_indexer_decode_fp8(const void* q, const void* k_cache, float k_scale,
+                               const int32_t* block_table, const int32_t* seq_lens, int32_t batch,
+                               int32_t max_blocks_per_seq, int32_t bt_stride, int64_t num_pages,
+                               int32_t qlen, int32_t topk, int32_t n_init, int32_t n_local,
+                               int32_t* out_ids, float* out_scores, void* workspace,
+                               size_t workspace_bytes, int32_t num_splits, void* stream) {
+  return verify_decode_impl(q, k_cache, true, k_scale, block_table, seq_lens, batch, max_blocks_per_seq,
+                            bt_stride, num_pages, qlen, topk, n_init, n_local, out_ids, out_scores,
+                            workspace, workspace_bytes, num_splits, static_cast<hipStream_t>(stream));
 }
 
 int32_t msa_indexer_block_scores_multi(const void* q, const void* k_cache, const int32_t* block_table,
@@ -1440,20 +1530,17 @@ int32_t msa_indexer_block_scores_multi(const void* q, const void* k_cache, const
                                        int32_t max_blocks_per_seq, int32_t bt_stride,
                                        int64_t num_pages, int32_t qlen, float* out,
                                        int32_t num_splits, void* stream) {
-  if (qlen < 1 || qlen > MSA_MAX_QUERY_LEN) return MSA_ERR_INVALID_ARG;
-  int32_t rc = check_inputs(q, k_cache, block_table, seq_lens, batch, max_blocks_per_seq, bt_stride,
-                            num_pages);
-  if (rc != MSA_OK) return rc;
-  Plan p;
-  if ((rc = make_plan(batch, max_blocks_per_seq, 16, num_splits, &p)) != MSA_OK) return rc;
-  if (batch == 0 || max_blocks_per_seq == 0) return MSA_OK;
-  if (!out || !aligned(out, 4)) return MSA_ERR_INVALID_ARG;
-  VerifyArgs a = make_verify_args(q, k_cache, block_table, seq_lens, max_blocks_per_seq, bt_stride,
-                                  num_pages, qlen, p, 16, 0, 0, nullptr, batch);
-  a.scores = out;
-  hipLaunchKernelGGL(verify_kernel<kScores>, dim3(p.S, batch), dim3(kThreads), 0,
-                     static_cast<hipStream_t>(stream), a);
-  return hipGetLastError() == hipSuccess ? MSA_OK : MSA_ERR_HIP;
+  return verify_scores_impl(q, k_cache, false, 1.0f, block_table, seq_lens, batch, max_blocks_per_seq,
+                            bt_stride, num_pages, qlen, out, num_splits, static_cast<hipStream_t>(stream));
+}
+
+int32_t msa_indexer_block_scores_fp8(const void* q, const void* k_cache, float k_scale,
+                                     const int32_t* block_table, const int32_t* seq_lens,
+                                     int32_t batch, int32_t max_blocks_per_seq, int32_t bt_stride,
+                                     int64_t num_pages, int32_t qlen, float* out, int32_t num_splits,
+                                     void* stream) {
+  return verify_scores_impl(q, k_cache, true, k_scale, block_table, seq_lens, batch, max_blocks_per_seq,
+                            bt_stride, num_pages, qlen, out, num_splits, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -251,6 +251,43 @@ def test_decode_multi_workspace_and_no_op(lib):
     assert bs(None, None, None, None, 0, 8, 8, 16, 4, None, 0, None) == OK
 
 
+def _decode_fp8(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, scale=1.0, bt=FAKE, lens=FAKE, batch=2, W=8, stride=8, pages=16, qlen=1,
+             topk=16, n_init=1, n_local=2, ids=FAKE, scores=FAKE, ws=FAKE, ws_bytes=1 << 20,
+             splits=0, stream=None)
+    a.update(kw)
+    return lib.msa_indexer_decode_fp8(a["q"], a["k"], a["scale"], a["bt"], a["lens"], a["batch"],
+                                      a["W"], a["stride"], a["pages"], a["qlen"], a["topk"],
+                                      a["n_init"], a["n_local"], a["ids"], a["scores"], a["ws"],
+                                      a["ws_bytes"], a["splits"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(scale=0.0), INVALID),
+    (dict(scale=-1.0), INVALID),
+    (dict(scale=float("inf")), INVALID),
+    (dict(scale=float("nan")), INVALID),
+    (dict(qlen=0), INVALID),
+    (dict(qlen=5), INVALID),
+    (dict(k=None), INVALID),
+    (dict(k=FAKE + 8), INVALID),
+    (dict(ids=None), INVALID),
+    (dict(topk=0), INVALID),
+    (dict(ws_bytes=100), WS_SMALL),
+])
+def test_decode_fp8_rejects_on_host(lib, kw, code):
+    assert _decode_fp8(lib, **kw) == code
+
+
+def test_decode_fp8_no_op_and_scores_rejections(lib):
+    assert _decode_fp8(lib, batch=0, q=None, k=None, bt=None, lens=None, ids=None, scores=None,
+                       ws=None, ws_bytes=0) == OK
+    bs = lib.msa_indexer_block_scores_fp8
+    assert bs(FAKE, FAKE, 0.0, FAKE, FAKE, 2, 8, 8, 16, 1, FAKE, 0, None) == INVALID
+    assert bs(FAKE, FAKE, 1.0, FAKE, FAKE, 2, 8, 8, 16, 1, None, 0, None) == INVALID
+    assert bs(None, None, 1.0, None, None, 0, 8, 8, 16, 1, None, 0, None) == OK
+
+
 def test_binding_refuses_host_tensors():
     torch = pytest.importorskip("torch")
     from sparse_attention_block_amd import msa_indexer_decode
