@@ -170,3 +170,46 @@ def test_multi_full_size(msa):
     ids, _ = run_multi(msa, inp)
     differ = [len({tuple(sorted(ids[b, 3, h])) for h in range(4)}) == 4 for b in range(inp.batch)]
     assert np.mean(differ) >= 0.9
+
+
+def test_multi_fused_workspace_reuse_and_graph_replay(msa):
+    # The fused verify pass counts each row's finished splits in the workspace and the last
+    # one resets the count: one workspace must serve changing lengths and split counts, and a
+    # captured graph must give the same result on every replay.
+    inp = synth.multi_case(210, [128 * 40] * 5, 40, 4)
+    q, k, bt, lens = to_device_multi(inp)
+    plans = [0, 4, 13, 2, 40, 0]
+    ws = torch.zeros(max(msa.workspace_bytes_multi(5, 40, 4, 16, ns) for ns in plans),
+                     dtype=torch.uint8, device="cuda")
+    rng = np.random.default_rng(3)
+    for it, ns in enumerate(plans):
+        new_lens = rng.integers(0, 128 * 40 + 1, size=5).astype(np.int32)
+        new_lens[it % 5] = 0
+        lens.copy_(torch.from_numpy(new_lens))
+        ids, sc = msa.msa_indexer_decode_multi(q, k, bt, lens, num_splits=ns, workspace=ws)
+        torch.cuda.synchronize()
+        assert np.all(ws[:256 + 5 * 256].view(torch.int32).cpu().numpy() == 0), it
+        cur = synth.Inputs("reuse", inp.q, inp.k_cache, inp.block_table, new_lens)
+        want_ids, _, ref = oracle.decode(cur)
+        for p in range(4):
+            check_selection_vs_oracle(ids.cpu().numpy()[:, p], ref[:, p], position_lens(cur, p),
+                                      16, 1, 2)
+    # graph capture, then replays with lengths changed on the device in between
+    ids = torch.empty((5, 4, 4, 16), dtype=torch.int32, device="cuda")
+    sc = torch.empty((5, 4, 4, 16), dtype=torch.float32, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        msa.msa_indexer_decode_multi(q, k, bt, lens, out_ids=ids, out_scores=sc, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        msa.msa_indexer_decode_multi(q, k, bt, lens, out_ids=ids, out_scores=sc, workspace=ws)
+    for it in range(4):
+        new_lens = rng.integers(1, 128 * 40 + 1, size=5).astype(np.int32)
+        lens.copy_(torch.from_numpy(new_lens))
+        g.replay()
+        torch.cuda.synchronize()
+        eager_ids, eager_sc = msa.msa_indexer_decode_multi(q, k, bt, lens)
+        assert torch.equal(ids, eager_ids) and torch.equal(sc, eager_sc), it
