@@ -50,13 +50,17 @@ def measured_traffic(engine: int):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(inp, repeats: int = 3):
+def cpu_baseline(inp, budget_s: float = 10.0, min_repeats: int = 3):
+    """The oracle as it is, on this host's cores: whole passes over the workload, repeated
+    until about budget_s seconds of wall time (at least min_repeats), median pass time."""
     import oracle
     times = []
-    for _ in range(repeats):
+    t_start = time.perf_counter()
+    while len(times) < min_repeats or time.perf_counter() - t_start < budget_s:
         t0 = time.perf_counter()
         oracle.decode(inp)
         times.append(time.perf_counter() - t0)
+    repeats = len(times)
     t = statistics.median(times)
     return {
         "value": round(inp.index_k_bytes / t / 1e9, 3),

@@ -1,18 +1,23 @@
 // msa_indexer.hip -- MI355X (gfx950) kernels and C ABI of the MiniMax-M3 lightning-indexer
 // decode pass. The ABI and the operation are documented in include/msa_indexer.h.
 //
-// Two kernels per call:
-//   split_kernel  grid (S, batch), 4 waves. A workgroup owns C = ceil(W/S) consecutive
-//                 logical blocks of one row (the split-KV axis of TensorRT-LLM PR #17008,
-//                 Changes). Each wave walks every 4th block of the split: it reads the
-//                 block's page once (32 KiB, 16 B per lane per load) and scores all four
-//                 heads from those registers (SGLang PR #41488, Modifications: every K tile
-//                 scored for all heads while resident). Block maxima go to LDS; then wave h
-//                 ranks the split's keys for head h and writes its top-k, best first.
-//   merge_kernel  grid (4, batch), 1 wave per (row, head): the exact top-min(k, nb) of the
-//                 splits' sorted candidate lists, by repeated extraction of the largest list
-//                 head (vLLM PR #57832, Solution: a global top-k block is in its own shard's
-//                 top-k, so the merge of the per-shard lists is exact).
+// Kernels:
+//   split_kernel   single-token pass over a bf16 cache, grid (S, batch), 4 waves. A
+//                  workgroup owns C = ceil(W/S) consecutive logical blocks of one row (the
+//                  split-KV axis of TensorRT-LLM PR #17008, Changes). Each wave walks every
+//                  4th block of the split: it reads the block's page once (32 KiB, 16 B per
+//                  lane per load) and scores all four heads from those registers (SGLang PR
+//                  #41488, Modifications: every K tile scored for all heads while resident).
+//                  Block maxima go to LDS; then wave h ranks the split's keys for head h and
+//                  writes its top-k, best first. Usually the row's last workgroup then merges
+//                  the row (the fused plan).
+//   verify_kernel  the same decomposition for 1..4 query positions per row and for FP8
+//                  caches, on the MFMA engine (4 positions x 4 heads = 16 rows).
+//   merge_kernel   one wave per (row, position, head): the exact top-min(k, nb) of the
+//                  splits' sorted candidate lists (vLLM PR #57832, Solution: a global top-k
+//                  block is in its own shard's top-k, so the merge of the per-shard lists is
+//                  exact), for unfused plans and the verify kernel.
+//   expand_kernel  16-token page tables of given selections.
 // Grid and workspace depend only on (batch, W, topk, S); per-row lengths are read on the
 // device and splits past a row's end return at once (vLLM PR #57832, CUDA graph capture).
 
@@ -544,6 +549,10 @@ __device__ __forceinline__ int row_tokens(const int32_t* lens, int b, int W) {
   return L < 0 ? 0 : (L > W * kBlock ? W * kBlock : L);
 }
 
+// Tokens that query position p of Q sees in a row of L tokens (the row's last Q tokens are
+// its query positions; TensorRT-LLM PR #17008, Description: the causal clamp).
+__device__ __forceinline__ int causal_len(int L, int Q, int p) { return max(0, L - (Q - 1 - p)); }
+
 // Scores block j of the row for the four heads.
 template <int ENGINE>
 __device__ __forceinline__ void score_page(const SplitArgs& a, const int32_t* btrow, int j, int L,
@@ -682,38 +691,50 @@ __global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Stage 2 on its own (plans too large for the fused merge): one wave per (row, head).
+// Stage 2 on its own: one wave per (row, position-head task), grid (Q*4, batch). Keys are
+// [batch][S][Q*4][Lk]; Q = 1 is the single-token layout [batch][S][4][Lk].
 
 struct MergeArgs {
   const int32_t* lens;
-  int32_t W, S, C, Lk, topk;
+  int32_t W, Q, S, C, Lk, topk;
   const uint64_t* keys;
-  int32_t* out_ids;
+  int32_t* out_ids;     // [batch][Q][4][topk]
   float* out_scores;
-  const int32_t* bt;    // with out_pages: the block table and its row stride
+  const int32_t* bt;    // with out_pages (Q = 1): the block table and its row stride
   int32_t bt_stride;
   int32_t* out_pages;   // may be null
   int32_t* out_tokens;
 };
 
+size_t merge_lds_bytes(int S, int Lk) {
+  return ((size_t)S * (Lk + 1) + 16 + kPrunedScratch) * sizeof(uint64_t);
+}
+
 __global__ __launch_bounds__(64) void merge_kernel(MergeArgs a) {
-  extern __shared__ uint64_t lk[];  // [ns][Lk]
-  const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+  extern __shared__ uint64_t lk[];  // [ns][Lk + 1] lists, 16 keys of slack, pruned scratch
+  const int task = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+  const int p = task >> 2;
   const int L = row_tokens(a.lens, b, a.W);
   const int nb = (L + kBlock - 1) / kBlock;
-  const int m = min(a.topk, nb);
+  const int Lp = causal_len(L, a.Q, p);
+  const int m = min(a.topk, (Lp + kBlock - 1) / kBlock);
   const int ns = (nb + a.C - 1) / a.C;
-  const uint64_t* head_keys = a.keys + ((size_t)b * a.S * kHeads + h) * a.Lk;
-  const int Lk = a.Lk;
-  stage_keys(head_keys, lk, ns * Lk, lane, 64, [Lk](int e) { return (e / Lk) * kHeads * Lk + e % Lk; },
-             [](int e) { return e; });
+  const int Lk = a.Lk, stride = Lk + 1, QH = a.Q * kHeads;
+  const uint64_t* src = a.keys + ((size_t)b * a.S * QH + task) * Lk;
+  stage_keys(src, lk, ns * Lk, lane, 64, [Lk, QH](int e) { return (e / Lk) * QH * Lk + e % Lk; },
+             [Lk, stride](int e) { return (e / Lk) * stride + e % Lk; });
+  for (int e = lane; e < 16; e += 64) lk[ns * stride + e] = 0;
   __syncthreads();
-  const uint64_t mine = merge_rounds(lk, ns, a.Lk, a.Lk, m, lane);
-  const size_t o = ((size_t)b * kHeads + h) * a.topk;
+  uint64_t mine;
+  if (ns <= 64 && a.topk <= kPrunedMaxM)
+    mine = merge_pruned(lk, ns, Lk, stride, m, lane, lk + (size_t)a.S * stride + 16);
+  else
+    mine = merge_rounds(lk, ns, Lk, stride, m, lane);
+  const size_t o = ((size_t)b * QH + task) * a.topk;
   write_selection(mine, m, a.topk, lane, a.out_ids + o, a.out_scores + o);
   if (a.out_pages != nullptr)
-    emit_pages(key_id(mine), lane < m, a.topk, lane, a.bt + (size_t)b * a.bt_stride, L,
-               a.out_pages + o * 8, a.out_tokens + (size_t)b * kHeads + h);
+    emit_pages(key_id(mine), lane < m, a.topk, lane, a.bt + (size_t)b * a.bt_stride, Lp,
+               a.out_pages + o * 8, a.out_tokens + (size_t)b * QH + task);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -867,8 +888,6 @@ struct VerifyArgs {
   float* scores;        // [batch][Q][4][W] (block-score mode)
 };
 
-// Tokens position p of a row of L tokens sees.
-__device__ __forceinline__ int causal_len(int L, int Q, int p) { return max(0, L - (Q - 1 - p)); }
 
 // Grid (S, batch), 4 waves; split s of row b owns blocks [s*C, min((s+1)*C, nb)), nb the
 // last position's block count. kScores: block scores out. kSplit: per (position, head) the
@@ -991,40 +1010,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     if (real && rank < a.Lk) out[rank] = key;
     if (lane >= cnt && lane < a.Lk) out[lane] = 0;
   }
-}
-
-struct VerifyMergeArgs {
-  const int32_t* lens;
-  int32_t W, Q, S, C, Lk, topk;
-  const uint64_t* keys;
-  int32_t* out_ids;     // [batch][Q][4][topk]
-  float* out_scores;
-};
-
-// One wave per (row, position-head task): the exact top-min(topk, nb_p) of the splits'
-// lists (the merge of the single-token pass, per position).
-__global__ __launch_bounds__(64) void verify_merge_kernel(VerifyMergeArgs a) {
-  extern __shared__ uint64_t lk[];  // [ns][Lk + 1] lists, 16 keys of slack, pruned scratch
-  const int task = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
-  const int p = task >> 2;
-  const int L = row_tokens(a.lens, b, a.W);
-  const int nb = (L + kBlock - 1) / kBlock;
-  const int nbp = (causal_len(L, a.Q, p) + kBlock - 1) / kBlock;
-  const int m = min(a.topk, nbp);
-  const int ns = (nb + a.C - 1) / a.C;
-  const int Lk = a.Lk, stride = Lk + 1, QH = a.Q * kHeads;
-  const uint64_t* src = a.keys + ((size_t)b * a.S * QH + task) * Lk;
-  stage_keys(src, lk, ns * Lk, lane, 64, [Lk, QH](int e) { return (e / Lk) * QH * Lk + e % Lk; },
-             [Lk, stride](int e) { return (e / Lk) * stride + e % Lk; });
-  for (int e = lane; e < 16; e += 64) lk[ns * stride + e] = 0;
-  __syncthreads();
-  uint64_t mine;
-  if (ns <= 64 && a.topk <= kPrunedMaxM)
-    mine = merge_pruned(lk, ns, Lk, stride, m, lane, lk + (size_t)a.S * stride + 16);
-  else
-    mine = merge_rounds(lk, ns, Lk, stride, m, lane);
-  const size_t o = ((size_t)b * QH + task) * a.topk;
-  write_selection(mine, m, a.topk, lane, a.out_ids + o, a.out_scores + o);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1177,6 +1162,29 @@ int32_t check_pages(const int32_t* out_pages, const int32_t* out_tokens, const i
   return MSA_OK;
 }
 
+int32_t launch_merge(const uint64_t* keys, const int32_t* lens, int32_t W, int32_t Q, const Plan& p,
+                     int32_t topk, int32_t* out_ids, float* out_scores, int32_t batch, hipStream_t st,
+                     const int32_t* bt = nullptr, int32_t bt_stride = 0, int32_t* out_pages = nullptr,
+                     int32_t* out_tokens = nullptr) {
+  MergeArgs a;
+  a.lens = lens;
+  a.W = W;
+  a.Q = Q;
+  a.S = p.S;
+  a.C = p.C;
+  a.Lk = p.Lk;
+  a.topk = topk;
+  a.keys = keys;
+  a.out_ids = out_ids;
+  a.out_scores = out_scores;
+  a.bt = bt;
+  a.bt_stride = bt_stride;
+  a.out_pages = out_pages;
+  a.out_tokens = out_tokens;
+  hipLaunchKernelGGL(merge_kernel, dim3(Q * kHeads, batch), dim3(64), merge_lds_bytes(p.S, p.Lk), st, a);
+  return hipGetLastError() == hipSuccess ? MSA_OK : MSA_ERR_HIP;
+}
+
 int32_t merge_impl(const int32_t* lens, int32_t batch, int32_t W, int32_t topk, int32_t* out_ids,
                    float* out_scores, const void* ws, size_t ws_size, int32_t num_splits,
                    hipStream_t st, const int32_t* bt = nullptr, int32_t bt_stride = 0,
@@ -1191,23 +1199,9 @@ int32_t merge_impl(const int32_t* lens, int32_t batch, int32_t W, int32_t topk, 
   if (!aligned(lens, 4) || !aligned(out_ids, 4) || !aligned(out_scores, 4) || !aligned(ws, kAlign))
     return MSA_ERR_INVALID_ARG;
   if (ws_size < ws_bytes(batch, p)) return MSA_ERR_WORKSPACE_TOO_SMALL;
-  MergeArgs a;
-  a.lens = lens;
-  a.W = W;
-  a.S = p.S;
-  a.C = p.C;
-  a.Lk = p.Lk;
-  a.topk = topk;
-  a.keys = reinterpret_cast<const uint64_t*>(static_cast<const char*>(ws) + keys_offset(batch));
-  a.out_ids = out_ids;
-  a.out_scores = out_scores;
-  a.bt = bt;
-  a.bt_stride = bt_stride;
-  a.out_pages = out_pages;
-  a.out_tokens = out_tokens;
-  const size_t lds = (size_t)p.S * p.Lk * sizeof(uint64_t);
-  hipLaunchKernelGGL(merge_kernel, dim3(kHeads, batch), dim3(64), lds, st, a);
-  return hipGetLastError() == hipSuccess ? MSA_OK : MSA_ERR_HIP;
+  const uint64_t* keys = reinterpret_cast<const uint64_t*>(static_cast<const char*>(ws) + keys_offset(batch));
+  return launch_merge(keys, lens, W, 1, p, topk, out_ids, out_scores, batch, st, bt, bt_stride,
+                      out_pages, out_tokens);
 }
 
 
@@ -1272,20 +1266,7 @@ int32_t verify_decode_impl(const void* q, const void* k_cache, bool fp8, float k
                                         p, topk, n_init, n_local, workspace, batch, k_scale);
   launch_verify<kSplit>(a, fp8, batch, st);
   if (hipGetLastError() != hipSuccess) return MSA_ERR_HIP;
-  VerifyMergeArgs mg;
-  mg.lens = seq_lens;
-  mg.W = W;
-  mg.Q = qlen;
-  mg.S = p.S;
-  mg.C = p.C;
-  mg.Lk = p.Lk;
-  mg.topk = topk;
-  mg.keys = a.keys;
-  mg.out_ids = out_ids;
-  mg.out_scores = out_scores;
-  const size_t lds = ((size_t)p.S * (p.Lk + 1) + 16 + kPrunedScratch) * sizeof(uint64_t);
-  hipLaunchKernelGGL(verify_merge_kernel, dim3(qlen * kHeads, batch), dim3(64), lds, st, mg);
-  return hipGetLastError() == hipSuccess ? MSA_OK : MSA_ERR_HIP;
+  return launch_merge(a.keys, seq_lens, W, qlen, p, topk, out_ids, out_scores, batch, st);
 }
 
 int32_t verify_scores_impl(const void* q, const void* k_cache, bool fp8, float k_scale,
