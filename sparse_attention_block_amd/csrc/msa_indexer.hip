@@ -862,12 +862,10 @@ __device__ __forceinline__ void chunk_mfma(const uint4* region, int ok_g, const 
 #pragma unroll
   for (int tg = 0; tg < KvGeom<FP8>::kChunkTokens / 16; ++tg) {
     const int t = 16 * tg + n;
-    bf16x8_t b[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) b[s] = chunk_operand<FP8>(region, t, s, g);
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qr.a[s], b[s], acc, 0, 0, 0);
+    for (int s = 0; s < 4; ++s)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qr.a[s], chunk_operand<FP8>(region, t, s, g), acc, 0, 0, 0);
     const bool ok = t < ok_g;
 #pragma unroll
     for (int h = 0; h < kHeads; ++h) m[h] = ok ? fmaxf(m[h], acc[h]) : m[h];
@@ -938,14 +936,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
       }
     }
   };
-  // First block at or after j with a page in range (out-of-range ones are emitted as -inf).
-  auto next_block = [&](int j, const uint8_t*& pg) {
+  // First block at or after j with a page in range (out-of-range ones are emitted as -inf);
+  // its page in *page. Everything here is wave-uniform and kept in scalar registers.
+  auto next_block = [&](int j, int& page) {
     for (; j < j1; j += kWaves) {
-      const int page = btrow[j];
-      if (page >= 0 && (int64_t)page < a.num_pages) {
-        pg = a.k + (size_t)page * G::kPageBytes;
-        return j;
-      }
+      page = __builtin_amdgcn_readfirstlane(btrow[j]);
+      if (page >= 0 && (int64_t)page < a.num_pages) return j;
       if (a.err != nullptr && lane == 0) atomicOr(a.err, (uint32_t)MSA_DEVERR_PAGE_OUT_OF_RANGE);
       float m[kHeads];
 #pragma unroll
@@ -956,41 +952,60 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   };
   auto chunks_of = [&](int j) { return (min(kBlock, L - j * kBlock) + G::kChunkTokens - 1) / G::kChunkTokens; };
 
-  const uint8_t* pg = nullptr;
-  int j = next_block(j0 + wave, pg);
-  if (j < j1) {
-    int c = 0, nch = chunks_of(j);
-    float m[kHeads];
+  // A cursor over that stream: chunk c of block j (page pg, nch chunks); j >= j1 ends it.
+  struct Cursor {
+    int j, c, nch, page;
+  };
+  auto first = [&]() {
+    Cursor u{0, 0, 0, 0};
+    u.j = next_block(j0 + wave, u.page);
+    u.nch = u.j < j1 ? chunks_of(u.j) : 0;
+    return u;
+  };
+  auto advance = [&](const Cursor& u) {
+    Cursor v = u;
+    if (u.j >= j1) return v;
+    if (++v.c < u.nch) return v;
+    v.c = 0;
+    v.j = next_block(u.j + kWaves, v.page);
+    v.nch = v.j < j1 ? chunks_of(v.j) : 0;
+    return v;
+  };
+  auto page_ptr = [&](const Cursor& u) { return a.k + (size_t)u.page * G::kPageBytes; };
+
+  // Two register buffers, two chunks in flight: the chunk in buffer A (landed) is copied to
+  // LDS, A is refilled at once with the chunk two ahead, and the MFMAs of the copied chunk
+  // run while that chunk and the next one (buffer B) are loading.
+  float m[kHeads];
 #pragma unroll
-    for (int h = 0; h < kHeads; ++h) m[h] = -__builtin_inff();
-    uint4 kv[kChunkLoads];
-    chunk_load(pg, 0, lane, kv);
-    while (true) {
-      // Next chunk: the rest of this block, else the first chunk of the wave's next block.
-      int nj = j, nc = c + 1;
-      const uint8_t* npg = pg;
-      if (nc == nch) {
-        nj = next_block(j + kWaves, npg);
-        nc = 0;
-      }
-      uint4 nx[kChunkLoads];
-      if (nj < j1) chunk_load(npg, nc, lane, nx);
-      chunk_to_lds<FP8>(region, kv, lane);
-      chunk_mfma<FP8>(region, Lg - j * kBlock - c * G::kChunkTokens, qr, lane, m);
-      if (c + 1 == nch) {
+  for (int h = 0; h < kHeads; ++h) m[h] = -__builtin_inff();
+  auto process = [&](const Cursor& cur, uint4 (&A)[kChunkLoads], const Cursor& ahead2) {
+    chunk_to_lds<FP8>(region, A, lane);
+    if (ahead2.j < j1) chunk_load(page_ptr(ahead2), ahead2.c, lane, A);
+    chunk_mfma<FP8>(region, Lg - cur.j * kBlock - cur.c * G::kChunkTokens, qr, lane, m);
+    if (cur.c + 1 == cur.nch) {
 #pragma unroll
-        for (int h = 0; h < kHeads; ++h) m[h] = row_max16(m[h]);
-        emit(j, m);
+      for (int h = 0; h < kHeads; ++h) m[h] = row_max16(m[h]);
+      emit(cur.j, m);
 #pragma unroll
-        for (int h = 0; h < kHeads; ++h) m[h] = -__builtin_inff();
-      }
-      if (nj >= j1) break;
-      if (nj != j) nch = chunks_of(nj);
-      j = nj;
-      c = nc;
-      pg = npg;
-#pragma unroll
-      for (int i = 0; i < kChunkLoads; ++i) kv[i] = nx[i];
+      for (int h = 0; h < kHeads; ++h) m[h] = -__builtin_inff();
+    }
+  };
+  Cursor c0 = first();
+  if (c0.j < j1) {
+    Cursor c1 = advance(c0);
+    uint4 A[kChunkLoads], B[kChunkLoads];
+    chunk_load(page_ptr(c0), c0.c, lane, A);
+    if (c1.j < j1) chunk_load(page_ptr(c1), c1.c, lane, B);
+    while (true) {  // two chunks per trip so that A and B trade roles without copies
+      Cursor c2 = advance(c1);
+      process(c0, A, c2);
+      if (c1.j >= j1) break;
+      Cursor c3 = advance(c2);
+      process(c1, B, c3);
+      if (c2.j >= j1) break;
+      c0 = c2;
+      c1 = c3;
     }
   }
   if (MODE == kScores) return;
