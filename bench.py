@@ -50,9 +50,44 @@ def measured_traffic(engine: int):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(inp, budget_s: float = 10.0, min_repeats: int = 3):
-    """The oracle as it is, on this host's cores: whole passes over the workload, repeated
-    until about budget_s seconds of wall time (at least min_repeats), median pass time."""
+def graph_us_per_call(torch, fn, calls: int = 8, replays: int = 100, rounds: int = 7) -> float:
+    """The pages' protocol: `calls` back-to-back calls captured in one HIP graph, replayed
+    `replays` times per round, median over `rounds` of the per-call time (us)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(calls):
+            fn()
+    graph.replay()
+    torch.cuda.synchronize()
+    per_call = []
+    for _ in range(rounds):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(replays):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        per_call.append(e0.elapsed_time(e1) * 1e3 / (replays * calls))
+    return statistics.median(per_call)
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_passes(inp, budget_s: float, min_repeats: int):
     import oracle
     times = []
     t_start = time.perf_counter()
@@ -60,17 +95,31 @@ def cpu_baseline(inp, budget_s: float = 10.0, min_repeats: int = 3):
         t0 = time.perf_counter()
         oracle.decode(inp)
         times.append(time.perf_counter() - t0)
-    repeats = len(times)
-    t = statistics.median(times)
+    return len(times), statistics.median(times)
+
+
+def cpu_baseline(inp, budget_s: float = 10.0, min_repeats: int = 3):
+    """The oracle as it is, on this host's cores: whole passes over the workload, repeated
+    until about budget_s seconds of wall time (at least min_repeats), median pass time; then
+    the same on one thread."""
+    import oracle
+    threads = oracle.num_threads()
+    repeats, t = _oracle_passes(inp, budget_s, min_repeats)
+    oracle.set_num_threads(1)
+    repeats1, t1 = _oracle_passes(inp, budget_s, min_repeats)
+    oracle.set_num_threads(threads)
     return {
         "value": round(inp.index_k_bytes / t / 1e9, 3),
         "unit": "GB/s",
-        "cores": oracle.num_threads(),
+        "cores": threads,
         "kind": "oracle",
         "sample": f"the whole workload (all {inp.batch} rows x {inp.max_blocks} blocks"
                   f"{' x %d positions' % inp.qlen if inp.qlen > 1 else ''}), median of {repeats} "
                   f"passes of scores + selection, fp64, {t * 1e3:.1f} ms/pass",
         "ms_per_step": round(t * 1e3, 3),
+        "single_thread": {"value": round(inp.index_k_bytes / t1 / 1e9, 3), "unit": "GB/s",
+                          "ms_per_step": round(t1 * 1e3, 3), "passes": repeats1},
+        "cpu_model": cpu_model(),
     }
 
 
@@ -115,6 +164,45 @@ def time_page_table(msa, torch, args, q, k, bt, lens, ids, ws, stream, topk, n_i
     res["expand_pages"]["bytes_per_call"] = B * 4 * (topk * 4 + topk * 4 + topk * 32 + 4)
     log(f"page table: {res}")
     return res
+
+
+def bench_configs(msa, synth, np, torch) -> int:
+    """The four smaller workloads, one JSON line each: the decode call under the graph
+    protocol on warm inputs, and cycling through enough copies of the inputs (at least 8,
+    more than 512 MB together) that no call finds its cache lines left by the previous one."""
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    for i in (1, 2, 4, 5):
+        inp = synth.config(i)
+        B, W = inp.batch, inp.max_blocks
+        copies = max(8, -(-(512 << 20) // (inp.k_cache.nbytes + 1)) + 1)
+        k_host = torch.from_numpy(inp.k_cache.view(np.int16))
+        ks = [k_host.to(dev).view(torch.bfloat16) for _ in range(copies)]
+        q = torch.from_numpy(inp.q.view(np.int16)).to(dev).view(torch.bfloat16)
+        bt = torch.from_numpy(inp.block_table).to(dev)
+        lens = torch.from_numpy(inp.seq_lens).to(dev)
+        ws = msa.new_workspace(B, W, inp.topk, 0, dev)
+        ids = torch.empty((B, 4, inp.topk), dtype=torch.int32, device=dev)
+        sc = torch.empty((B, 4, inp.topk), dtype=torch.float32, device=dev)
+
+        def call(k):
+            msa.msa_indexer_decode(q, k, bt, lens, inp.topk, inp.n_init, inp.n_local, out_ids=ids,
+                                   out_scores=sc, workspace=ws)
+
+        warm = graph_us_per_call(torch, lambda: call(ks[0]))
+
+        def rotating():
+            for k in ks:
+                call(k)
+        rot = graph_us_per_call(torch, rotating, calls=1, replays=max(1, 800 // copies)) / copies
+        nbytes = inp.index_k_bytes
+        print(json.dumps({"config": i, "workload": inp.name, "index_k_bytes": nbytes,
+                          "warm_us": round(warm, 2), "rotating_us": round(rot, 2),
+                          "rotating_GBs": round(nbytes / (rot * 1e-6) / 1e9, 1),
+                          "copies": copies, "plan": msa.plan(B, W, inp.topk)}), flush=True)
+        del ks
+        torch.cuda.empty_cache()
+    return 0
 
 
 def bench_multi(args, msa, synth, np, torch) -> int:
@@ -171,6 +259,7 @@ def bench_multi(args, msa, synth, np, torch) -> int:
     if msa.msa_indexer_read_error(ws) != 0:
         log("device error flag set")
         return 1
+    graph_us = graph_us_per_call(torch, step)
     ms_per_step = elapsed * 1e3 / args.steps
     gbs = nbytes / (ms_per_step * 1e-3) / 1e9
     k_gbs = nbytes / (k_ms * 1e-3) / 1e9
@@ -212,6 +301,9 @@ def bench_multi(args, msa, synth, np, torch) -> int:
             "kernel_us": round(k_ms * 1e3, 2),
             "algorithmic_bytes_per_launch": nbytes,
         },
+        "graph": {"us_per_step": round(graph_us, 2),
+                  "GBs": round(nbytes / (graph_us * 1e-6) / 1e9, 2),
+                  "protocol": "8 calls per HIP graph, 100 replays per round, median of 7 rounds"},
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on the same workload")
@@ -235,6 +327,9 @@ def main() -> int:
                          "decode of the same cache, msa_indexer_decode_multi")
     ap.add_argument("--fp8", action="store_true",
                     help="an FP8 E4M3 index-K cache (msa_indexer_decode_fp8, 512 MiB at this shape)")
+    ap.add_argument("--configs", action="store_true",
+                    help="time the four smaller workloads (graph protocol, warm and with rotating "
+                         "input copies) instead of the benchmark step")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip timing the page-table entry points")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -263,6 +358,8 @@ def main() -> int:
     from sparse_attention_block_amd import synth
 
     lib = msa.load()  # raises if the HIP library is not built
+    if args.configs:
+        return bench_configs(msa, synth, np, torch)
     if args.qlen != 1 or args.fp8:
         return bench_multi(args, msa, synth, np, torch)
     log("generating the batch 32 x 131072 workload (1 GiB of bf16 index-K)")
@@ -340,6 +437,9 @@ def main() -> int:
         log("device error flag set")
         return 1
 
+    graph_us = graph_us_per_call(torch, step)
+    log(f"graph protocol: {graph_us:.2f} us per call")
+
     extra = {}
     if plan["fused"] and not args.no_extra:
         extra = time_page_table(msa, torch, args, q, k, bt, lens, ids, ws, stream, topk, n_init,
@@ -392,6 +492,9 @@ def main() -> int:
             "algorithmic_bytes_per_launch": nbytes,
         },
     }
+    out["graph"] = {"us_per_step": round(graph_us, 2),
+                    "GBs": round(nbytes / (graph_us * 1e-6) / 1e9, 2),
+                    "protocol": "8 calls per HIP graph, 100 replays per round, median of 7 rounds"}
     if extra:
         out["page_table"] = extra
     if not args.no_cpu_baseline:

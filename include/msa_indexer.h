@@ -7,6 +7,9 @@
  *      accumulated in fp32, with no scale applied;
  *   2. selects the top `topk` blocks, with the first `n_init` blocks and the last
  *      `n_local` blocks of the row always selected (pinned).
+ * Variants: up to 4 query positions per row (speculative-decode verification,
+ * msa_indexer_decode_multi), an FP8 E4M3 cache (msa_indexer_decode_fp8), and the selection
+ * written as a 16-token page table (msa_indexer_decode_pages, msa_indexer_expand_pages).
  * Sources:
  *   - vLLM PR #57832 "context-parallel decode scoring for MiniMax-M3's sparse lightning
  *     indexer on ROCm": Problem (one index-K head shared by the 4 index heads, every
@@ -34,8 +37,9 @@
  *     device surface at the caller's next synchronization or through the workspace's
  *     error word (msa_indexer_read_error).
  *   - Grid and workspace sizes depend only on (batch, max_blocks_per_seq, topk,
- *     num_splits), never on seq_lens or block_table contents, so a call can be captured
- *     once in a HIP graph and replayed after seq_lens / block_table change on device.
+ *     num_splits) and, for the multi-token and FP8 calls, qlen; never on seq_lens or
+ *     block_table contents, so a call can be captured once in a HIP graph and replayed
+ *     after seq_lens / block_table change on device.
  *   - Argument checks run on the host before any HIP call; a failed check returns a
  *     negative status and enqueues nothing. Nothing aborts.
  *   - Concurrent calls that share a workspace on one device race; give each stream its own.
@@ -92,7 +96,8 @@ int32_t msa_indexer_num_splits(int32_t batch, int32_t max_blocks_per_seq, int32_
  * The plan a call with these arguments uses: S splits per row, C blocks per split, Lk =
  * min(topk, C) candidates kept per (split, head), and whether the merge runs inside the
  * split kernel (fused: one launch) or as a second launch. Any output pointer may be NULL.
- * Returns MSA_OK or a negative status.
+ * Returns MSA_OK or a negative status. The multi-token and FP8 calls use the same S and C
+ * and always merge in a second launch (measured faster for them at every shape tried).
  */
 int32_t msa_indexer_plan(int32_t batch, int32_t max_blocks_per_seq, int32_t topk, int32_t num_splits,
                          int32_t *splits, int32_t *blocks_per_split, int32_t *candidates_per_split,
@@ -103,10 +108,10 @@ int32_t msa_indexer_plan(int32_t batch, int32_t max_blocks_per_seq, int32_t topk
  * Layout: a 256-byte header whose first uint32 is the device error word; then one 256-byte
  * line per row whose first uint32 counts the row's finished splits (uint32 [batch][64]);
  * then the per-split candidate keys, uint64 [batch][S][4][Lk]. The whole workspace must be
- * zero before its first use (e.g.
- * hipMemset once after allocation). The library leaves the counters at zero at the end of
- * every call, so the same workspace can be reused, and replayed in a graph, without
- * clearing it again; the error word only ever gains bits (msa_indexer_read_error clears it).
+ * zero before its first use (e.g. hipMemset once after allocation). The library leaves the
+ * counters at zero at the end of every call, so the same workspace can be reused, and
+ * replayed in a graph, without clearing it again; the error word only ever gains bits
+ * (msa_indexer_read_error clears it).
  */
 size_t msa_indexer_workspace_bytes(int32_t batch, int32_t max_blocks_per_seq, int32_t topk,
                                    int32_t num_splits);

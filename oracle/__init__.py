@@ -43,6 +43,8 @@ class Oracle:
         lib.msa_oracle_decode_multi_fp8.argtypes = [P, P, f64, P, P, i32, i32, i32, i64, i32, i32,
                                                     i32, i32, P, P, P]
         lib.msa_oracle_decode_multi_fp8.restype = ctypes.c_int
+        lib.msa_oracle_set_num_threads.argtypes = [ctypes.c_int]
+        lib.msa_oracle_set_num_threads.restype = None
         lib.msa_oracle_num_threads.argtypes = []
         lib.msa_oracle_num_threads.restype = ctypes.c_int
         self.lib = lib
@@ -50,6 +52,9 @@ class Oracle:
 
     def num_threads(self) -> int:
         return int(self.lib.msa_oracle_num_threads())
+
+    def set_num_threads(self, n: int) -> None:
+        self.lib.msa_oracle_set_num_threads(int(n))
 
     def block_scores(self, q, k_cache, block_table, seq_lens) -> np.ndarray:
         """fp64 block scores [B, 4, W]; -inf at and past each row's end."""
@@ -184,6 +189,10 @@ def default() -> Oracle:
 
 def num_threads() -> int:
     return default().num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    default().set_num_threads(n)
 
 
 def block_scores(q, k_cache, block_table, seq_lens) -> np.ndarray:

@@ -126,6 +126,16 @@ int msa_oracle_num_threads(void)
 #endif
 }
 
+/* Threads later calls use (for timing the oracle on one core and on all of them). */
+void msa_oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /*
  * Block scores, out[b][h][j] for j < max_blocks (fp64). Blocks at or past the
  * row's end hold -inf. Returns OR_ERR_PAGE if a block the row needs maps to a
