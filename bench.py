@@ -473,7 +473,8 @@ def main() -> int:
                         "top-16, 1 initial + 2 recent blocks pinned",
             "batch": B, "seq_len": int(inp.seq_lens[0]), "index_heads": 4, "head_dim": 128,
             "block_tokens": 128, "topk": topk, "n_init": n_init, "n_local": n_local,
-            "num_splits": splits, "blocks_per_split": plan["blocks_per_split"],
+            "num_splits": splits,
+            "blocks_per_split": plan["blocks_per_split"] or "chosen per call on the device",
             "fused_merge": plan["fused"], "engine": engine, "index_k_bytes": nbytes,
             "step_call": "msa_indexer_decode_pages" if args.step == "decode_pages" and plan["fused"]
                          else "msa_indexer_decode",

@@ -383,11 +383,12 @@ __device__ __forceinline__ int count_larger_lds(const uint64_t* a, int n, uint64
   return r;
 }
 
-// Exclusive prefix sum over the wave of c in [0, 31], without LDS: one ballot per bit.
+// Exclusive prefix sum over the wave of c in [0, 2^BITS), without LDS: one ballot per bit.
+template <int BITS = 5>
 __device__ __forceinline__ int wave_prefix_small(int c, int lane) {
   int off = 0;
 #pragma unroll
-  for (int bit = 0; bit < 5; ++bit) {
+  for (int bit = 0; bit < BITS; ++bit) {
     const uint64_t mask = __ballot((c >> bit) & 1);
     const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
@@ -534,6 +535,8 @@ struct SplitArgs {
   int32_t W, bt_stride;
   int64_t num_pages;
   int32_t S, C, Lk, topk, n_init, n_local;
+  int32_t batch;
+  int32_t device_plan;  // fused mode: C and each workgroup's (row, split) chosen on the device
   uint64_t* keys;       // [batch][S][4][Lk]
   uint32_t* err;        // device error word (may be null)
   uint32_t* counters;   // [batch][kCounterStride]: [0] workgroups finished; zero between calls
@@ -554,6 +557,76 @@ __device__ __forceinline__ int row_tokens(const int32_t* lens, int b, int W) {
 __device__ __forceinline__ int causal_len(int L, int Q, int p) { return max(0, L - (Q - 1 - p)); }
 
 // Scores block j of the row for the four heads.
+// ---------------------------------------------------------------------------------------
+// The device plan of the fused single-token pass. The host launches a 1-D grid sized from
+// its arguments alone; every workgroup then reads the row lengths and picks the same split
+// width C: about 512 workgroups in all (measured best for uniform batches: 4..32 rows of
+// 128K tokens), at least 4 blocks per split, and at most 64 splits in any row (the fused
+// merge's fan-in), so a long row among short ones still gets 64 workgroups. Row b takes
+// max(1, ceil(nb_b / C)) consecutive workgroup ids (an empty row one, to write its
+// padding); workgroups past the last row have nothing to do.
+constexpr int kDeviceTarget = 512;     // workgroups the device plan aims at
+constexpr int kDeviceMaxSplits = 64;   // splits per row (the fused merge's fan-in)
+// Tables of fewer blocks (batch x W) keep the host plan: the device plan's prologue (the
+// row lengths read before any page) costs ~1 us, which only pays where a row can be long.
+constexpr int64_t kDeviceMinBlocks = 8192;
+
+// Sum over the wave of x in [0, 2^BITS), without LDS: one ballot per bit.
+template <int BITS>
+__device__ __forceinline__ int wave_sum_bits(int x) {
+  int total = 0;
+#pragma unroll
+  for (int bit = 0; bit < BITS; ++bit) total += __popcll(__ballot((x >> bit) & 1)) << bit;
+  return total;
+}
+
+__device__ __forceinline__ int pow2_ceil_dev(int x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+
+struct DevicePlan {
+  int C, b, s;
+  bool active;
+};
+
+// Wave-uniform: every lane of every wave computes the same plan. Lane l reads the lengths
+// of rows l, l+64, ... (rows past the first 64 are read again in the second pass; they are
+// cache hits); sums, the longest-row bound and prefix sums are ballots, without LDS. Block
+// counts are at most 4096 (13 bits) and split counts at most 64 (7 bits).
+__device__ __forceinline__ DevicePlan device_plan(const int32_t* lens, int batch, int W, int g, int lane) {
+  auto blocks = [&](int r) { return r < batch ? (row_tokens(lens, r, W) + kBlock - 1) / kBlock : 0; };
+  const int nb0 = blocks(lane);
+  int N = 0;
+  bool over[5] = {false, false, false, false, false};  // a row needs more than 64 splits of 4 << t blocks
+  for (int r0 = 0; r0 < batch; r0 += 64) {
+    const int nb = r0 == 0 ? nb0 : blocks(r0 + lane);
+    N += wave_sum_bits<13>(nb);
+#pragma unroll
+    for (int t = 0; t < 5; ++t) over[t] = over[t] || __ballot(nb > (kDeviceMaxSplits << (2 + t))) != 0;
+  }
+  int C_min = 4;
+#pragma unroll
+  for (int t = 0; t < 5; ++t) C_min = over[t] ? (4 << (t + 1)) : C_min;
+  const int C = min(max(pow2_ceil_dev(max(1, (N + kDeviceTarget - 1) / kDeviceTarget)), C_min),
+                    kMaxSplitBlocks);
+  int base = 0;
+  for (int r0 = 0; r0 < batch; r0 += 64) {
+    const int r = r0 + lane;
+    const int nb = r0 == 0 ? nb0 : blocks(r);
+    const int cnt = r < batch ? max(1, (nb + C - 1) / C) : 0;
+    const int first = base + wave_prefix_small<7>(cnt, lane);
+    const uint64_t hit = __ballot(r < batch && g >= first && g < first + cnt);
+    if (hit) {
+      const int l = __builtin_ctzll(hit);
+      return DevicePlan{C, r0 + l, g - __builtin_amdgcn_readlane(first, l), true};
+    }
+    base += wave_sum_bits<7>(cnt);
+  }
+  return DevicePlan{C, 0, 0, false};
+}
+
 template <int ENGINE>
 __device__ __forceinline__ void score_page(const SplitArgs& a, const int32_t* btrow, int j, int L,
                                            int lane, const void* qr, float (&m)[kHeads]) {
@@ -576,10 +649,17 @@ __global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
   __shared__ float sc[kMaxSplitBlocks][kHeads];
   __shared__ int s_last;
 
-  const int s = blockIdx.x;
-  const int b = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int s = blockIdx.x, b = blockIdx.y, C = a.C;
+  if (MODE == kFused && a.device_plan) {
+    const DevicePlan dp = device_plan(a.lens, a.batch, a.W, blockIdx.x, lane);
+    if (!dp.active) return;
+    s = dp.s;
+    b = dp.b;
+    C = dp.C;
+  }
+  const int Lk = min(a.topk, C);
   const int L = row_tokens(a.lens, b, a.W);
   const int nb = (L + kBlock - 1) / kBlock;
 
@@ -587,8 +667,8 @@ __global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
   const int32_t* btrow = a.bt + (size_t)b * a.bt_stride;
 
   if (MODE == kScores) {  // block scores out; -inf at and past the row's end
-    const int j0 = s * a.C, j1 = min(j0 + a.C, nb);
-    const int e0 = max(j0, nb), e1 = min(j0 + a.C, a.W);
+    const int j0 = s * C, j1 = min(j0 + C, nb);
+    const int e0 = max(j0, nb), e1 = min(j0 + C, a.W);
     for (int idx = threadIdx.x; idx < (e1 - e0) * kHeads; idx += kThreads) {
       const int h = idx / (e1 - e0), j = e0 + idx % (e1 - e0);
       a.scores[((size_t)b * kHeads + h) * a.W + j] = -__builtin_inff();
@@ -604,9 +684,9 @@ __global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
     return;
   }
 
-  const int ns = (nb + a.C - 1) / a.C;  // workgroups that take part in this row
-  const int j0 = s * a.C;
-  const int j1 = min(j0 + a.C, nb);
+  const int ns = (nb + C - 1) / C;  // workgroups that take part in this row
+  const int j0 = s * C;
+  const int j1 = min(j0 + C, nb);
   if (s >= ns) {
     // An empty row has no workgroup to merge it: its first workgroup writes the padding.
     if (MODE == kFused && nb == 0 && s == 0) {
@@ -644,9 +724,9 @@ __global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
   const int rank = count_larger(key, n);  // lanes >= n hold key 0
   // Agent-scope atomic stores: written through to the device-coherent level, so the
   // row's last workgroup can read them from any XCD without an L2 writeback.
-  uint64_t* out = a.keys + ((size_t)(b * a.S + s) * kHeads + h) * a.Lk;
-  if (lane < n && rank < a.Lk) __hip_atomic_store(out + rank, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (lane >= n && lane < a.Lk) __hip_atomic_store(out + lane, uint64_t(0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  uint64_t* out = a.keys + ((size_t)(b * a.S + s) * kHeads + h) * Lk;
+  if (lane < n && rank < Lk) __hip_atomic_store(out + rank, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (lane >= n && lane < Lk) __hip_atomic_store(out + lane, uint64_t(0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // Publish this workgroup's lists and count it in. Every wave waits until its list
   // stores have completed (reached the device-coherent level) before the barrier, so the
@@ -670,8 +750,8 @@ __global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
   // Row b's lists are one contiguous range [s][h][i] of the workspace. In LDS each
   // workgroup's four lists get one pad key after them, so that lanes reading list s
   // (stride 4 Lk + 1 keys) fall on different banks.
-  const uint64_t* row_keys = a.keys + (size_t)b * a.S * kHeads * a.Lk;
-  const int row_len = kHeads * a.Lk, stride = row_len + 1;
+  const uint64_t* row_keys = a.keys + (size_t)b * a.S * kHeads * Lk;
+  const int row_len = kHeads * Lk, stride = row_len + 1;
   stage_keys(row_keys, lk, ns * row_len, threadIdx.x, kThreads, [](int e) { return e; },
              [row_len](int e) { return e + e / row_len; });
   __syncthreads();
@@ -679,9 +759,9 @@ __global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
   uint64_t mine;
   if (ns <= 64 && a.topk <= kPrunedMaxM) {
     uint64_t* scratch = lk + (size_t)a.S * stride + h * kPrunedScratch;
-    mine = merge_pruned(lk + h * a.Lk, ns, a.Lk, stride, m, lane, scratch);
+    mine = merge_pruned(lk + h * Lk, ns, Lk, stride, m, lane, scratch);
   } else {
-    mine = merge_rounds(lk + h * a.Lk, ns, a.Lk, stride, m, lane);
+    mine = merge_rounds(lk + h * Lk, ns, Lk, stride, m, lane);
   }
   const size_t o = ((size_t)b * kHeads + h) * a.topk;
   write_selection(mine, m, a.topk, lane, a.out_ids + o, a.out_scores + o);
@@ -1033,6 +1113,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 struct Plan {
   int S, C, Lk;
   bool fused;
+  bool device = false;  // C and the (row, split) of each workgroup are chosen on the device
+  int grid = 0;         // device plan: workgroups launched (1-D)
 };
 
 int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
@@ -1074,6 +1156,26 @@ int32_t make_plan(int32_t batch, int32_t W, int32_t topk, int32_t num_splits, Pl
   }
 }
 
+// The plan of msa_indexer_decode: with num_splits = 0, 0 < W <= 64 * 64, topk <= 16 and
+// batch * W >= kDeviceMinBlocks the device plan (fused, at most min(64, ceil(W/4)) splits per row, Lk <= topk keys per split
+// and head, a grid that covers any lengths: with C >= N/512 and C >= 4 the rows need at
+// most N/C + batch <= 512 + batch workgroups, or ceil(batch*W/64) + batch when C is held at
+// 64); otherwise the host plan above.
+int32_t make_decode_plan(int32_t batch, int32_t W, int32_t topk, int32_t num_splits, Plan* p) {
+  int32_t rc = make_plan(batch, W, topk, num_splits, p);
+  if (rc != MSA_OK) return rc;
+  if (num_splits == 0 && W > 0 && W <= kDeviceMaxSplits * kMaxSplitBlocks && topk <= kPrunedMaxM &&
+      (int64_t)batch * W >= kDeviceMinBlocks) {
+    const int64_t per_row = ceil_div(W, 4);
+    const int64_t need = std::max<int64_t>(kDeviceTarget, ceil_div((int64_t)batch * W, kMaxSplitBlocks)) + batch;
+    Plan d{(int)std::min<int64_t>(kDeviceMaxSplits, per_row), 0, topk, true};
+    d.device = true;
+    d.grid = (int)std::min<int64_t>((int64_t)batch * per_row, need);
+    *p = d;
+  }
+  return MSA_OK;
+}
+
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Workspace: [error word (256 B) | counters uint32 [batch][64] | keys uint64 [batch][S][4][Lk]]
@@ -1084,6 +1186,7 @@ size_t keys_offset(int32_t batch) {
 size_t fused_lds_bytes(const Plan& p) {
   return ((size_t)p.S * (kHeads * p.Lk + 1) + kHeads * kPrunedScratch) * sizeof(uint64_t);
 }
+// (For the device plan p.S and p.Lk bound the per-call values: S splits, Lk <= topk.)
 
 size_t ws_bytes(int32_t batch, const Plan& p) {
   return keys_offset(batch) + (size_t)batch * p.S * kHeads * p.Lk * sizeof(uint64_t);
@@ -1109,8 +1212,10 @@ int32_t check_select(int32_t topk, int32_t n_init, int32_t n_local) {
 }
 
 template <int MODE>
-int32_t launch_split(const SplitArgs& a, int32_t batch, int32_t engine, size_t lds, hipStream_t st) {
+int32_t launch_split(const SplitArgs& a, int32_t batch, int32_t engine, size_t lds, hipStream_t st,
+                     int device_grid = 0) {
   dim3 grid(a.S, batch), block(kThreads);
+  if (device_grid > 0) grid = dim3(device_grid, 1);
   if (engine == MSA_ENGINE_DEFAULT) engine = MSA_ENGINE_VALU;
   if (engine == MSA_ENGINE_VALU)
     hipLaunchKernelGGL((split_kernel<MSA_ENGINE_VALU, MODE>), grid, block, lds, st, a);
@@ -1138,6 +1243,8 @@ SplitArgs make_split_args(const void* q, const void* k, const int32_t* bt, const
   a.topk = topk;
   a.n_init = n_init;
   a.n_local = n_local;
+  a.batch = batch;
+  a.device_plan = p.device ? 1 : 0;
   char* w = static_cast<char*>(ws);
   a.err = w ? reinterpret_cast<uint32_t*>(w) : nullptr;
   a.counters = w ? reinterpret_cast<uint32_t*>(w + kHeaderBytes) : nullptr;
@@ -1154,11 +1261,12 @@ SplitArgs make_split_args(const void* q, const void* k, const int32_t* bt, const
 int32_t check_call(const void* q, const void* k, const int32_t* bt, const int32_t* lens,
                    int32_t batch, int32_t W, int32_t bt_stride, int64_t num_pages, int32_t topk,
                    int32_t n_init, int32_t n_local, const void* ws, size_t ws_size,
-                   int32_t num_splits, Plan* p) {
+                   int32_t num_splits, Plan* p, bool decode = false) {
   int32_t rc = check_inputs(q, k, bt, lens, batch, W, bt_stride, num_pages);
   if (rc != MSA_OK) return rc;
   if ((rc = check_select(topk, n_init, n_local)) != MSA_OK) return rc;
-  if ((rc = make_plan(batch, W, topk, num_splits, p)) != MSA_OK) return rc;
+  rc = decode ? make_decode_plan(batch, W, topk, num_splits, p) : make_plan(batch, W, topk, num_splits, p);
+  if (rc != MSA_OK) return rc;
   if (batch == 0) return MSA_OK;
   if (!ws || !aligned(ws, kAlign)) return MSA_ERR_INVALID_ARG;
   if (ws_size < ws_bytes(batch, *p)) return MSA_ERR_WORKSPACE_TOO_SMALL;
@@ -1314,7 +1422,7 @@ int32_t decode_impl(const void* q, const void* k_cache, const int32_t* block_tab
   if (engine < MSA_ENGINE_DEFAULT || engine > MSA_ENGINE_MFMA) return MSA_ERR_INVALID_ARG;
   Plan p;
   int32_t rc = check_call(q, k_cache, block_table, seq_lens, batch, W, bt_stride, num_pages, topk,
-                          n_init, n_local, workspace, workspace_bytes, num_splits, &p);
+                          n_init, n_local, workspace, workspace_bytes, num_splits, &p, true);
   if (rc != MSA_OK) return rc;
   if (batch > 0 && (rc = check_pages(out_pages, out_tokens, block_table, W, num_pages)) != MSA_OK)
     return rc;
@@ -1326,7 +1434,7 @@ int32_t decode_impl(const void* q, const void* k_cache, const int32_t* block_tab
     a.out_scores = out_scores;
     a.out_pages = out_pages;
     a.out_tokens = out_tokens;
-    return launch_split<kFused>(a, batch, engine, fused_lds_bytes(p), st);
+    return launch_split<kFused>(a, batch, engine, fused_lds_bytes(p), st, p.device ? p.grid : 0);
   }
   if ((rc = launch_split<kSplit>(a, batch, engine, 0, st)) != MSA_OK) return rc;
   return merge_impl(seq_lens, batch, W, topk, out_ids, out_scores, workspace, workspace_bytes,
@@ -1351,7 +1459,7 @@ const char* msa_status_string(int32_t status) {
 int32_t msa_indexer_num_splits(int32_t batch, int32_t max_blocks_per_seq, int32_t topk,
                                int32_t num_splits) {
   Plan p;
-  const int32_t rc = make_plan(batch, max_blocks_per_seq, topk, num_splits, &p);
+  const int32_t rc = make_decode_plan(batch, max_blocks_per_seq, topk, num_splits, &p);
   return rc == MSA_OK ? p.S : rc;
 }
 
@@ -1359,7 +1467,7 @@ int32_t msa_indexer_plan(int32_t batch, int32_t max_blocks_per_seq, int32_t topk
                          int32_t num_splits, int32_t* splits, int32_t* blocks_per_split,
                          int32_t* candidates_per_split, int32_t* fused) {
   Plan p;
-  const int32_t rc = make_plan(batch, max_blocks_per_seq, topk, num_splits, &p);
+  const int32_t rc = make_decode_plan(batch, max_blocks_per_seq, topk, num_splits, &p);
   if (rc != MSA_OK) return rc;
   if (splits) *splits = p.S;
   if (blocks_per_split) *blocks_per_split = p.C;
@@ -1370,9 +1478,10 @@ int32_t msa_indexer_plan(int32_t batch, int32_t max_blocks_per_seq, int32_t topk
 
 size_t msa_indexer_workspace_bytes(int32_t batch, int32_t max_blocks_per_seq, int32_t topk,
                                    int32_t num_splits) {
-  Plan p;
+  Plan p, d;
   if (make_plan(batch, max_blocks_per_seq, topk, num_splits, &p) != MSA_OK) return 0;
-  return ws_bytes(batch, p);
+  if (make_decode_plan(batch, max_blocks_per_seq, topk, num_splits, &d) != MSA_OK) return 0;
+  return std::max(ws_bytes(batch, p), ws_bytes(batch, d));  // the decode and the stage calls
 }
 
 int32_t msa_indexer_split_topk(const void* q, const void* k_cache, const int32_t* block_table,

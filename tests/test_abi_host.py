@@ -44,10 +44,18 @@ def test_status_strings(lib):
 
 def test_split_plan(lib):
     ns = lib.msa_indexer_num_splits
-    # Automatic plan: about batch*W/1024 blocks per split, between 4 and 64.
-    assert ns(32, 1024, 16, 0) == 32
+    # Automatic plan with W <= 4096 and topk <= 16: chosen on the device; the host reports the
+    # most splits a row can get (64, or ceil(W/4) for narrow tables).
+    assert ns(32, 1024, 16, 0) == 64
+    assert ns(16, 4096, 16, 0) == 64
+    assert ns(8, 1024, 16, 0) == 64
+    # small tables (batch * W < 8192 blocks) keep the host plan
     assert ns(1, 64, 16, 0) == 16
     assert ns(16, 68, 16, 0) == 17
+    assert ns(7, 1024, 16, 0) == 128
+    # Wider tables or larger topk: the host plan, about batch*W/1024 blocks per split.
+    assert ns(32, 1024, 17, 0) == 32
+    assert ns(1, 8192, 16, 0) == 256
     # Requested counts are honoured up to empty trailing splits.
     assert ns(16, 68, 16, 4) == 4
     assert ns(16, 68, 16, 60) == 34
@@ -63,17 +71,24 @@ def test_split_plan(lib):
 
 def test_workspace_size(lib):
     ws = lib.msa_indexer_workspace_bytes
-    # error word (256 B), one 256-byte counter line per row, then the keys
-    assert ws(32, 1024, 16, 0) == 256 + 32 * 256 + 32 * 32 * 4 * 16 * 8
-    assert ws(16, 68, 16, 0) == 256 + 16 * 256 + 16 * 17 * 4 * 4 * 8   # 4-block splits keep 4 keys
+    # error word (256 B), one 256-byte counter line per row, then the keys: the larger of the
+    # device plan (up to 64 splits x topk keys per head) and the host plan (the stage calls)
+    assert ws(32, 1024, 16, 0) == 256 + 32 * 256 + 32 * 64 * 4 * 16 * 8
+    assert ws(32, 1024, 16, 32) == 256 + 32 * 256 + 32 * 32 * 4 * 16 * 8
+    # small tables (batch * W < 8192 blocks) keep the host plan: 4-block splits keep 4 keys
+    assert ws(16, 68, 16, 0) == 256 + 16 * 256 + 16 * 17 * 4 * 4 * 8
+    assert ws(16, 68, 16, 17) == 256 + 16 * 256 + 16 * 17 * 4 * 4 * 8   # 4-block splits keep 4 keys
     assert ws(0, 1024, 16, 0) == 256
     assert ws(1, 8, 0, 0) == 0
 
 
 def test_plan_fuses_the_merge_when_it_fits(lib):
     from sparse_attention_block_amd import plan
-    assert plan(32, 1024, 16) == {"splits": 32, "blocks_per_split": 32,
+    # device plan: blocks per split chosen per call (reported as 0)
+    assert plan(32, 1024, 16) == {"splits": 64, "blocks_per_split": 0,
                                   "candidates_per_split": 16, "fused": True}
+    assert plan(32, 1024, 16, 32) == {"splits": 32, "blocks_per_split": 32,
+                                      "candidates_per_split": 16, "fused": True}
     assert plan(1, 64, 16)["fused"] and plan(16, 68, 16)["fused"] and plan(8, 256, 16)["fused"]
     assert plan(16, 1024, 16)["fused"]
     big = plan(1, 16384, 16)          # 256 splits x 16 candidates: merged by a second kernel

@@ -1,0 +1,118 @@
+"""GPU parity of the device plan: with num_splits = 0 (W <= 4096, topk <= 16, batch * W at
+least 8192 blocks) the fused
+single-token pass picks the split width and each workgroup's (row, split) on the device from
+the row lengths (about 512 workgroups in all, at most 64 splits per row). Scores do not depend
+on the plan, so the selection must equal the oracle's selection on the GPU's own block scores,
+and the oracle's within the near-tie rule; exact-integer data must match bit for bit."""
+import numpy as np
+import pytest
+
+import oracle
+from sparse_attention_block_amd import synth
+
+from gpu_util import check_selection_exact_given_scores, check_selection_vs_oracle, to_device
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def msa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_attention_block_amd as m
+    m.load()
+    return m
+
+
+def check(msa, inp, ids=None, sc=None):
+    q, k, bt, lens = to_device(inp)
+    assert msa.plan(inp.batch, inp.max_blocks, inp.topk)["blocks_per_split"] == 0  # device plan
+    if ids is None:
+        ids, sc = msa.msa_indexer_decode(q, k, bt, lens, inp.topk, inp.n_init, inp.n_local)
+    gpu_s = msa.msa_indexer_block_scores(q, k, bt, lens).cpu().numpy()
+    ids, sc = ids.cpu().numpy(), sc.cpu().numpy()
+    check_selection_exact_given_scores(ids, sc, gpu_s, inp.seq_lens, inp.topk, inp.n_init, inp.n_local)
+    ref = oracle.block_scores(inp.q, inp.k_cache, inp.block_table, inp.seq_lens)
+    check_selection_vs_oracle(ids, ref, inp.seq_lens, inp.topk, inp.n_init, inp.n_local)
+    return ids
+
+
+def test_many_rows_cross_the_wave_scan(msa):
+    # 150 rows: the device prefix scan over row split counts runs in three 64-row chunks.
+    rng = np.random.default_rng(401)
+    lens = rng.integers(0, 128 * 20, size=150)
+    lens[[3, 70, 149]] = [128 * 40, 128 * 33 + 5, 1]
+    inp = synth.paged_case(401, lens.tolist(), 60)   # 150 x 60 blocks: the device plan
+    check(msa, inp)
+
+
+def test_long_row_among_empty_rows(msa):
+    # One 1024-block row and 47 empty rows: each empty row still gets a workgroup for its
+    # padding, and the long row gets 64 splits.
+    lens = [0] * 48
+    lens[17] = 128 * 1024
+    inp = synth.paged_case(402, lens, 1024)
+    ids = check(msa, inp)
+    assert np.all(ids[np.arange(48) != 17] == -1)
+
+
+def test_widest_device_table(msa):
+    # W = 4096: the longest row takes 64 splits of 64 blocks (the largest staged lists).
+    inp = synth.paged_case(403, [128 * 4096, 128 * 100 + 7, 128 * 4095], 4096, poison=False)
+    check(msa, inp)
+    # one block wider: the host plan
+    assert msa.plan(3, 4097, 16)["blocks_per_split"] > 0
+
+
+def test_planted_exact_under_device_plan(msa):
+    # The planted workload behind a table widened to 512 blocks, so that the decode call
+    # takes the device plan (the rows still hold 68 blocks).
+    inp = synth.config(5)
+    want_ids, want_sc, _ = oracle.decode(inp)
+    q, k, bt, lens = to_device(inp, extra_cols=512 - 68)
+    assert msa.plan(16, 512, 16)["blocks_per_split"] == 0
+    ids, sc = msa.msa_indexer_decode(q, k, bt, lens)
+    assert np.array_equal(ids.cpu().numpy(), want_ids)
+    assert np.array_equal(sc.cpu().numpy().astype(np.float64), want_sc)
+
+
+def test_split_width_changes_between_graph_replays(msa):
+    # The captured grid covers any lengths; replays with lengths that move the device's
+    # split width (C = 4 .. 64) and the long row's split count must match eager calls.
+    inp = synth.paged_case(404, [128 * 512] * 32, 512, poison=False)
+    q, k, bt, lens = to_device(inp)
+    ws = msa.new_workspace(32, 512, 16)
+    ids = torch.empty((32, 4, 16), dtype=torch.int32, device="cuda")
+    sc = torch.empty((32, 4, 16), dtype=torch.float32, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        msa.msa_indexer_decode(q, k, bt, lens, out_ids=ids, out_scores=sc, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        msa.msa_indexer_decode(q, k, bt, lens, out_ids=ids, out_scores=sc, workspace=ws)
+    rng = np.random.default_rng(5)
+    for it, kind in enumerate(["all long", "one long", "all short", "mixed", "empty"]):
+        if kind == "all long":
+            new = np.full(32, 128 * 512)
+        elif kind == "one long":
+            new = np.zeros(32, np.int64); new[9] = 128 * 512
+        elif kind == "all short":
+            new = rng.integers(1, 300, size=32)
+        elif kind == "mixed":
+            new = rng.integers(0, 128 * 512 + 1, size=32)
+        else:
+            new = np.zeros(32, np.int64)
+        lens.copy_(torch.from_numpy(new.astype(np.int32)))
+        g.replay()
+        torch.cuda.synchronize()
+        eager_ids, eager_sc = msa.msa_indexer_decode(q, k, bt, lens)
+        assert torch.equal(ids, eager_ids) and torch.equal(sc, eager_sc), kind
+        cur = synth.Inputs("replay", inp.q, inp.k_cache, inp.block_table, new.astype(np.int32))
+        gpu_s = msa.msa_indexer_block_scores(q, k, bt, lens).cpu().numpy()
+        check_selection_exact_given_scores(ids.cpu().numpy(), sc.cpu().numpy(), gpu_s, cur.seq_lens,
+                                           16, 1, 2)

@@ -222,11 +222,12 @@ def test_graph_replay_with_changing_lengths(msa):
 
 
 def test_unfused_plan_parity(msa):
-    # Long rows at batch 2: 256 splits x 16 candidates per head do not fit the fused merge,
-    # so decode runs stage 1 and the separate merge kernel.
-    lens = [128 * 3000 + 65, 128 * 4096]
-    assert not msa.plan(2, 4096, 16)["fused"]
-    inp = synth.paged_case(110, lens, 4096)
+    # Long rows at batch 2 in a table wider than the device plan's 4096 blocks: about 240
+    # splits x 16 candidates per head do not fit the fused merge, so decode runs stage 1
+    # and the separate merge kernel.
+    lens = [128 * 3000 + 65, 128 * 4097]
+    assert not msa.plan(2, 4097, 16)["fused"]
+    inp = synth.paged_case(110, lens, 4097)
     ref = oracle.block_scores(inp.q, inp.k_cache, inp.block_table, inp.seq_lens)
     run_case(msa, inp, ref, engine_list=[1], splits=(0,))
 
