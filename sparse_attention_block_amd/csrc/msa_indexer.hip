@@ -18,8 +18,9 @@
 //                  block is in its own shard's top-k, so the merge of the per-shard lists is
 //                  exact), for unfused plans and the verify kernel.
 //   expand_kernel  16-token page tables of given selections.
-// Grid and workspace depend only on (batch, W, topk, S); per-row lengths are read on the
-// device and splits past a row's end return at once (vLLM PR #57832, CUDA graph capture).
+// Grid and workspace depend only on host arguments (batch, W, topk, S, qlen); row lengths
+// are read on the device, where the decode call's device plan also picks its split width,
+// and splits past a row's end return at once (vLLM PR #57832, CUDA graph capture).
 
 #include <hip/hip_runtime.h>
 
@@ -48,7 +49,7 @@ constexpr size_t kAlign = 256;
 // like atomics on one address (measured ~10 ns each under contention), so rows sharing a
 // line would queue behind each other.
 constexpr int kCounterStride = 64;
-constexpr int kPageElems = kBlock * kDim;       // bf16 elements per page
+constexpr int kPageElems = kBlock * kDim;       // elements per page (bf16: 32 KiB, E4M3: 16 KiB)
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
