@@ -34,8 +34,17 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def code_hash(text: str) -> str:
+    """sha256 (first 16 hex) of HIP/C++ source with its comments and whitespace removed, so
+    that an edit of comments alone does not count as a change of the kernel."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return hashlib.sha256(" ".join(text.split()).encode()).hexdigest()[:16]
+
+
 def kernel_source_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+    return code_hash(open(KERNEL_SOURCE).read())
 
 
 def measured_traffic(engine: int):
