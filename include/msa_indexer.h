@@ -208,6 +208,21 @@ int32_t msa_indexer_expand_pages(const int32_t *ids, const int32_t *block_table,
                                  int32_t *out_pages, int32_t *out_tokens, void *stream);
 
 /*
+ * msa_indexer_expand_pages for the selections of a multi-token pass (the page-table builder
+ * reused for speculative-decode verification, vLLM blog "Following the Bottleneck", section
+ * 3): ids int32 [batch][qlen][4][topk] as msa_indexer_decode_multi writes them; selection
+ * (b, p) uses block_table row b and position p's causal length L_p = max(0, len_b -
+ * (qlen-1-p)) (len_b clamped to the table first) for its ids' range and its token count.
+ * out_pages int32 [batch][qlen][4][8*topk] (16-byte aligned), out_tokens int32
+ * [batch][qlen][4]. qlen in 1..MSA_MAX_QUERY_LEN; qlen = 1 is msa_indexer_expand_pages.
+ */
+int32_t msa_indexer_expand_pages_multi(const int32_t *ids, const int32_t *block_table,
+                                       const int32_t *seq_lens, int32_t batch,
+                                       int32_t max_blocks_per_seq, int32_t bt_stride, int32_t qlen,
+                                       int32_t topk, int32_t *out_pages, int32_t *out_tokens,
+                                       void *stream);
+
+/*
  * Workspace bytes of msa_indexer_decode_multi (0 on invalid arguments): the layout of
  * msa_indexer_workspace_bytes with keys uint64 [batch][S][qlen*4][Lk]. Zeroed once before
  * its first use, like the single-token workspace.

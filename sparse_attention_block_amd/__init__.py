@@ -18,6 +18,7 @@ from ._lib import (  # noqa: F401
     msa_indexer_decode_multi,
     msa_indexer_decode_pages,
     msa_indexer_expand_pages,
+    msa_indexer_expand_pages_multi,
     msa_indexer_merge,
     msa_indexer_read_error,
     msa_indexer_split_topk,

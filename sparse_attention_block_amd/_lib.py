@@ -47,6 +47,7 @@ _SIGNATURES = {
     "msa_indexer_decode_pages": ([_P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32, _I32, _P, _P,
                                   _P, _P, _P, _SZ, _I32, _I32, _P], _I32),
     "msa_indexer_expand_pages": ([_P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _P], _I32),
+    "msa_indexer_expand_pages_multi": ([_P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P], _I32),
     "msa_indexer_workspace_bytes_multi": ([_I32, _I32, _I32, _I32, _I32], _SZ),
     "msa_indexer_decode_multi": ([_P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32, _I32, _I32, _P,
                                   _P, _P, _SZ, _I32, _P], _I32),
@@ -355,6 +356,30 @@ def msa_indexer_block_scores_fp8(q, k_cache, k_scale, block_table, seq_lens, num
                                              num_splits, _stream(stream))
     _check("msa_indexer_block_scores_fp8", rc)
     return out
+
+
+def msa_indexer_expand_pages_multi(ids, block_table, seq_lens, out_pages=None, out_tokens=None,
+                                   stream=None):
+    """16-token page tables of multi-token selections ids int32 [B,Q,4,topk]:
+    (out_pages [B,Q,4,8*topk], out_tokens [B,Q,4])."""
+    torch = _torch()
+    if ids.dim() != 4 or ids.shape[2] != HEADS:
+        raise ValueError("ids: expected [batch, qlen, 4, topk]")
+    B, Q, topk = ids.shape[0], ids.shape[1], ids.shape[3]
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table: expected [batch, max_blocks]")
+    if out_pages is None:
+        out_pages = torch.empty((B, Q, HEADS, 8 * topk), dtype=torch.int32, device=ids.device)
+    if out_tokens is None:
+        out_tokens = torch.empty((B, Q, HEADS), dtype=torch.int32, device=ids.device)
+    rc = load().msa_indexer_expand_pages_multi(
+        _dev(ids, "ids", torch.int32), _dev(block_table, "block_table", torch.int32),
+        _dev(seq_lens, "seq_lens", torch.int32, (B,)), B, block_table.shape[1],
+        block_table.stride(0), Q, topk,
+        _dev(out_pages, "out_pages", torch.int32, (B, Q, HEADS, 8 * topk)),
+        _dev(out_tokens, "out_tokens", torch.int32, (B, Q, HEADS)), _stream(stream))
+    _check("msa_indexer_expand_pages_multi", rc)
+    return out_pages, out_tokens
 
 
 def msa_indexer_split_topk(q, k_cache, block_table, seq_lens, workspace, topk=16, n_init=1,

@@ -822,20 +822,21 @@ __global__ __launch_bounds__(64) void merge_kernel(MergeArgs a) {
 // Page tables of given selections: one workgroup per row, wave h for head h.
 
 struct ExpandArgs {
-  const int32_t* ids;   // [batch][4][topk]
+  const int32_t* ids;   // [batch][Q][4][topk]
   const int32_t* bt;
   const int32_t* lens;
-  int32_t W, bt_stride, topk;
-  int32_t* out_pages;   // [batch][4][8 topk]
-  int32_t* out_tokens;  // [batch][4]
+  int32_t W, bt_stride, topk, Q;
+  int32_t* out_pages;   // [batch][Q][4][8 topk]
+  int32_t* out_tokens;  // [batch][Q][4]
 };
 
+// Workgroup r = b*Q + p: selection (b, p), block-table row b, position p's causal length.
 __global__ __launch_bounds__(kThreads) void expand_kernel(ExpandArgs a) {
-  const int b = blockIdx.x;
+  const int r = blockIdx.x, b = r / a.Q, p = r % a.Q;
   const int h = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int L = row_tokens(a.lens, b, a.W);
+  const int L = causal_len(row_tokens(a.lens, b, a.W), a.Q, p);
   const int nb = (L + kBlock - 1) / kBlock;
-  const size_t bh = (size_t)b * kHeads + h;
+  const size_t bh = (size_t)r * kHeads + h;
   const int id = lane < a.topk ? a.ids[bh * a.topk + lane] : -1;
   emit_pages(id, id >= 0 && id < nb, a.topk, lane, a.bt + (size_t)b * a.bt_stride, L,
              a.out_pages + bh * a.topk * 8, a.out_tokens + bh);
@@ -1551,8 +1552,17 @@ int32_t msa_indexer_expand_pages(const int32_t* ids, const int32_t* block_table,
                                  const int32_t* seq_lens, int32_t batch,
                                  int32_t max_blocks_per_seq, int32_t bt_stride, int32_t topk,
                                  int32_t* out_pages, int32_t* out_tokens, void* stream) {
+  return msa_indexer_expand_pages_multi(ids, block_table, seq_lens, batch, max_blocks_per_seq,
+                                        bt_stride, 1, topk, out_pages, out_tokens, stream);
+}
+
+int32_t msa_indexer_expand_pages_multi(const int32_t* ids, const int32_t* block_table,
+                                       const int32_t* seq_lens, int32_t batch,
+                                       int32_t max_blocks_per_seq, int32_t bt_stride, int32_t qlen,
+                                       int32_t topk, int32_t* out_pages, int32_t* out_tokens,
+                                       void* stream) {
   if (batch < 0 || max_blocks_per_seq < 0 || bt_stride < max_blocks_per_seq) return MSA_ERR_INVALID_ARG;
-  if (topk < 1 || topk > MSA_MAX_TOPK) return MSA_ERR_INVALID_ARG;
+  if (topk < 1 || topk > MSA_MAX_TOPK || qlen < 1 || qlen > MSA_MAX_QUERY_LEN) return MSA_ERR_INVALID_ARG;
   if (max_blocks_per_seq > MSA_MAX_BLOCKS_PER_SEQ) return MSA_ERR_UNSUPPORTED;
   if (batch == 0) return MSA_OK;
   if (!ids || !seq_lens || !out_pages || !out_tokens || (!block_table && max_blocks_per_seq > 0))
@@ -1567,9 +1577,10 @@ int32_t msa_indexer_expand_pages(const int32_t* ids, const int32_t* block_table,
   a.W = max_blocks_per_seq;
   a.bt_stride = bt_stride;
   a.topk = topk;
+  a.Q = qlen;
   a.out_pages = out_pages;
   a.out_tokens = out_tokens;
-  hipLaunchKernelGGL(expand_kernel, dim3(batch), dim3(kThreads), 0, static_cast<hipStream_t>(stream), a);
+  hipLaunchKernelGGL(expand_kernel, dim3(batch * qlen), dim3(kThreads), 0, static_cast<hipStream_t>(stream), a);
   return hipGetLastError() == hipSuccess ? MSA_OK : MSA_ERR_HIP;
 }
 

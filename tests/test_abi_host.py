@@ -217,6 +217,15 @@ def test_expand_pages_rejects_on_host(lib, kw, code):
     assert _expand(lib, **kw) == code
 
 
+def test_expand_pages_multi_rejects_on_host(lib):
+    ex = lib.msa_indexer_expand_pages_multi
+    assert ex(FAKE, FAKE, FAKE, 2, 8, 8, 0, 16, FAKE, FAKE, None) == INVALID    # qlen 0
+    assert ex(FAKE, FAKE, FAKE, 2, 8, 8, 5, 16, FAKE, FAKE, None) == INVALID    # qlen 5
+    assert ex(FAKE, FAKE, FAKE, 2, 8, 8, 4, 65, FAKE, FAKE, None) == INVALID    # topk
+    assert ex(FAKE, FAKE, FAKE, 2, 8, 8, 4, 16, FAKE + 4, FAKE, None) == INVALID
+    assert ex(None, None, None, 0, 8, 8, 4, 16, None, None, None) == OK
+
+
 def test_expand_pages_batch_zero_is_a_no_op(lib):
     assert _expand(lib, batch=0, ids=None, bt=None, lens=None, pt=None, tok=None) == OK
 

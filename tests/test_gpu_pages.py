@@ -143,3 +143,23 @@ def test_expand_pages_strided_table(msa):
     want_p, want_t = oracle.expand_pages(ids, np.ascontiguousarray(full[:, :16]), lens)
     assert np.array_equal(out_p.cpu().numpy(), want_p)
     assert np.array_equal(out_t.cpu().numpy(), want_t)
+
+
+@pytest.mark.parametrize("Q", [1, 3, 4])
+def test_expand_pages_multi_token(msa, Q):
+    # The selections of a multi-token pass, expanded per (row, position) with the position's
+    # causal length; each position's table equals the oracle's expansion with that length.
+    inp = synth.multi_case(66, [128 * 30 + 2, 3, 0, 128 * 12, 129], 31, Q)
+    q = torch.from_numpy(np.ascontiguousarray(inp.q).view(np.int16)).cuda().view(torch.bfloat16)
+    k = torch.from_numpy(inp.k_cache.view(np.int16)).cuda().view(torch.bfloat16)
+    bt = torch.from_numpy(inp.block_table).cuda()
+    lens = torch.from_numpy(inp.seq_lens).cuda()
+    ids, _ = msa.msa_indexer_decode_multi(q, k, bt, lens)
+    pages, tokens = msa.msa_indexer_expand_pages_multi(ids, bt, lens)
+    ids, pages, tokens = ids.cpu().numpy(), pages.cpu().numpy(), tokens.cpu().numpy()
+    L = np.clip(inp.seq_lens.astype(np.int64), 0, inp.max_blocks * 128)
+    for p in range(Q):
+        lp = np.maximum(L - (Q - 1 - p), 0).astype(np.int32)
+        want_p, want_t = oracle.expand_pages(np.ascontiguousarray(ids[:, p]), inp.block_table, lp)
+        assert np.array_equal(pages[:, p], want_p), p
+        assert np.array_equal(tokens[:, p], want_t), p
