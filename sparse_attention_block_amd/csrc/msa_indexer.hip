@@ -66,9 +66,11 @@ __device__ __forceinline__ uint4 load_stream(const uint4* p) {
 // ---------------------------------------------------------------------------------------
 // Cross-lane helpers (DPP within 16-lane rows, readlane across rows).
 
+// Every pattern used here reads a lane of the same row, so bound_ctrl (out-of-row reads
+// give 0) never applies; setting it lets the compiler fold more moves into their adds.
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, true);
 }
 
 template <int CTRL>
@@ -114,17 +116,65 @@ __device__ __forceinline__ uint64_t readlane_u64(uint64_t x, int lane) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-// Number of lanes i < n whose x is larger than this lane's x (all lanes active). Lanes
-// past n are read too when n is not a multiple of 8; callers keep them at 0, which is
-// never larger. Eight reads per step keep the loop from stalling on each one.
-__device__ __forceinline__ int count_larger(uint64_t x, int n) {
-  int r = 0;
-  const int n8 = (n + 7) & ~7;
-  for (int i0 = 0; i0 < n8; i0 += 8) {
-#pragma unroll
-    for (int u = 0; u < 8; ++u) r += readlane_u64(x, i0 + u) > x ? 1 : 0;
-  }
-  return r;
+// Bitonic networks on 64-bit keys over the 64 lanes of a wave (all lanes active), best
+// (largest) first. A step pairs each lane with a partner, and of the two the lane with the
+// lower index keeps the larger key. Stage k (k = 2, 4, .., 64) sorts blocks of k lanes:
+// its first step pairs a lane with its mirror in the block (lane ^ (k - 1)), which leaves
+// two bitonic halves with every key of the first at least every key of the second, and
+// the half-cleaner steps after it pair lane ^ j for j = k/4, .., 1. Partners within a
+// 16-lane row come from DPP (lane ^ 4 as lane ^ 3 followed by lane ^ 7); the others from
+// ds_bpermute.
+constexpr int kQuadRev = 0x1B;  // quad_perm [3,2,1,0]: partner lane ^ 3
+constexpr int kRowRor8 = 0x128; // row_ror:8: partner lane ^ 8 within each 16 lanes
+
+__device__ __forceinline__ uint64_t bpermute_u64(uint64_t x, int src_lane) {
+  const int lo = __builtin_amdgcn_ds_bpermute(src_lane << 2, (int)(uint32_t)x);
+  const int hi = __builtin_amdgcn_ds_bpermute(src_lane << 2, (int)(uint32_t)(x >> 32));
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+// The key of lane ^ X.
+template <int X>
+__device__ __forceinline__ uint64_t partner_u64(uint64_t x) {
+  if constexpr (X == 1) return dpp_u64<kQuadSwap1>(x);
+  else if constexpr (X == 2) return dpp_u64<kQuadSwap2>(x);
+  else if constexpr (X == 3) return dpp_u64<kQuadRev>(x);
+  else if constexpr (X == 4) return dpp_u64<kRowHalfMirror>(dpp_u64<kQuadRev>(x));
+  else if constexpr (X == 7) return dpp_u64<kRowHalfMirror>(x);
+  else if constexpr (X == 8) return dpp_u64<kRowRor8>(x);
+  else if constexpr (X == 15) return dpp_u64<kRowMirror>(x);
+  else return bpermute_u64(x, (int)(__lane_id() ^ X));
+}
+
+template <int X, int UPPER>
+__device__ __forceinline__ uint64_t bitonic_step(uint64_t x, int lane) {
+  const uint64_t p = partner_u64<X>(x);
+  return ((p > x) != ((lane & UPPER) != 0)) ? p : x;
+}
+
+// Sorts each 16-lane row that holds a bitonic sequence.
+__device__ __forceinline__ uint64_t bitonic_clean16(uint64_t x, int lane) {
+  x = bitonic_step<8, 8>(x, lane);
+  x = bitonic_step<4, 4>(x, lane);
+  x = bitonic_step<2, 2>(x, lane);
+  return bitonic_step<1, 1>(x, lane);
+}
+
+// Sorts the wave's 64 keys: lane r ends with the r-th largest.
+__device__ __forceinline__ uint64_t sort64_desc(uint64_t x, int lane) {
+  x = bitonic_step<1, 1>(x, lane);
+  x = bitonic_step<3, 2>(x, lane);
+  x = bitonic_step<1, 1>(x, lane);
+  x = bitonic_step<7, 4>(x, lane);
+  x = bitonic_step<2, 2>(x, lane);
+  x = bitonic_step<1, 1>(x, lane);
+  x = bitonic_step<15, 8>(x, lane);
+  x = bitonic_step<4, 4>(x, lane);
+  x = bitonic_step<2, 2>(x, lane);
+  x = bitonic_step<1, 1>(x, lane);
+  x = bitonic_clean16(bitonic_step<31, 16>(x, lane), lane);
+  x = bitonic_step<63, 32>(x, lane);
+  return bitonic_clean16(bitonic_step<16, 16>(x, lane), lane);
 }
 
 // Largest value over the 64 lanes of a wave (all lanes active).
@@ -326,7 +376,7 @@ __device__ __forceinline__ void stage_keys(const uint64_t* __restrict__ src, uin
 // One wave, all lanes active: the m largest keys of ns lists of Lk keys each (sorted best
 // first, zero padded; list sp starts at lk[sp * stride]) held in LDS, by m rounds of "take
 // the largest list head". Lane l owns lists l, l+64, l+128, l+192. Lane i < m returns the
-// i-th key. Used when the lists are too many or too long for merge_pruned.
+// i-th key. Used when the lists are too many or too long for merge_top16.
 __device__ __forceinline__ uint64_t merge_rounds(const uint64_t* lk, int ns, int Lk, int stride, int m,
                                                  int lane) {
   constexpr int kLists = kMaxSplits / 64;
@@ -357,116 +407,43 @@ __device__ __forceinline__ uint64_t merge_rounds(const uint64_t* lk, int ns, int
   return mine;
 }
 
-// One wave, all lanes active, ns <= 64 lists (lane l owns list l), m <= kPrunedMaxM:
-// the same result as merge_rounds without m serial rounds. A list whose head ranks r-th
-// among the heads has r larger heads and, at position i, i larger keys of its own, so
-// only lists with r < m and positions i < m - r can hold a winner; and no winner is below
-// T0, the m-th largest head (m heads are at least T0). The at most m(m+1)/2 survivors are
-// ranked by counting; since every key above a winner is itself a survivor, ranks among
-// survivors are the global ranks for the winners. Every count reads LDS at one address
-// for all lanes (broadcast), 16 reads in flight, rather than a chain of readlanes.
-// cand: kPrunedScratch keys of LDS private to this wave.
-constexpr int kPrunedMaxM = 16;
-constexpr int kPrunedScratch = 64 + kPrunedMaxM * (kPrunedMaxM + 1) / 2 + 16 + 64;
+// Top 16 of up to 64 sorted lists with a bitonic merge network held in registers (one
+// wave, all lanes active). Lane l reads element l % 16 of lists 4t + l / 16, t < 16: 16
+// lists of a register, one per 16-lane row, every list best first and zero padded to 16
+// keys. Two sorted lists A and B of 16 merge into their top 16 as max(A[i], B[15 - i]),
+// which is bitonic, followed by a half-cleaner (bitonic_clean16): registers merge
+// pairwise in the same lane (B mirrored within its row), then the four rows of the last
+// register merge with their mirrored neighbours (lane ^ 31, then lane ^ 63). Every row
+// ends with the same 16 keys; lane i < 16 returns the i-th largest, and for m <= 16 the
+// first m are the m largest of the union (the merge of vLLM PR #57832, Solution, with a
+// network in place of repeated extraction). The lists may have been written by other
+// workgroups on other XCDs, so they are read with agent-scope atomic loads
+// (device-coherent), all in flight at once.
+constexpr int kNetworkMaxM = 16;
 
-// Number of keys among a[0 .. n) (LDS, read by every lane at the same address, so the
-// reads broadcast) that are larger than x; 16 reads in flight per step. a must hold at
-// least round_up(n, 16) readable keys.
-__device__ __forceinline__ int count_larger_lds(const uint64_t* a, int n, uint64_t x) {
-  int r = 0;
-  for (int j0 = 0; j0 < n; j0 += 16) {
-    uint64_t v[16];
+__device__ __forceinline__ uint64_t merge_top16(const uint64_t* __restrict__ lists, size_t list_stride,
+                                                int ns, int Lk, int lane) {
+  const int i = lane & 15, row = lane >> 4;
+  const int R = (ns + 3) >> 2;  // registers that hold a list
+  uint64_t r[16];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) v[u] = a[j0 + u];
-#pragma unroll
-    for (int u = 0; u < 16; ++u) r += (j0 + u < n && v[u] > x) ? 1 : 0;
+  for (int t = 0; t < 16; ++t) {
+    const int sp = 4 * t + row;
+    r[t] = (t < R && sp < ns && i < Lk)
+               ? __hip_atomic_load(lists + sp * list_stride + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+               : 0;
   }
-  return r;
-}
-
-// Exclusive prefix sum over the wave of c in [0, 2^BITS), without LDS: one ballot per bit.
-template <int BITS = 5>
-__device__ __forceinline__ int wave_prefix_small(int c, int lane) {
-  int off = 0;
 #pragma unroll
-  for (int bit = 0; bit < BITS; ++bit) {
-    const uint64_t mask = __ballot((c >> bit) & 1);
-    const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
-                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-    off += (int)below << bit;
-  }
-  (void)lane;
-  return off;
-}
-
-__device__ __forceinline__ int wave_sum_small(int c) {
-  int total = 0;
+  for (int half = 8; half >= 1; half >>= 1) {
+    if (R > half) {  // otherwise registers half .. 2 half - 1 hold no list
 #pragma unroll
-  for (int bit = 0; bit < 5; ++bit) total += __popcll(__ballot((c >> bit) & 1)) << bit;
-  return total;
-}
-
-__device__ __forceinline__ uint64_t merge_pruned(const uint64_t* lk, int ns, int Lk, int stride, int m,
-                                                 int lane, uint64_t* cand) {
-  // Heads into a dense array, then every lane counts the heads above its own.
-  uint64_t* heads = cand;  // kPrunedHeads keys, reused below
-  const uint64_t head = lane < ns ? lk[lane * stride] : 0;
-  heads[lane] = head;
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  const int r = count_larger_lds(heads, ns, head);
-  const uint64_t at_m = __ballot(lane < ns && head != 0 && r == m - 1);
-  const uint64_t t0 = at_m ? readlane_u64(head, __builtin_ctzll(at_m)) : 1;  // fewer than m lists: no cut
-  // This lane's survivors: a prefix of its list (at most kPrunedMaxM keys, read at once).
-  const int lim = (lane < ns && head != 0 && r < m) ? min(Lk, m - r) : 0;
-  // Read kPrunedMaxM keys from the start of this lane's list whatever lim is: they lie in
-  // the lane's staged row group or the next one (stride >= 4 Lk + 1 keys, rows up to S),
-  // so they are in bounds, and the count below masks the ones past lim.
-  const uint64_t* mylist = lk + (lane < ns ? lane : 0) * stride;
-  uint64_t v[kPrunedMaxM];
-  int c = 0;
-#pragma unroll
-  for (int i = 0; i < kPrunedMaxM; ++i) {
-    v[i] = mylist[i];
-    c += (i < lim && v[i] >= t0) ? 1 : 0;
-  }
-  const int off = wave_prefix_small(c, lane);
-  const int nc = __builtin_amdgcn_readfirstlane(wave_sum_small(c));
-  uint64_t* sv = cand + 64;                      // survivors, after the heads
-  uint64_t* sink = cand + kPrunedScratch - 64;   // one discard slot per lane
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // heads read before sv overwrites
-#pragma unroll
-  for (int i = 0; i < kPrunedMaxM; ++i) *(i < c ? sv + off + i : sink + lane) = v[i];
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  // Rank each survivor by counting the survivors above it; winners land at their rank.
-  uint64_t* winners = cand;  // the heads are no longer needed
-  if (nc <= 64) {  // the usual case: one survivor per lane
-    const uint64_t x = lane < nc ? sv[lane] : 0;
-    const int rank = count_larger_lds(sv, nc, x);
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    if (lane < nc && rank < m) winners[rank] = x;
-  } else {
-    uint64_t x[3];
-#pragma unroll
-    for (int t = 0; t < 3; ++t) x[t] = lane + 64 * t < nc ? sv[lane + 64 * t] : 0;
-    int rank[3] = {0, 0, 0};
-    for (int j0 = 0; j0 < nc; j0 += 16) {
-      uint64_t w[16];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) w[u] = sv[j0 + u];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const bool in = j0 + u < nc;
-#pragma unroll
-        for (int t = 0; t < 3; ++t) rank[t] += (in && w[u] > x[t]) ? 1 : 0;
-      }
+      for (int t = 0; t < half; ++t) r[t] = bitonic_clean16(umax64(r[t], partner_u64<15>(r[t + half])), lane);
     }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-#pragma unroll
-    for (int t = 0; t < 3; ++t)
-      if (lane + 64 * t < nc && rank[t] < m) winners[rank[t]] = x[t];
   }
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  return lane < m ? winners[lane] : 0;
+  uint64_t x = r[0];
+  x = bitonic_clean16(umax64(x, partner_u64<31>(x)), lane);
+  x = bitonic_clean16(umax64(x, partner_u64<63>(x)), lane);
+  return x;
 }
 
 __device__ __forceinline__ void write_selection(uint64_t mine, int m, int topk, int lane,
@@ -489,23 +466,21 @@ __device__ __forceinline__ void write_selection(uint64_t mine, int m, int topk, 
 __device__ __forceinline__ void emit_pages(int id, bool valid, int topk, int lane,
                                            const int32_t* __restrict__ btrow, int L,
                                            int32_t* __restrict__ pages, int32_t* __restrict__ tokens) {
-  // Slot of a valid lane: the valid lanes with a smaller (id, lane) before it, so repeated
-  // ids keep one slot each. Invalid lanes below topk fill the slots after the valid ones.
+  // Sorted descending, ~((id << 6) | lane) puts the valid lanes first in ascending
+  // (id, lane) order (repeated ids keep one slot each) and the invalid ones (0) after:
+  // slot i takes the i-th sorted entry.
+  valid = valid && id >= 0 && id < (L + kBlock - 1) / kBlock;
   const uint64_t ord = valid ? ~(((uint64_t)(uint32_t)id << 6) | (uint64_t)lane) : 0;
-  const int pos = count_larger(ord, topk);
-  const uint64_t vmask = __ballot(valid);
-  const int n = __popcll(vmask);
-  const int valid_below = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(vmask >> 32),
-                                                         __builtin_amdgcn_mbcnt_lo((uint32_t)vmask, 0u));
-  const int slot = valid ? pos : n + (lane - valid_below);
+  const uint64_t mine = sort64_desc(ord, lane);
+  const int n = __popcll(__ballot(valid));
   if (lane < topk) {
     int4 lo = make_int4(-1, -1, -1, -1), hi = lo;
-    if (valid) {
-      const uint32_t p = (uint32_t)btrow[id] * 8u;
+    if (lane < n && mine != 0) {
+      const uint32_t p = (uint32_t)btrow[(int)(uint32_t)(~mine >> 6)] * 8u;
       lo = make_int4((int)p, (int)(p + 1), (int)(p + 2), (int)(p + 3));
       hi = make_int4((int)(p + 4), (int)(p + 5), (int)(p + 6), (int)(p + 7));
     }
-    int4* dst = reinterpret_cast<int4*>(pages + (size_t)slot * 8);
+    int4* dst = reinterpret_cast<int4*>(pages + (size_t)lane * 8);
     dst[0] = lo;
     dst[1] = hi;
   }
@@ -573,6 +548,20 @@ constexpr int kDeviceMaxSplits = 64;   // splits per row (the fused merge's fan-
 constexpr int64_t kDeviceMinBlocks = 8192;
 
 // Sum over the wave of x in [0, 2^BITS), without LDS: one ballot per bit.
+// Exclusive prefix sum over the wave of c in [0, 2^BITS), without LDS: one ballot per bit.
+template <int BITS>
+__device__ __forceinline__ int wave_prefix_small(int c) {
+  int off = 0;
+#pragma unroll
+  for (int bit = 0; bit < BITS; ++bit) {
+    const uint64_t mask = __ballot((c >> bit) & 1);
+    const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+    off += (int)below << bit;
+  }
+  return off;
+}
+
 template <int BITS>
 __device__ __forceinline__ int wave_sum_bits(int x) {
   int total = 0;
@@ -617,7 +606,7 @@ __device__ __forceinline__ DevicePlan device_plan(const int32_t* lens, int batch
     const int r = r0 + lane;
     const int nb = r0 == 0 ? nb0 : blocks(r);
     const int cnt = r < batch ? max(1, (nb + C - 1) / C) : 0;
-    const int first = base + wave_prefix_small<7>(cnt, lane);
+    const int first = base + wave_prefix_small<7>(cnt);
     const uint64_t hit = __ballot(r < batch && g >= first && g < first + cnt);
     if (hit) {
       const int l = __builtin_ctzll(hit);
@@ -713,8 +702,8 @@ __global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
   }
   __syncthreads();
 
-  // Wave h ranks the split's keys of head h: rank = number of larger keys (keys are
-  // distinct), so the keys of rank < Lk land best first; the rest of the list is zero.
+  // Wave h sorts the split's keys of head h (one per lane, 0 past the split's blocks) and
+  // keeps the first Lk: the split's list, best first, zero padded.
   const int n = j1 - j0;
   const int h = wave;
   uint64_t key = 0;
@@ -722,12 +711,11 @@ __global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
     const int jj = j0 + lane;
     key = make_key(sc[lane][h], jj, jj < a.n_init || jj >= nb - a.n_local);
   }
-  const int rank = count_larger(key, n);  // lanes >= n hold key 0
+  key = sort64_desc(key, lane);
   // Agent-scope atomic stores: written through to the device-coherent level, so the
   // row's last workgroup can read them from any XCD without an L2 writeback.
   uint64_t* out = a.keys + ((size_t)(b * a.S + s) * kHeads + h) * Lk;
-  if (lane < n && rank < Lk) __hip_atomic_store(out + rank, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (lane >= n && lane < Lk) __hip_atomic_store(out + lane, uint64_t(0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (lane < Lk) __hip_atomic_store(out + lane, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // Publish this workgroup's lists and count it in. Every wave waits until its list
   // stores have completed (reached the device-coherent level) before the barrier, so the
@@ -748,20 +736,20 @@ __global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
   if (threadIdx.x == 0) __hip_atomic_store(row_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (MODE != kFused) return;
 
-  // Row b's lists are one contiguous range [s][h][i] of the workspace. In LDS each
-  // workgroup's four lists get one pad key after them, so that lanes reading list s
-  // (stride 4 Lk + 1 keys) fall on different banks.
+  // Row b's lists are one contiguous range [s][h][i] of the workspace. Wave h merges
+  // head h's lists straight from it with the network; otherwise the lists are staged in
+  // LDS, each workgroup's four lists with one pad key after them so that lanes reading
+  // list s (stride 4 Lk + 1 keys) fall on different banks.
   const uint64_t* row_keys = a.keys + (size_t)b * a.S * kHeads * Lk;
-  const int row_len = kHeads * Lk, stride = row_len + 1;
-  stage_keys(row_keys, lk, ns * row_len, threadIdx.x, kThreads, [](int e) { return e; },
-             [row_len](int e) { return e + e / row_len; });
-  __syncthreads();
   const int m = min(a.topk, nb);
   uint64_t mine;
-  if (ns <= 64 && a.topk <= kPrunedMaxM) {
-    uint64_t* scratch = lk + (size_t)a.S * stride + h * kPrunedScratch;
-    mine = merge_pruned(lk + h * Lk, ns, Lk, stride, m, lane, scratch);
+  if (ns <= 64 && a.topk <= kNetworkMaxM) {
+    mine = merge_top16(row_keys + h * Lk, (size_t)kHeads * Lk, ns, Lk, lane);
   } else {
+    const int row_len = kHeads * Lk, stride = row_len + 1;
+    stage_keys(row_keys, lk, ns * row_len, threadIdx.x, kThreads, [](int e) { return e; },
+               [row_len](int e) { return e + e / row_len; });
+    __syncthreads();
     mine = merge_rounds(lk + h * Lk, ns, Lk, stride, m, lane);
   }
   const size_t o = ((size_t)b * kHeads + h) * a.topk;
@@ -787,12 +775,13 @@ struct MergeArgs {
   int32_t* out_tokens;
 };
 
-size_t merge_lds_bytes(int S, int Lk) {
-  return ((size_t)S * (Lk + 1) + 16 + kPrunedScratch) * sizeof(uint64_t);
+// LDS for the lists when merge_rounds runs (more than 64 splits or topk above 16).
+size_t merge_lds_bytes(int S, int Lk, int topk) {
+  return S <= 64 && topk <= kNetworkMaxM ? 0 : (size_t)S * (Lk + 1) * sizeof(uint64_t);
 }
 
 __global__ __launch_bounds__(64) void merge_kernel(MergeArgs a) {
-  extern __shared__ uint64_t lk[];  // [ns][Lk + 1] lists, 16 keys of slack, pruned scratch
+  extern __shared__ uint64_t lk[];  // merge_rounds: [ns][Lk + 1] lists
   const int task = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
   const int p = task >> 2;
   const int L = row_tokens(a.lens, b, a.W);
@@ -802,15 +791,15 @@ __global__ __launch_bounds__(64) void merge_kernel(MergeArgs a) {
   const int ns = (nb + a.C - 1) / a.C;
   const int Lk = a.Lk, stride = Lk + 1, QH = a.Q * kHeads;
   const uint64_t* src = a.keys + ((size_t)b * a.S * QH + task) * Lk;
-  stage_keys(src, lk, ns * Lk, lane, 64, [Lk, QH](int e) { return (e / Lk) * QH * Lk + e % Lk; },
-             [Lk, stride](int e) { return (e / Lk) * stride + e % Lk; });
-  for (int e = lane; e < 16; e += 64) lk[ns * stride + e] = 0;
-  __syncthreads();
   uint64_t mine;
-  if (ns <= 64 && a.topk <= kPrunedMaxM)
-    mine = merge_pruned(lk, ns, Lk, stride, m, lane, lk + (size_t)a.S * stride + 16);
-  else
+  if (ns <= 64 && a.topk <= kNetworkMaxM) {
+    mine = merge_top16(src, (size_t)QH * Lk, ns, Lk, lane);
+  } else {
+    stage_keys(src, lk, ns * Lk, lane, 64, [Lk, QH](int e) { return (e / Lk) * QH * Lk + e % Lk; },
+               [Lk, stride](int e) { return (e / Lk) * stride + e % Lk; });
+    __syncthreads();
     mine = merge_rounds(lk, ns, Lk, stride, m, lane);
+  }
   const size_t o = ((size_t)b * QH + task) * a.topk;
   write_selection(mine, m, a.topk, lane, a.out_ids + o, a.out_scores + o);
   if (a.out_pages != nullptr)
@@ -1093,19 +1082,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   if (MODE == kScores) return;
   __syncthreads();
 
-  // Wave h ranks head h of every position. A block past position p's end has no key (0).
+  // Wave h sorts head h's keys of every position and keeps the first Lk. A block past
+  // position p's end has no key (0).
   const int n = j1 - j0;
   const int h = wave;
   for (int p = 0; p < a.Q; ++p) {
     const int nbp = (causal_len(L, a.Q, p) + kBlock - 1) / kBlock;
     const int jj = j0 + lane;
     const bool real = lane < n && jj < nbp;
-    const uint64_t key = real ? make_key(sc[lane][4 * p + h], jj, jj < a.n_init || jj >= nbp - a.n_local) : 0;
-    const int rank = count_larger(key, n);
-    const int cnt = __popcll(__ballot(real));
+    uint64_t key = real ? make_key(sc[lane][4 * p + h], jj, jj < a.n_init || jj >= nbp - a.n_local) : 0;
+    key = sort64_desc(key, lane);
     uint64_t* out = a.keys + ((size_t)(b * a.S + s) * a.Q * kHeads + 4 * p + h) * a.Lk;
-    if (real && rank < a.Lk) out[rank] = key;
-    if (lane >= cnt && lane < a.Lk) out[lane] = 0;
+    if (lane < a.Lk) out[lane] = key;
   }
 }
 
@@ -1166,7 +1154,7 @@ int32_t make_plan(int32_t batch, int32_t W, int32_t topk, int32_t num_splits, Pl
 int32_t make_decode_plan(int32_t batch, int32_t W, int32_t topk, int32_t num_splits, Plan* p) {
   int32_t rc = make_plan(batch, W, topk, num_splits, p);
   if (rc != MSA_OK) return rc;
-  if (num_splits == 0 && W > 0 && W <= kDeviceMaxSplits * kMaxSplitBlocks && topk <= kPrunedMaxM &&
+  if (num_splits == 0 && W > 0 && W <= kDeviceMaxSplits * kMaxSplitBlocks && topk <= kNetworkMaxM &&
       (int64_t)batch * W >= kDeviceMinBlocks) {
     const int64_t per_row = ceil_div(W, 4);
     const int64_t need = std::max<int64_t>(kDeviceTarget, ceil_div((int64_t)batch * W, kMaxSplitBlocks)) + batch;
@@ -1185,8 +1173,9 @@ size_t keys_offset(int32_t batch) {
   return kHeaderBytes + (size_t)batch * kCounterStride * sizeof(uint32_t);
 }
 
-size_t fused_lds_bytes(const Plan& p) {
-  return ((size_t)p.S * (kHeads * p.Lk + 1) + kHeads * kPrunedScratch) * sizeof(uint64_t);
+// LDS for the fused merge when merge_rounds runs (more than 64 splits or topk above 16).
+size_t fused_lds_bytes(const Plan& p, int topk) {
+  return p.S <= 64 && topk <= kNetworkMaxM ? 0 : (size_t)p.S * (kHeads * p.Lk + 1) * sizeof(uint64_t);
 }
 // (For the device plan p.S and p.Lk bound the per-call values: S splits, Lk <= topk.)
 
@@ -1306,7 +1295,7 @@ int32_t launch_merge(const uint64_t* keys, const int32_t* lens, int32_t W, int32
   a.bt_stride = bt_stride;
   a.out_pages = out_pages;
   a.out_tokens = out_tokens;
-  hipLaunchKernelGGL(merge_kernel, dim3(Q * kHeads, batch), dim3(64), merge_lds_bytes(p.S, p.Lk), st, a);
+  hipLaunchKernelGGL(merge_kernel, dim3(Q * kHeads, batch), dim3(64), merge_lds_bytes(p.S, p.Lk, topk), st, a);
   return hipGetLastError() == hipSuccess ? MSA_OK : MSA_ERR_HIP;
 }
 
@@ -1436,7 +1425,7 @@ int32_t decode_impl(const void* q, const void* k_cache, const int32_t* block_tab
     a.out_scores = out_scores;
     a.out_pages = out_pages;
     a.out_tokens = out_tokens;
-    return launch_split<kFused>(a, batch, engine, fused_lds_bytes(p), st, p.device ? p.grid : 0);
+    return launch_split<kFused>(a, batch, engine, fused_lds_bytes(p, topk), st, p.device ? p.grid : 0);
   }
   if ((rc = launch_split<kSplit>(a, batch, engine, 0, st)) != MSA_OK) return rc;
   return merge_impl(seq_lens, batch, W, topk, out_ids, out_scores, workspace, workspace_bytes,
