@@ -160,21 +160,29 @@ __device__ __forceinline__ uint64_t bitonic_clean16(uint64_t x, int lane) {
   return bitonic_step<1, 1>(x, lane);
 }
 
-// Sorts the wave's 64 keys: lane r ends with the r-th largest.
-__device__ __forceinline__ uint64_t sort64_desc(uint64_t x, int lane) {
-  x = bitonic_step<1, 1>(x, lane);
-  x = bitonic_step<3, 2>(x, lane);
-  x = bitonic_step<1, 1>(x, lane);
-  x = bitonic_step<7, 4>(x, lane);
-  x = bitonic_step<2, 2>(x, lane);
-  x = bitonic_step<1, 1>(x, lane);
-  x = bitonic_step<15, 8>(x, lane);
-  x = bitonic_step<4, 4>(x, lane);
-  x = bitonic_step<2, 2>(x, lane);
-  x = bitonic_step<1, 1>(x, lane);
-  x = bitonic_clean16(bitonic_step<31, 16>(x, lane), lane);
-  x = bitonic_step<63, 32>(x, lane);
-  return bitonic_clean16(bitonic_step<16, 16>(x, lane), lane);
+// Stage k of the network: sorts every block of k lanes whose halves are sorted.
+template <int K>
+__device__ __forceinline__ uint64_t bitonic_stage(uint64_t x, int lane) {
+  x = bitonic_step<K - 1, K / 2>(x, lane);
+  if constexpr (K >= 64) x = bitonic_step<16, 16>(x, lane);
+  if constexpr (K >= 32) x = bitonic_step<8, 8>(x, lane);
+  if constexpr (K >= 16) x = bitonic_step<4, 4>(x, lane);
+  if constexpr (K >= 8) x = bitonic_step<2, 2>(x, lane);
+  if constexpr (K >= 4) x = bitonic_step<1, 1>(x, lane);
+  return x;
+}
+
+// Sorts lanes 0 .. n-1 of the wave (n uniform, at most 64; the other lanes must hold 0,
+// which stays behind every key): lane r < n ends with the r-th largest. Stages stop at the
+// first block size k >= n, so n candidates take 1 + 2 + .. + log2(k) steps.
+__device__ __forceinline__ uint64_t sort_desc_first(uint64_t x, int lane, int n) {
+  if (n > 1) x = bitonic_stage<2>(x, lane);
+  if (n > 2) x = bitonic_stage<4>(x, lane);
+  if (n > 4) x = bitonic_stage<8>(x, lane);
+  if (n > 8) x = bitonic_stage<16>(x, lane);
+  if (n > 16) x = bitonic_stage<32>(x, lane);
+  if (n > 32) x = bitonic_stage<64>(x, lane);
+  return x;
 }
 
 // Largest value over the 64 lanes of a wave (all lanes active).
@@ -408,36 +416,52 @@ __device__ __forceinline__ uint64_t merge_rounds(const uint64_t* lk, int ns, int
 }
 
 // Top 16 of up to 64 sorted lists with a bitonic merge network held in registers (one
-// wave, all lanes active). Lane l reads element l % 16 of lists 4t + l / 16, t < 16: 16
-// lists of a register, one per 16-lane row, every list best first and zero padded to 16
-// keys. Two sorted lists A and B of 16 merge into their top 16 as max(A[i], B[15 - i]),
-// which is bitonic, followed by a half-cleaner (bitonic_clean16): registers merge
-// pairwise in the same lane (B mirrored within its row), then the four rows of the last
-// register merge with their mirrored neighbours (lane ^ 31, then lane ^ 63). Every row
-// ends with the same 16 keys; lane i < 16 returns the i-th largest, and for m <= 16 the
-// first m are the m largest of the union (the merge of vLLM PR #57832, Solution, with a
-// network in place of repeated extraction). The lists may have been written by other
-// workgroups on other XCDs, so they are read with agent-scope atomic loads
-// (device-coherent), all in flight at once.
+// wave, all lanes active). Every list is best first with Lk <= 16 keys; rounded up to
+// Lk2 = 2^lg >= Lk (zero padded), 16 / Lk2 lists share a 16-lane row, so a register holds
+// 64 / Lk2 lists: lane l of register t reads element l % Lk2 of list
+// t * (64 / Lk2) + l / Lk2. Each row is first sorted from its runs of Lk2 into 16 (the
+// network's stages 2 Lk2 .. 16). Two sorted rows A and B of 16 merge into their top 16 as
+// max(A[i], B[15 - i]), which is bitonic, followed by a half-cleaner (bitonic_clean16):
+// registers merge pairwise in the same lane (B mirrored within its row; a register with
+// no partner is left as it is), then the four rows of the last register merge with their
+// mirrored neighbours (lane ^ 31, then lane ^ 63). Every row ends with the same 16 keys;
+// lane i < 16 returns the i-th largest, and for m <= 16 the first m are the m largest of
+// the union (the merge of vLLM PR #57832, Solution, with a network in place of repeated
+// extraction). The lists may have been written by other workgroups on other XCDs, so they
+// are read with agent-scope atomic loads (device-coherent), all in flight at once.
 constexpr int kNetworkMaxM = 16;
 
 __device__ __forceinline__ uint64_t merge_top16(const uint64_t* __restrict__ lists, size_t list_stride,
                                                 int ns, int Lk, int lane) {
-  const int i = lane & 15, row = lane >> 4;
-  const int R = (ns + 3) >> 2;  // registers that hold a list
+  const int lg = Lk <= 1 ? 0 : Lk <= 2 ? 1 : Lk <= 4 ? 2 : Lk <= 8 ? 3 : 4;
+  const int per_reg = 64 >> lg;
+  const int R = (ns + per_reg - 1) / per_reg;  // registers that hold a list
+  const int e = lane & ((1 << lg) - 1), sub = lane >> lg;
   uint64_t r[16];
 #pragma unroll
   for (int t = 0; t < 16; ++t) {
-    const int sp = 4 * t + row;
-    r[t] = (t < R && sp < ns && i < Lk)
-               ? __hip_atomic_load(lists + sp * list_stride + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+    const int sp = t * per_reg + sub;
+    r[t] = (t < R && sp < ns && e < Lk)
+               ? __hip_atomic_load(lists + sp * list_stride + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                : 0;
+  }
+  if (lg < 4) {  // several lists per row (then at most 8 registers): sort each row
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      if (t < R) {
+        if (lg < 1) r[t] = bitonic_stage<2>(r[t], lane);
+        if (lg < 2) r[t] = bitonic_stage<4>(r[t], lane);
+        if (lg < 3) r[t] = bitonic_stage<8>(r[t], lane);
+        r[t] = bitonic_stage<16>(r[t], lane);
+      }
+    }
   }
 #pragma unroll
   for (int half = 8; half >= 1; half >>= 1) {
-    if (R > half) {  // otherwise registers half .. 2 half - 1 hold no list
+    if (R > half) {
 #pragma unroll
-      for (int t = 0; t < half; ++t) r[t] = bitonic_clean16(umax64(r[t], partner_u64<15>(r[t + half])), lane);
+      for (int t = 0; t < half; ++t)
+        if (t + half < R) r[t] = bitonic_clean16(umax64(r[t], partner_u64<15>(r[t + half])), lane);
     }
   }
   uint64_t x = r[0];
@@ -471,7 +495,7 @@ __device__ __forceinline__ void emit_pages(int id, bool valid, int topk, int lan
   // slot i takes the i-th sorted entry.
   valid = valid && id >= 0 && id < (L + kBlock - 1) / kBlock;
   const uint64_t ord = valid ? ~(((uint64_t)(uint32_t)id << 6) | (uint64_t)lane) : 0;
-  const uint64_t mine = sort64_desc(ord, lane);
+  const uint64_t mine = sort_desc_first(ord, lane, topk);
   const int n = __popcll(__ballot(valid));
   if (lane < topk) {
     int4 lo = make_int4(-1, -1, -1, -1), hi = lo;
@@ -711,7 +735,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
     const int jj = j0 + lane;
     key = make_key(sc[lane][h], jj, jj < a.n_init || jj >= nb - a.n_local);
   }
-  key = sort64_desc(key, lane);
+  key = sort_desc_first(key, lane, n);
   // Agent-scope atomic stores: written through to the device-coherent level, so the
   // row's last workgroup can read them from any XCD without an L2 writeback.
   uint64_t* out = a.keys + ((size_t)(b * a.S + s) * kHeads + h) * Lk;
@@ -1091,7 +1115,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     const int jj = j0 + lane;
     const bool real = lane < n && jj < nbp;
     uint64_t key = real ? make_key(sc[lane][4 * p + h], jj, jj < a.n_init || jj >= nbp - a.n_local) : 0;
-    key = sort64_desc(key, lane);
+    key = sort_desc_first(key, lane, n);
     uint64_t* out = a.keys + ((size_t)(b * a.S + s) * a.Q * kHeads + 4 * p + h) * a.Lk;
     if (lane < a.Lk) out[lane] = key;
   }
