@@ -641,10 +641,10 @@ __device__ __forceinline__ DevicePlan device_plan(const int32_t* lens, int batch
   return DevicePlan{C, 0, 0, false};
 }
 
+// Block j of the row, held in cache page `page`.
 template <int ENGINE>
-__device__ __forceinline__ void score_page(const SplitArgs& a, const int32_t* btrow, int j, int L,
-                                           int lane, const void* qr, float (&m)[kHeads]) {
-  const int page = btrow[j];
+__device__ __forceinline__ void score_page(const SplitArgs& a, int page, int j, int L, int lane,
+                                           const void* qr, float (&m)[kHeads]) {
   const int valid = min(kBlock, L - j * kBlock);
   if (page < 0 || (int64_t)page >= a.num_pages) {
 #pragma unroll
@@ -674,11 +674,18 @@ __global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
     C = dp.C;
   }
   const int Lk = min(a.topk, C);
+  // The wave's first page number and the row's query are read together with the row
+  // length rather than after it (the table row has W entries, so the read is in bounds
+  // whatever the length); each page number after it is read while the page before it is
+  // being scored.
+  const int32_t* btrow = a.bt + (size_t)b * a.bt_stride;
+  const int j_first = s * C + wave;
+  int page = j_first < a.W ? btrow[j_first] : 0;
+  typename std::conditional<ENGINE == MSA_ENGINE_MFMA, QMfma, QValu>::type qr;
+  if constexpr (ENGINE == MSA_ENGINE_MFMA) load_q_mfma(a.q, b, lane, qr);
+  else load_q_valu(a.q, b, lane, qr);
   const int L = row_tokens(a.lens, b, a.W);
   const int nb = (L + kBlock - 1) / kBlock;
-
-  typename std::conditional<ENGINE == MSA_ENGINE_MFMA, QMfma, QValu>::type qr;
-  const int32_t* btrow = a.bt + (size_t)b * a.bt_stride;
 
   if (MODE == kScores) {  // block scores out; -inf at and past the row's end
     const int j0 = s * C, j1 = min(j0 + C, nb);
@@ -688,12 +695,12 @@ __global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
       a.scores[((size_t)b * kHeads + h) * a.W + j] = -__builtin_inff();
     }
     if (j0 >= nb) return;
-    if constexpr (ENGINE == MSA_ENGINE_MFMA) load_q_mfma(a.q, b, lane, qr);
-    else load_q_valu(a.q, b, lane, qr);
     for (int j = j0 + wave; j < j1; j += kWaves) {
+      const int next = j + kWaves < j1 ? btrow[j + kWaves] : 0;
       float m[kHeads];
-      score_page<ENGINE>(a, btrow, j, L, lane, &qr, m);
+      score_page<ENGINE>(a, page, j, L, lane, &qr, m);
       if (lane < kHeads) a.scores[((size_t)b * kHeads + lane) * a.W + j] = m[lane];
+      page = next;
     }
     return;
   }
@@ -717,12 +724,12 @@ __global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
     }
     return;
   }
-  if constexpr (ENGINE == MSA_ENGINE_MFMA) load_q_mfma(a.q, b, lane, qr);
-  else load_q_valu(a.q, b, lane, qr);
   for (int j = j0 + wave; j < j1; j += kWaves) {
+    const int next = j + kWaves < j1 ? btrow[j + kWaves] : 0;
     float m[kHeads];
-    score_page<ENGINE>(a, btrow, j, L, lane, &qr, m);
+    score_page<ENGINE>(a, page, j, L, lane, &qr, m);
     if (lane < kHeads) sc[j - j0][lane] = m[lane];
+    page = next;
   }
   __syncthreads();
 
