@@ -571,7 +571,6 @@ constexpr int kDeviceMaxSplits = 64;   // splits per row (the fused merge's fan-
 // row lengths read before any page) costs ~1 us, which only pays where a row can be long.
 constexpr int64_t kDeviceMinBlocks = 8192;
 
-// Sum over the wave of x in [0, 2^BITS), without LDS: one ballot per bit.
 // Exclusive prefix sum over the wave of c in [0, 2^BITS), without LDS: one ballot per bit.
 template <int BITS>
 __device__ __forceinline__ int wave_prefix_small(int c) {
@@ -586,6 +585,7 @@ __device__ __forceinline__ int wave_prefix_small(int c) {
   return off;
 }
 
+// Sum over the wave of x in [0, 2^BITS), without LDS: one ballot per bit.
 template <int BITS>
 __device__ __forceinline__ int wave_sum_bits(int x) {
   int total = 0;
@@ -986,36 +986,49 @@ struct VerifyArgs {
   uint64_t* keys;       // [batch][S][Q*4][Lk]
   uint32_t* err;        // device error word (may be null)
   float* scores;        // [batch][Q][4][W] (block-score mode)
+  uint32_t* counters;   // fused mode: [batch][kCounterStride], zero between calls
+  int32_t* out_ids;     // fused mode (Q = 1): [batch][4][topk]
+  float* out_scores;
 };
 
 
 // Grid (S, batch), 4 waves; split s of row b owns blocks [s*C, min((s+1)*C, nb)), nb the
 // last position's block count. kScores: block scores out. kSplit: per (position, head) the
-// split's top Lk keys, best first, zero padded.
+// split's top Lk keys, best first, zero padded. kFused (one position, topk <= 16, lists that
+// merge_top16 holds in at most 4 registers): kSplit, then the row's last workgroup merges
+// the lists as split_kernel does.
 template <int MODE, bool FP8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void verify_kernel(VerifyArgs a) {
   using G = KvGeom<FP8>;
   __shared__ float sc[kMaxSplitBlocks][16];
   __shared__ uint4 stage[kWaves * kChunkSlots];  // one 8 KiB chunk region per wave
-  const int s = blockIdx.x;
-  const int b = blockIdx.y;
+  __shared__ int s_last;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4;
+  const int s = blockIdx.x, b = blockIdx.y, C = a.C, Lk = a.Lk;
   const int L = row_tokens(a.lens, b, a.W);
   const int nb = (L + kBlock - 1) / kBlock;
   const int Lg = g < a.Q ? causal_len(L, a.Q, g) : 0;
   const int32_t* btrow = a.bt + (size_t)b * a.bt_stride;
-  const int j0 = s * a.C, j1 = min(j0 + a.C, nb);
+  const int j0 = s * C, j1 = min(j0 + C, nb);
 
   if (MODE == kScores) {  // blocks past the row's end: -inf for every position
-    const int e0 = max(j0, nb), e1 = min(j0 + a.C, a.W), ne = e1 - e0;
+    const int e0 = max(j0, nb), e1 = min(j0 + C, a.W), ne = e1 - e0;
     for (int idx = threadIdx.x; idx < ne * a.Q * kHeads; idx += kThreads) {
       const int r = idx / ne, j = e0 + idx % ne;
       a.scores[((size_t)b * a.Q * kHeads + r) * a.W + j] = -__builtin_inff();
     }
   }
-  if (j0 >= nb) return;
+  if (j0 >= nb) {
+    // An empty row has no workgroup to merge it: its first workgroup writes the padding.
+    if (MODE == kFused && nb == 0 && s == 0 && threadIdx.x < kHeads * a.topk) {
+      const size_t o = (size_t)b * kHeads * a.topk + threadIdx.x;
+      a.out_ids[o] = -1;
+      a.out_scores[o] = -__builtin_inff();
+    }
+    return;
+  }
   QMulti qr;
   load_q_multi(a.q, b, a.Q, lane, qr);
   uint4* region = stage + wave * kChunkSlots;
@@ -1123,9 +1136,33 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     const bool real = lane < n && jj < nbp;
     uint64_t key = real ? make_key(sc[lane][4 * p + h], jj, jj < a.n_init || jj >= nbp - a.n_local) : 0;
     key = sort_desc_first(key, lane, n);
-    uint64_t* out = a.keys + ((size_t)(b * a.S + s) * a.Q * kHeads + 4 * p + h) * a.Lk;
-    if (lane < a.Lk) out[lane] = key;
+    uint64_t* out = a.keys + ((size_t)(b * a.S + s) * a.Q * kHeads + 4 * p + h) * Lk;
+    if (MODE == kFused) {
+      if (lane < Lk) __hip_atomic_store(out + lane, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      if (lane < Lk) out[lane] = key;
+    }
   }
+  if (MODE != kFused) return;
+
+  // Publication and the last workgroup's merge, as in split_kernel (one position: wave h
+  // merges head h).
+  const int ns = (nb + C - 1) / C;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  uint32_t* row_done = a.counters + (size_t)b * kCounterStride;
+  if (threadIdx.x == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(row_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = prev == (uint32_t)(ns - 1);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  if (threadIdx.x == 0) __hip_atomic_store(row_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int msel = min(a.topk, nb);
+  const uint64_t mine = merge_top16(a.keys + ((size_t)b * a.S * kHeads + h) * Lk, (size_t)kHeads * Lk,
+                                    ns, Lk, lane);
+  const size_t o = ((size_t)b * kHeads + h) * a.topk;
+  write_selection(mine, msel, a.topk, lane, a.out_ids + o, a.out_scores + o);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1377,11 +1414,25 @@ VerifyArgs make_verify_args(const void* q, const void* k, const int32_t* bt, con
   char* w = static_cast<char*>(ws);
   a.err = w ? reinterpret_cast<uint32_t*>(w) : nullptr;
   a.keys = w ? reinterpret_cast<uint64_t*>(w + keys_offset(batch)) : nullptr;
+  a.counters = w ? reinterpret_cast<uint32_t*>(w + kHeaderBytes) : nullptr;
   a.scores = nullptr;
+  a.out_ids = nullptr;
+  a.out_scores = nullptr;
   return a;
 }
 
 bool valid_scale(float k_scale) { return k_scale > 0.0f && k_scale <= 3.402823466e38f; }
+
+// Whether the one-position pass merges in its own launch: when merge_top16 holds each head's
+// lists in at most 4 registers (S lists of Lk keys, 64 / Lk2 per register). With more, the
+// serial merge in the row's last workgroup measured slower than the merge kernel, which
+// runs every (row, head) at once (FP8 at batch 32 x 128K: 32 lists of 16, 89.8 vs 88.7 us).
+bool fuse_verify(const Plan& p, int topk) {
+  if (p.S > 64 || topk > kNetworkMaxM) return false;
+  int lk2 = 1;
+  while (lk2 < p.Lk) lk2 <<= 1;
+  return ceil_div(p.S, 64 / lk2) <= 4;
+}
 
 template <int MODE>
 void launch_verify(const VerifyArgs& a, bool fp8, int32_t batch, hipStream_t st) {
@@ -1407,8 +1458,14 @@ int32_t verify_decode_impl(const void* q, const void* k_cache, bool fp8, float k
   if (!out_ids || !out_scores || !aligned(out_ids, 4) || !aligned(out_scores, 4)) return MSA_ERR_INVALID_ARG;
   if (!workspace || !aligned(workspace, kAlign)) return MSA_ERR_INVALID_ARG;
   if (workspace_bytes < ws_bytes_multi(batch, qlen, p)) return MSA_ERR_WORKSPACE_TOO_SMALL;
-  const VerifyArgs a = make_verify_args(q, k_cache, block_table, seq_lens, W, bt_stride, num_pages, qlen,
-                                        p, topk, n_init, n_local, workspace, batch, k_scale);
+  VerifyArgs a = make_verify_args(q, k_cache, block_table, seq_lens, W, bt_stride, num_pages, qlen,
+                                  p, topk, n_init, n_local, workspace, batch, k_scale);
+  if (qlen == 1 && fuse_verify(p, topk)) {  // one position, few lists: merge in the same launch
+    a.out_ids = out_ids;
+    a.out_scores = out_scores;
+    launch_verify<kFused>(a, fp8, batch, st);
+    return hipGetLastError() == hipSuccess ? MSA_OK : MSA_ERR_HIP;
+  }
   launch_verify<kSplit>(a, fp8, batch, st);
   if (hipGetLastError() != hipSuccess) return MSA_ERR_HIP;
   return launch_merge(a.keys, seq_lens, W, qlen, p, topk, out_ids, out_scores, batch, st);

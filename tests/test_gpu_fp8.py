@@ -155,6 +155,31 @@ def test_fp8_edges_and_out_of_range_page(msa):
     assert np.all(np.isneginf(s[2, :, :, 1]))
 
 
+def test_fp8_single_position_workspace_reuse(msa):
+    # One position merges in the same launch through per-row counters in the workspace; they
+    # must be back at zero after every call, whatever the lengths and split counts.
+    inp = synth.fp8_case(308, [128 * 70] * 6, 70, 1, k_scale=0.5)
+    q, k, bt, lens = to_device_fp8(inp)
+    plans = [0, 3, 70, 2, 0]
+    ws = torch.zeros(max(msa.workspace_bytes_multi(6, 70, 1, 16, ns) for ns in plans),
+                     dtype=torch.uint8, device="cuda")
+    rng = np.random.default_rng(5)
+    for it, ns in enumerate(plans):
+        new_lens = rng.integers(0, 128 * 70 + 1, size=6).astype(np.int32)
+        new_lens[it % 6] = 0
+        lens.copy_(torch.from_numpy(new_lens))
+        ids, sc = msa.msa_indexer_decode_fp8(q, k, 0.5, bt, lens, num_splits=ns, workspace=ws)
+        s = msa.msa_indexer_block_scores_fp8(q, k, 0.5, bt, lens, num_splits=ns).cpu().numpy()
+        torch.cuda.synchronize()
+        assert np.all(ws[:256 + 6 * 256].view(torch.int32).cpu().numpy() == 0), it
+        cur = synth.Inputs("reuse", inp.q, inp.k_cache, inp.block_table, new_lens, k_scale=0.5)
+        gi, gs = oracle.select(s[:, 0].astype(np.float64), position_lens(cur, 0, 1), 16, 1, 2)
+        assert np.array_equal(ids.cpu().numpy()[:, 0], gi), it
+        _, _, ref = oracle.decode(cur)
+        check_selection_vs_oracle(ids.cpu().numpy()[:, 0], ref[:, 0], position_lens(cur, 0, 1),
+                                  16, 1, 2, tol=1e-3 * 4.0 * 0.5)
+
+
 @pytest.mark.slow
 @pytest.mark.timeout(600)
 def test_fp8_full_size(msa):

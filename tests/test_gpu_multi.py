@@ -172,14 +172,16 @@ def test_multi_full_size(msa):
     assert np.mean(differ) >= 0.9
 
 
-def test_multi_fused_workspace_reuse_and_graph_replay(msa):
-    # The fused verify pass counts each row's finished splits in the workspace and the last
-    # one resets the count: one workspace must serve changing lengths and split counts, and a
+@pytest.mark.parametrize("Q", [1, 4])
+def test_multi_workspace_reuse_and_graph_replay(msa, Q):
+    # With one position the pass merges in the same launch: each row's last split, found by
+    # counting finished splits in the workspace, merges and resets the count. One workspace
+    # must serve changing lengths (rows of length 0 included) and split counts, and a
     # captured graph must give the same result on every replay.
-    inp = synth.multi_case(210, [128 * 40] * 5, 40, 4)
+    inp = synth.multi_case(210, [128 * 40] * 5, 40, Q)
     q, k, bt, lens = to_device_multi(inp)
     plans = [0, 4, 13, 2, 40, 0]
-    ws = torch.zeros(max(msa.workspace_bytes_multi(5, 40, 4, 16, ns) for ns in plans),
+    ws = torch.zeros(max(msa.workspace_bytes_multi(5, 40, Q, 16, ns) for ns in plans),
                      dtype=torch.uint8, device="cuda")
     rng = np.random.default_rng(3)
     for it, ns in enumerate(plans):
@@ -191,12 +193,12 @@ def test_multi_fused_workspace_reuse_and_graph_replay(msa):
         assert np.all(ws[:256 + 5 * 256].view(torch.int32).cpu().numpy() == 0), it
         cur = synth.Inputs("reuse", inp.q, inp.k_cache, inp.block_table, new_lens)
         want_ids, _, ref = oracle.decode(cur)
-        for p in range(4):
+        for p in range(Q):
             check_selection_vs_oracle(ids.cpu().numpy()[:, p], ref[:, p], position_lens(cur, p),
                                       16, 1, 2)
     # graph capture, then replays with lengths changed on the device in between
-    ids = torch.empty((5, 4, 4, 16), dtype=torch.int32, device="cuda")
-    sc = torch.empty((5, 4, 4, 16), dtype=torch.float32, device="cuda")
+    ids = torch.empty((5, Q, 4, 16), dtype=torch.int32, device="cuda")
+    sc = torch.empty((5, Q, 4, 16), dtype=torch.float32, device="cuda")
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
