@@ -80,18 +80,10 @@ __device__ __forceinline__ float dpp_f32(float x) {
 
 constexpr int kQuadSwap1 = 0xB1;      // quad_perm [1,0,3,2]: partner lane ^ 1
 constexpr int kQuadSwap2 = 0x4E;      // quad_perm [2,3,0,1]: partner lane ^ 2
+constexpr int kQuadSwapMid = 0xD8;    // quad_perm [0,2,1,3]: lanes 1 and 2 of each quad swap
+constexpr int kRowRor4 = 0x124;       // row_ror:4 (keeps lane & 3)
 constexpr int kRowHalfMirror = 0x141; // lane i <-> 7-i within each 8 lanes
 constexpr int kRowMirror = 0x140;     // lane i <-> 15-i within each 16 lanes
-
-// Sum over the 16 lanes of each row; every lane of the row ends with the same value
-// (each step adds a pair in the same order on both partners).
-__device__ __forceinline__ float row_sum16(float x) {
-  x += dpp_f32<kQuadSwap1>(x);
-  x += dpp_f32<kQuadSwap2>(x);
-  x += dpp_f32<kRowHalfMirror>(x);
-  x += dpp_f32<kRowMirror>(x);
-  return x;
-}
 
 __device__ __forceinline__ float row_max16(float x) {
   x = fmaxf(x, dpp_f32<kQuadSwap1>(x));
@@ -222,8 +214,10 @@ __device__ __forceinline__ float key_score(uint64_t key) {
 
 // VALU engine. Load i of a wave covers bytes [1024 i, 1024 i + 1024) of the page: lane l
 // holds token 4i + l/16, dims 8(l%16) .. +7 (fully coalesced). Each lane forms partial dot
-// products of its 8 dims with bf16 dot2 instructions (fp32 accumulate), the 16 lanes of a
-// row are summed with DPP, and the running max is kept per row; rows merge at the end.
+// products of its 8 dims with bf16 dot2 instructions (fp32 accumulate) for the four heads,
+// the 16 lanes of a row reduce-scatter them (row_sum4_scatter) so that each lane ends with
+// the row's full sum for one head, and each lane keeps a running max of its head; rows
+// merge at the end.
 struct QValu {
   uint32_t d[kHeads][4];  // this lane's 8 dims of each head, as 4 bf16 pairs
 };
@@ -249,13 +243,29 @@ __device__ __forceinline__ float dot8(const uint4& k, const uint32_t (&qd)[4]) {
   return s;
 }
 
+// The four heads' sums over a 16-lane row, one head per lane: lane l ends with the row
+// sum of head 2 (l & 1) + ((l >> 1) & 1) (lanes 1 and 2 swapped against l & 3). Across
+// lane ^ 1, a lane keeps two heads and sends the other two; across lane ^ 2 it keeps one;
+// rotations of the row by 4 and 8 (which keep l & 3) add the four quads. 9 adds/selects
+// and 5 DPP moves instead of 16 DPP adds for four separate row sums.
+__device__ __forceinline__ float row_sum4_scatter(float p0, float p1, float p2, float p3, bool b0, bool b1) {
+  const float a0 = (b0 ? p2 : p0) + dpp_f32<kQuadSwap1>(b0 ? p0 : p2);
+  const float a1 = (b0 ? p3 : p1) + dpp_f32<kQuadSwap1>(b0 ? p1 : p3);
+  float x = (b1 ? a1 : a0) + dpp_f32<kQuadSwap2>(b1 ? a0 : a1);
+  x += dpp_f32<kRowRor4>(x);
+  x += dpp_f32<kRowRor8>(x);
+  return x;
+}
+
 // A page is scored in batches of 16 wave loads (16 KiB); the compiler schedules each
 // batch's loads ahead of its arithmetic.
 constexpr int kValuBatch = 16;
 
 template <bool FULL>
-__device__ __forceinline__ void valu_batch(const uint4* p, int i0, int nl, int valid, int row,
-                                           const QValu& qr, float (&m)[kHeads]) {
+__device__ __forceinline__ void valu_batch(const uint4* p, int i0, int nl, int valid, int lane,
+                                           const QValu& qr, float& m) {
+  const int row = lane >> 4;
+  const bool b0 = (lane & 1) != 0, b1 = (lane & 2) != 0;
   uint4 kv[kValuBatch];
 #pragma unroll
   for (int i = 0; i < kValuBatch; ++i)
@@ -263,32 +273,27 @@ __device__ __forceinline__ void valu_batch(const uint4* p, int i0, int nl, int v
 #pragma unroll
   for (int i = 0; i < kValuBatch; ++i) {
     const bool ok = FULL || 4 * (i0 + i) + row < valid;
-#pragma unroll
-    for (int h = 0; h < kHeads; ++h) {
-      const float sc = row_sum16(dot8(kv[i], qr.d[h]));
-      m[h] = ok ? fmaxf(m[h], sc) : m[h];
-    }
+    const float x = row_sum4_scatter(dot8(kv[i], qr.d[0]), dot8(kv[i], qr.d[1]), dot8(kv[i], qr.d[2]),
+                                     dot8(kv[i], qr.d[3]), b0, b1);
+    m = ok ? fmaxf(m, x) : m;
   }
 }
 
-__device__ __forceinline__ void score_block_valu(const uint16_t* __restrict__ page, int valid,
-                                                 const QValu& qr, int lane, float (&m)[kHeads]) {
+// The block maximum of head (lane & 3) in lanes 0..3 (and every lane with the same lane & 3).
+__device__ __forceinline__ float score_block_valu(const uint16_t* __restrict__ page, int valid,
+                                                  const QValu& qr, int lane) {
   const uint4* p = reinterpret_cast<const uint4*>(page) + lane;
-#pragma unroll
-  for (int h = 0; h < kHeads; ++h) m[h] = -__builtin_inff();
-  const int row = lane >> 4;
+  float m = -__builtin_inff();
   const int nl = (valid + 3) >> 2;  // wave loads that hold a valid token
   if (valid == kBlock) {
 #pragma unroll
-    for (int i0 = 0; i0 < 32; i0 += kValuBatch) valu_batch<true>(p, i0, nl, valid, row, qr, m);
+    for (int i0 = 0; i0 < 32; i0 += kValuBatch) valu_batch<true>(p, i0, nl, valid, lane, qr, m);
   } else {
-    for (int i0 = 0; i0 < nl; i0 += kValuBatch) valu_batch<false>(p, i0, nl, valid, row, qr, m);
+    for (int i0 = 0; i0 < nl; i0 += kValuBatch) valu_batch<false>(p, i0, nl, valid, lane, qr, m);
   }
-#pragma unroll
-  for (int h = 0; h < kHeads; ++h) {
-    m[h] = fmaxf(m[h], __shfl_xor(m[h], 16));
-    m[h] = fmaxf(m[h], __shfl_xor(m[h], 32));
-  }
+  m = fmaxf(m, __shfl_xor(m, 16));
+  m = fmaxf(m, __shfl_xor(m, 32));
+  return dpp_f32<kQuadSwapMid>(m);  // lane l & 3 = h now holds head h
 }
 
 // MFMA engine. v_mfma_f32_16x16x32_bf16 with A = q (rows = heads, padded 4 -> 16 with
@@ -641,20 +646,25 @@ __device__ __forceinline__ DevicePlan device_plan(const int32_t* lens, int batch
   return DevicePlan{C, 0, 0, false};
 }
 
-// Block j of the row, held in cache page `page`.
+// Block j of the row, held in cache page `page`: the maximum of head (lane & 3), valid in
+// lanes 0..3.
 template <int ENGINE>
-__device__ __forceinline__ void score_page(const SplitArgs& a, int page, int j, int L, int lane,
-                                           const void* qr, float (&m)[kHeads]) {
+__device__ __forceinline__ float score_page(const SplitArgs& a, int page, int j, int L, int lane,
+                                            const void* qr) {
   const int valid = min(kBlock, L - j * kBlock);
   if (page < 0 || (int64_t)page >= a.num_pages) {
-#pragma unroll
-    for (int h = 0; h < kHeads; ++h) m[h] = -__builtin_inff();
     if (a.err != nullptr && lane == 0) atomicOr(a.err, (uint32_t)MSA_DEVERR_PAGE_OUT_OF_RANGE);
-    return;
+    return -__builtin_inff();
   }
   const uint16_t* pg = a.k + (size_t)page * kPageElems;
-  if constexpr (ENGINE == MSA_ENGINE_MFMA) score_block_mfma(pg, valid, *static_cast<const QMfma*>(qr), lane, m);
-  else score_block_valu(pg, valid, *static_cast<const QValu*>(qr), lane, m);
+  if constexpr (ENGINE == MSA_ENGINE_MFMA) {
+    float m[kHeads];
+    score_block_mfma(pg, valid, *static_cast<const QMfma*>(qr), lane, m);
+    const int h = lane & 3;
+    return h == 0 ? m[0] : h == 1 ? m[1] : h == 2 ? m[2] : m[3];
+  } else {
+    return score_block_valu(pg, valid, *static_cast<const QValu*>(qr), lane);
+  }
 }
 
 template <int ENGINE, int MODE>
@@ -697,9 +707,8 @@ __global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
     if (j0 >= nb) return;
     for (int j = j0 + wave; j < j1; j += kWaves) {
       const int next = j + kWaves < j1 ? btrow[j + kWaves] : 0;
-      float m[kHeads];
-      score_page<ENGINE>(a, page, j, L, lane, &qr, m);
-      if (lane < kHeads) a.scores[((size_t)b * kHeads + lane) * a.W + j] = m[lane];
+      const float m = score_page<ENGINE>(a, page, j, L, lane, &qr);
+      if (lane < kHeads) a.scores[((size_t)b * kHeads + lane) * a.W + j] = m;
       page = next;
     }
     return;
@@ -726,9 +735,8 @@ __global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
   }
   for (int j = j0 + wave; j < j1; j += kWaves) {
     const int next = j + kWaves < j1 ? btrow[j + kWaves] : 0;
-    float m[kHeads];
-    score_page<ENGINE>(a, page, j, L, lane, &qr, m);
-    if (lane < kHeads) sc[j - j0][lane] = m[lane];
+    const float m = score_page<ENGINE>(a, page, j, L, lane, &qr);
+    if (lane < kHeads) sc[j - j0][lane] = m;
     page = next;
   }
   __syncthreads();
