@@ -436,6 +436,55 @@ __device__ __forceinline__ uint64_t merge_rounds(const uint64_t* lk, int ns, int
 // are read with agent-scope atomic loads (device-coherent), all in flight at once.
 constexpr int kNetworkMaxM = 16;
 
+// One level of the register tree: r[t] takes the top 16 of r[t] and r[t + HALF], t < HALF.
+// The HALF merges are independent; each step is applied to all of them before the next, so
+// their dependency chains overlap.
+template <int HALF>
+__device__ __forceinline__ void merge_level(uint64_t (&r)[16], int lane) {
+#pragma unroll
+  for (int t = 0; t < HALF; ++t) r[t] = umax64(r[t], partner_u64<15>(r[t + HALF]));
+#pragma unroll
+  for (int t = 0; t < HALF; ++t) r[t] = bitonic_step<8, 8>(r[t], lane);
+#pragma unroll
+  for (int t = 0; t < HALF; ++t) r[t] = bitonic_step<4, 4>(r[t], lane);
+#pragma unroll
+  for (int t = 0; t < HALF; ++t) r[t] = bitonic_step<2, 2>(r[t], lane);
+#pragma unroll
+  for (int t = 0; t < HALF; ++t) r[t] = bitonic_step<1, 1>(r[t], lane);
+}
+
+// Sorts each row of r[0 .. N) from its runs of 2^lg keys into 16 (stages 2^(lg+1) .. 16),
+// the N registers step by step together.
+template <int N>
+__device__ __forceinline__ void sort_rows(uint64_t (&r)[16], int lg, int lane) {
+  if (lg < 1) {
+#pragma unroll
+    for (int t = 0; t < N; ++t) r[t] = bitonic_stage<2>(r[t], lane);
+  }
+  if (lg < 2) {
+#pragma unroll
+    for (int t = 0; t < N; ++t) r[t] = bitonic_step<3, 2>(r[t], lane);
+#pragma unroll
+    for (int t = 0; t < N; ++t) r[t] = bitonic_step<1, 1>(r[t], lane);
+  }
+  if (lg < 3) {
+#pragma unroll
+    for (int t = 0; t < N; ++t) r[t] = bitonic_step<7, 4>(r[t], lane);
+#pragma unroll
+    for (int t = 0; t < N; ++t) r[t] = bitonic_step<2, 2>(r[t], lane);
+#pragma unroll
+    for (int t = 0; t < N; ++t) r[t] = bitonic_step<1, 1>(r[t], lane);
+  }
+#pragma unroll
+  for (int t = 0; t < N; ++t) r[t] = bitonic_step<15, 8>(r[t], lane);
+#pragma unroll
+  for (int t = 0; t < N; ++t) r[t] = bitonic_step<4, 4>(r[t], lane);
+#pragma unroll
+  for (int t = 0; t < N; ++t) r[t] = bitonic_step<2, 2>(r[t], lane);
+#pragma unroll
+  for (int t = 0; t < N; ++t) r[t] = bitonic_step<1, 1>(r[t], lane);
+}
+
 __device__ __forceinline__ uint64_t merge_top16(const uint64_t* __restrict__ lists, size_t list_stride,
                                                 int ns, int Lk, int lane) {
   const int lg = Lk <= 1 ? 0 : Lk <= 2 ? 1 : Lk <= 4 ? 2 : Lk <= 8 ? 3 : 4;
@@ -450,25 +499,18 @@ __device__ __forceinline__ uint64_t merge_top16(const uint64_t* __restrict__ lis
                ? __hip_atomic_load(lists + sp * list_stride + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                : 0;
   }
-  if (lg < 4) {  // several lists per row (then at most 8 registers): sort each row
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      if (t < R) {
-        if (lg < 1) r[t] = bitonic_stage<2>(r[t], lane);
-        if (lg < 2) r[t] = bitonic_stage<4>(r[t], lane);
-        if (lg < 3) r[t] = bitonic_stage<8>(r[t], lane);
-        r[t] = bitonic_stage<16>(r[t], lane);
-      }
-    }
+  // Registers past R hold zeros: sorting or merging them changes nothing, so the stages
+  // below run on power-of-two register counts without a branch per register.
+  if (lg < 4) {  // several lists per row (then R <= 8): sort each row first
+    if (R > 4) sort_rows<8>(r, lg, lane);
+    else if (R > 2) sort_rows<4>(r, lg, lane);
+    else if (R > 1) sort_rows<2>(r, lg, lane);
+    else sort_rows<1>(r, lg, lane);
   }
-#pragma unroll
-  for (int half = 8; half >= 1; half >>= 1) {
-    if (R > half) {
-#pragma unroll
-      for (int t = 0; t < half; ++t)
-        if (t + half < R) r[t] = bitonic_clean16(umax64(r[t], partner_u64<15>(r[t + half])), lane);
-    }
-  }
+  if (R > 8) merge_level<8>(r, lane);
+  if (R > 4) merge_level<4>(r, lane);
+  if (R > 2) merge_level<2>(r, lane);
+  if (R > 1) merge_level<1>(r, lane);
   uint64_t x = r[0];
   x = bitonic_clean16(umax64(x, partner_u64<31>(x)), lane);
   x = bitonic_clean16(umax64(x, partner_u64<63>(x)), lane);
