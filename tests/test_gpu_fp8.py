@@ -155,6 +155,43 @@ def test_fp8_edges_and_out_of_range_page(msa):
     assert np.all(np.isneginf(s[2, :, :, 1]))
 
 
+@pytest.mark.parametrize("bf16", [False, True])
+def test_single_position_merge_in_or_after_the_launch(msa, bf16):
+    # One position merges inside the verify launch when each head's split lists fit four
+    # registers of the merge network (16 splits of 17 blocks here) and in a second launch
+    # otherwise (17 splits of 16): both must select exactly what the oracle selects on the
+    # GPU's own scores, and agree with each other bit for bit.
+    inp = synth.fp8_case(309, [128 * 272, 128 * 272 - 5, 128 * 200 + 1, 128 * 16, 3000, 0, 1],
+                         272, 1, k_scale=0.5)
+    if bf16:
+        inp = synth.multi_case(309, inp.seq_lens.tolist(), 272, 1)
+    q, k, bt, lens = (to_device_fp8(inp) if not bf16 else
+                      (torch.from_numpy(np.ascontiguousarray(inp.q).view(np.int16)).cuda().view(torch.bfloat16),
+                       torch.from_numpy(inp.k_cache.view(np.int16)).cuda().view(torch.bfloat16),
+                       torch.from_numpy(inp.block_table).cuda(), torch.from_numpy(inp.seq_lens).cuda()))
+    assert msa.plan(7, 272, 16, 16)["blocks_per_split"] == 17 and msa.plan(7, 272, 16, 17)["blocks_per_split"] == 16
+    if bf16:
+        s = msa.msa_indexer_block_scores_multi(q, k, bt, lens).cpu().numpy()
+        run = lambda ns: msa.msa_indexer_decode_multi(q, k, bt, lens, num_splits=ns)
+        tol = 1e-3
+    else:
+        s = msa.msa_indexer_block_scores_fp8(q, k, 0.5, bt, lens).cpu().numpy()
+        run = lambda ns: msa.msa_indexer_decode_fp8(q, k, 0.5, bt, lens, num_splits=ns)
+        tol = 1e-3 * 4.0 * 0.5
+    _, _, ref = oracle.decode(inp)
+    lp = position_lens(inp, 0, 1)
+    gi, gs = oracle.select(s[:, 0].astype(np.float64), lp, 16, 1, 2)
+    out = {}
+    for ns in (16, 17, 0):
+        ids, sc = run(ns)
+        ids, sc = ids.cpu().numpy()[:, 0], sc.cpu().numpy()[:, 0]
+        assert np.array_equal(ids, gi), ns
+        assert np.array_equal(sc[gi >= 0].astype(np.float64), gs[gi >= 0]), ns
+        check_selection_vs_oracle(ids, ref[:, 0], lp, 16, 1, 2, tol=tol)
+        out[ns] = (ids, sc)
+    assert np.array_equal(out[16][1], out[17][1])
+
+
 def test_fp8_single_position_workspace_reuse(msa):
     # One position merges in the same launch through per-row counters in the workspace; they
     # must be back at zero after every call, whatever the lengths and split counts.
