@@ -113,8 +113,10 @@ int32_t msa_indexer_plan(int32_t batch, int32_t max_blocks_per_seq, int32_t topk
  * then the per-split candidate keys, uint64 [batch][S][4][Lk]. The whole workspace must be
  * zero before its first use (e.g. hipMemset once after allocation). The library leaves the
  * counters at zero at the end of every call, so the same workspace can be reused, and
- * replayed in a graph, without clearing it again; the error word only ever gains bits
- * (msa_indexer_read_error clears it).
+ * replayed in a graph, without clearing it again, by calls with the same batch; the error
+ * word only ever gains bits (msa_indexer_read_error clears it). Before a call with a larger
+ * batch than the workspace last served, clear the counter lines of the extra rows (they
+ * held keys): the lines sit at fixed offsets, the keys right after batch lines.
  */
 size_t msa_indexer_workspace_bytes(int32_t batch, int32_t max_blocks_per_seq, int32_t topk,
                                    int32_t num_splits);

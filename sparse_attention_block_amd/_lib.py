@@ -172,6 +172,30 @@ def _inputs(q, k_cache, block_table, seq_lens):
     return ptrs, B, block_table.shape[1], block_table.stride(0), k_cache.shape[0]
 
 
+_WS_CACHE = {}
+
+
+def _default_workspace(nbytes: int, batch: int, device, stream):
+    """The workspace of a call that passes none: one zeroed buffer per (device, stream, batch,
+    size), reused, since the library leaves its per-row counters at zero at the end of every
+    call. The counter lines sit right after the header, one per row, so a buffer is only
+    reused for the same batch (with another batch they would overlap the last call's keys).
+    Calls on one stream run in order, so they never use it at the same time. Under graph
+    capture a fresh buffer is made instead (it then belongs to the graph's memory)."""
+    torch = _torch()
+    if nbytes == 0:
+        raise ValueError("invalid arguments for a workspace")
+    if torch.cuda.is_current_stream_capturing():
+        return torch.zeros(nbytes, dtype=torch.uint8, device=device)
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    key = (device.index, s.cuda_stream, batch, nbytes)
+    ws = _WS_CACHE.get(key)
+    if ws is None:
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        _WS_CACHE[key] = ws
+    return ws
+
+
 def new_workspace(batch: int, max_blocks: int, topk: int, splits: int = 0, device="cuda"):
     """A zeroed workspace tensor (uint8) of the size the library asks for."""
     torch = _torch()
@@ -193,7 +217,7 @@ def msa_indexer_decode(q, k_cache, block_table, seq_lens, topk=16, n_init=1, n_l
     if out_scores is None:
         out_scores = torch.empty((B, HEADS, topk), dtype=torch.float32, device=q.device)
     if workspace is None:
-        workspace = new_workspace(B, W, topk, num_splits, q.device)
+        workspace = _default_workspace(workspace_bytes(B, W, topk, num_splits), B, q.device, stream)
     args = [pq, pk, pbt, pl, B, W, stride, pages, topk, n_init, n_local,
             _dev(out_ids, "out_ids", torch.int32, (B, HEADS, topk)),
             _dev(out_scores, "out_scores", torch.float32, (B, HEADS, topk)),
@@ -223,7 +247,7 @@ def msa_indexer_decode_pages(q, k_cache, block_table, seq_lens, topk=16, n_init=
     if out_tokens is None:
         out_tokens = torch.empty((B, HEADS), dtype=torch.int32, device=dev)
     if workspace is None:
-        workspace = new_workspace(B, W, topk, num_splits, dev)
+        workspace = _default_workspace(workspace_bytes(B, W, topk, num_splits), B, dev, stream)
     rc = load().msa_indexer_decode_pages(
         pq, pk, pbt, pl, B, W, stride, pages, topk, n_init, n_local,
         _dev(out_ids, "out_ids", torch.int32, (B, HEADS, topk)),
@@ -289,10 +313,7 @@ def msa_indexer_decode_multi(q, k_cache, block_table, seq_lens, topk=16, n_init=
     if out_scores is None:
         out_scores = torch.empty((B, Q, HEADS, topk), dtype=torch.float32, device=dev)
     if workspace is None:
-        n = workspace_bytes_multi(B, W, Q, topk, num_splits)
-        if n == 0:
-            raise ValueError("invalid arguments for a workspace")
-        workspace = torch.zeros(n, dtype=torch.uint8, device=dev)
+        workspace = _default_workspace(workspace_bytes_multi(B, W, Q, topk, num_splits), B, dev, stream)
     rc = load().msa_indexer_decode_multi(
         pq, pk, pbt, pl, B, W, stride, pages, Q, topk, n_init, n_local,
         _dev(out_ids, "out_ids", torch.int32, (B, Q, HEADS, topk)),
@@ -330,10 +351,7 @@ def msa_indexer_decode_fp8(q, k_cache, k_scale, block_table, seq_lens, topk=16, 
     if out_scores is None:
         out_scores = torch.empty((B, Q, HEADS, topk), dtype=torch.float32, device=dev)
     if workspace is None:
-        n = workspace_bytes_multi(B, W, Q, topk, num_splits)
-        if n == 0:
-            raise ValueError("invalid arguments for a workspace")
-        workspace = torch.zeros(n, dtype=torch.uint8, device=dev)
+        workspace = _default_workspace(workspace_bytes_multi(B, W, Q, topk, num_splits), B, dev, stream)
     rc = load().msa_indexer_decode_fp8(
         pq, pk, float(k_scale), pbt, pl, B, W, stride, pages, Q, topk, n_init, n_local,
         _dev(out_ids, "out_ids", torch.int32, (B, Q, HEADS, topk)),

@@ -259,6 +259,30 @@ def test_workspace_reuse_and_counter_reset(msa):
         check_selection_vs_oracle(ids.cpu().numpy(), ref, new_lens, 16, 1, 2)
 
 
+def test_default_workspace_is_reused(msa):
+    # Calls that pass no workspace share one per (device, stream, size); the library leaves
+    # its counters at zero, so repeated calls with changing lengths stay exact.
+    from sparse_attention_block_amd import _lib
+    inp = synth.paged_case(112, [128 * 40] * 5, 40)
+    q, k, bt, lens = to_device(inp)
+    rng = np.random.default_rng(2)
+    before = len(_lib._WS_CACHE)
+    for it in range(4):
+        new_lens = rng.integers(0, 128 * 40 + 1, size=5).astype(np.int32)
+        lens.copy_(torch.from_numpy(new_lens))
+        ids, sc = msa.msa_indexer_decode(q, k, bt, lens)
+        gpu_s = msa.msa_indexer_block_scores(q, k, bt, lens).cpu().numpy()
+        check_selection_exact_given_scores(ids.cpu().numpy(), sc.cpu().numpy(), gpu_s, new_lens, 16, 1, 2)
+    assert len(_lib._WS_CACHE) <= before + 1
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        ids2, sc2 = msa.msa_indexer_decode(q, k, bt, lens)
+    torch.cuda.synchronize()
+    assert torch.equal(ids2, ids) and torch.equal(sc2, sc)
+    for (_, _, batch, _), ws in _lib._WS_CACHE.items():  # every cached counter line is zero
+        assert int(ws[256:256 + 256 * batch].view(torch.int32).abs().sum()) == 0
+
+
 def test_decode_engines_agree_on_exact_data(msa):
     # Both engines through the whole pass on the planted workload: bit-exact ids and scores.
     inp, want_ids, want_sc, _ = cfg(5)
