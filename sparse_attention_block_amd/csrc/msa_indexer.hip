@@ -762,7 +762,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
   if (s >= ns) {
     // An empty row has no workgroup to merge it: its first workgroup writes the padding.
     if (MODE == kFused && nb == 0 && s == 0) {
-      if (threadIdx.x < kHeads * a.topk) {
+      if ((int)threadIdx.x < kHeads * a.topk) {
         const size_t o = (size_t)b * kHeads * a.topk + threadIdx.x;
         a.out_ids[o] = -1;
         a.out_scores[o] = -__builtin_inff();
@@ -1072,7 +1072,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   }
   if (j0 >= nb) {
     // An empty row has no workgroup to merge it: its first workgroup writes the padding.
-    if (MODE == kFused && nb == 0 && s == 0 && threadIdx.x < kHeads * a.topk) {
+    if (MODE == kFused && nb == 0 && s == 0 && (int)threadIdx.x < kHeads * a.topk) {
       const size_t o = (size_t)b * kHeads * a.topk + threadIdx.x;
       a.out_ids[o] = -1;
       a.out_scores[o] = -__builtin_inff();
@@ -1283,8 +1283,6 @@ int32_t make_decode_plan(int32_t batch, int32_t W, int32_t topk, int32_t num_spl
   }
   return MSA_OK;
 }
-
-size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Workspace: [error word (256 B) | counters uint32 [batch][64] | keys uint64 [batch][S][4][Lk]]
 size_t keys_offset(int32_t batch) {
