@@ -214,6 +214,67 @@ def bench_configs(msa, synth, np, torch) -> int:
     return 0
 
 
+def bench_sweep(msa, np, torch) -> int:
+    """The batch x context grid the SGLang PR #41488 Speed Tests table measures (batch 1, 8,
+    16, 32 at 8K, 32K and 128K tokens, and batches of 16 and 32 with one 128K row and the rest
+    1K), for the bf16 and the FP8 E4M3 cache, one JSON line per shape: the decode call (one
+    position) under the graph protocol. The pages' numbers are for four GPUs with
+    communication, so they are context, not a comparison. Each shape draws its pages
+    without repetition from one random pool (a 1 GiB bf16 cache and a 512 MiB FP8 one,
+    ~N(0,1) values), so every call reads distinct pages."""
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(9)
+    pool_pages = 32768
+    k_bf16 = torch.randn((pool_pages, 128, 128), generator=gen, device=dev).to(torch.bfloat16)
+    k_fp8 = torch.randn((pool_pages, 128, 128), generator=gen, device=dev).clamp_(-448, 448)
+    k_fp8 = k_fp8.to(torch.float8_e4m3fn).view(torch.uint8)
+    rng = np.random.default_rng(9)
+    shapes = [(b, ctx) for ctx in (8192, 32768, 131072) for b in (1, 8, 16, 32)]
+    shapes += [("mixed", 16), ("mixed", 32)]
+    for shape in shapes:
+        if shape[0] == "mixed":
+            B = shape[1]
+            lens_np = np.full(B, 1024, dtype=np.int32)
+            lens_np[0] = 131072
+            name = f"batch {B}: one 131072-token row, the rest 1024"
+        else:
+            B, ctx = shape
+            lens_np = np.full(B, ctx, dtype=np.int32)
+            name = f"batch {B} x {ctx}"
+        W = int(-(-int(lens_np.max()) // 128))
+        nb = -(-lens_np // 128)
+        pages = rng.permutation(pool_pages)[:int(nb.sum())].astype(np.int32)
+        bt_np = np.zeros((B, W), dtype=np.int32)
+        off = 0
+        for b in range(B):
+            bt_np[b, :nb[b]] = pages[off:off + nb[b]]
+            off += nb[b]
+        bt = torch.from_numpy(bt_np).to(dev)
+        lens = torch.from_numpy(lens_np).to(dev)
+        q = torch.randn((B, 4, 128), generator=gen, device=dev).to(torch.bfloat16)
+        q1 = q[:, None].contiguous()
+        ids = torch.empty((B, 4, 16), dtype=torch.int32, device=dev)
+        sc = torch.empty((B, 4, 16), dtype=torch.float32, device=dev)
+        ws = msa.new_workspace(B, W, 16, 0, dev)
+        ws8 = torch.zeros(msa.workspace_bytes_multi(B, W, 1, 16), dtype=torch.uint8, device=dev)
+        tokens = int(lens_np.sum())
+        us = graph_us_per_call(torch, lambda: msa.msa_indexer_decode(q, k_bf16, bt, lens, out_ids=ids,
+                                                                     out_scores=sc, workspace=ws))
+        ids8 = ids.view(B, 1, 4, 16)
+        sc8 = sc.view(B, 1, 4, 16)
+        us8 = graph_us_per_call(torch, lambda: msa.msa_indexer_decode_fp8(q1, k_fp8, 1.0, bt, lens,
+                                                                          out_ids=ids8, out_scores=sc8,
+                                                                          workspace=ws8))
+        print(json.dumps({"workload": name, "batch": B, "tokens": tokens,
+                          "bf16_us": round(us, 2), "bf16_GBs": round(tokens * 256 / (us * 1e-6) / 1e9, 1),
+                          "fp8_us": round(us8, 2), "fp8_GBs": round(tokens * 128 / (us8 * 1e-6) / 1e9, 1),
+                          "protocol": "8 calls per HIP graph, 100 replays per round, median of 7 rounds"}),
+              flush=True)
+    return 0
+
+
 def bench_multi(args, msa, synth, np, torch) -> int:
     """Multi-token decode step (qlen draft positions per row) over the benchmark's cache."""
     Q = args.qlen
@@ -339,6 +400,9 @@ def main() -> int:
     ap.add_argument("--configs", action="store_true",
                     help="time the four smaller workloads (graph protocol, warm and with rotating "
                          "input copies) instead of the benchmark step")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time the decode call (bf16 and FP8 caches) over a batch x context grid "
+                         "instead of the benchmark step")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip timing the page-table entry points")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -369,6 +433,8 @@ def main() -> int:
     lib = msa.load()  # raises if the HIP library is not built
     if args.configs:
         return bench_configs(msa, synth, np, torch)
+    if args.sweep:
+        return bench_sweep(msa, np, torch)
     if args.qlen != 1 or args.fp8:
         return bench_multi(args, msa, synth, np, torch)
     log("generating the batch 32 x 131072 workload (1 GiB of bf16 index-K)")

@@ -96,11 +96,14 @@ int32_t msa_indexer_num_splits(int32_t batch, int32_t max_blocks_per_seq, int32_
  * The plan a call with these arguments uses: S splits per row, C blocks per split, Lk =
  * min(topk, C) candidates kept per (split, head), and whether the merge runs inside the
  * split kernel (fused: one launch) or as a second launch. Any output pointer may be NULL.
- * Returns MSA_OK or a negative status. The multi-token and FP8 calls use the host plan's S
- * and C (this function with batch * max_blocks_per_seq below 8192, or with num_splits > 0)
- * and merge in a second launch, except with qlen = 1, topk <= 16 and lists short enough
- * that a row's merge is cheap (S lists of Lk keys rounded up to a power of two, at most
- * 4 * 64 / Lk2 lists), where the last split of each row merges it in the same launch.
+ * Returns MSA_OK or a negative status. With num_splits = 0, topk <= 16 and batch *
+ * max_blocks_per_seq >= 8192 the plan is the device plan: S is then the most splits a row
+ * can have (min(64, ceil(W/4))), and the kernel itself picks C (a power of two >= 4) and
+ * each workgroup's (row, split) from seq_lens, so that about 512 workgroups cover the
+ * tokens actually present. The multi-token and FP8 calls use the same plan and merge in a
+ * second launch, except with qlen = 1, topk <= 16 and either the device plan or lists short
+ * enough that a row's merge is cheap (S lists of Lk keys rounded up to a power of two, at
+ * most 4 * 64 / Lk2 lists): then the last split of each row merges it in the same launch.
  */
 int32_t msa_indexer_plan(int32_t batch, int32_t max_blocks_per_seq, int32_t topk, int32_t num_splits,
                          int32_t *splits, int32_t *blocks_per_split, int32_t *candidates_per_split,
@@ -252,9 +255,9 @@ size_t msa_indexer_workspace_bytes_multi(int32_t batch, int32_t max_blocks_per_s
  *   workspace    at least msa_indexer_workspace_bytes_multi(...) bytes, 256-byte aligned.
  * Every other argument as in msa_indexer_decode. Each page is read once for all positions
  * and heads (MFMA: 4 positions x 4 heads fill the 16 rows of v_mfma_f32_16x16x32_bf16).
- * Two launches (one for qlen = 1 with a cheap merge, see msa_indexer_plan): per-split
- * top-k of every (position, head), then one wave per (b, p, h)
- * merging the splits' lists.
+ * Two launches (one for qlen = 1 under the conditions msa_indexer_plan states): per-split
+ * top-k of every (position, head), then one wave per (b, p, h) merging the splits' lists.
+ * Under the device plan both launches derive the split width from seq_lens alike.
  */
 int32_t msa_indexer_decode_multi(const void *q, const void *k_cache, const int32_t *block_table,
                                  const int32_t *seq_lens, int32_t batch,

@@ -656,9 +656,14 @@ struct DevicePlan {
 // of rows l, l+64, ... (rows past the first 64 are read again in the second pass; they are
 // cache hits); sums, the longest-row bound and prefix sums are ballots, without LDS. Block
 // counts are at most 4096 (13 bits) and split counts at most 64 (7 bits).
-__device__ __forceinline__ DevicePlan device_plan(const int32_t* lens, int batch, int W, int g, int lane) {
-  auto blocks = [&](int r) { return r < batch ? (row_tokens(lens, r, W) + kBlock - 1) / kBlock : 0; };
-  const int nb0 = blocks(lane);
+__device__ __forceinline__ int device_blocks(const int32_t* lens, int batch, int W, int r) {
+  return r < batch ? (row_tokens(lens, r, W) + kBlock - 1) / kBlock : 0;
+}
+
+// The split width C of the device plan (the same in every lane); nb0 = this lane's row's
+// block count, device_blocks(lens, batch, W, lane).
+__device__ __forceinline__ int device_split_width(const int32_t* lens, int batch, int W, int lane, int nb0) {
+  auto blocks = [&](int r) { return device_blocks(lens, batch, W, r); };
   int N = 0;
   bool over[5] = {false, false, false, false, false};  // a row needs more than 64 splits of 4 << t blocks
   for (int r0 = 0; r0 < batch; r0 += 64) {
@@ -670,8 +675,13 @@ __device__ __forceinline__ DevicePlan device_plan(const int32_t* lens, int batch
   int C_min = 4;
 #pragma unroll
   for (int t = 0; t < 5; ++t) C_min = over[t] ? (4 << (t + 1)) : C_min;
-  const int C = min(max(pow2_ceil_dev(max(1, (N + kDeviceTarget - 1) / kDeviceTarget)), C_min),
-                    kMaxSplitBlocks);
+  return min(max(pow2_ceil_dev(max(1, (N + kDeviceTarget - 1) / kDeviceTarget)), C_min), kMaxSplitBlocks);
+}
+
+__device__ __forceinline__ DevicePlan device_plan(const int32_t* lens, int batch, int W, int g, int lane) {
+  auto blocks = [&](int r) { return device_blocks(lens, batch, W, r); };
+  const int nb0 = blocks(lane);
+  const int C = device_split_width(lens, batch, W, lane, nb0);
   int base = 0;
   for (int r0 = 0; r0 < batch; r0 += 64) {
     const int r = r0 + lane;
@@ -847,6 +857,8 @@ __global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
 struct MergeArgs {
   const int32_t* lens;
   int32_t W, Q, S, C, Lk, topk;
+  int32_t batch;
+  int32_t device_plan;  // C (and Lk = min(topk, C)) chosen on the device, as the split pass did
   const uint64_t* keys;
   int32_t* out_ids;     // [batch][Q][4][topk]
   float* out_scores;
@@ -869,8 +881,11 @@ __global__ __launch_bounds__(64) void merge_kernel(MergeArgs a) {
   const int nb = (L + kBlock - 1) / kBlock;
   const int Lp = causal_len(L, a.Q, p);
   const int m = min(a.topk, (Lp + kBlock - 1) / kBlock);
-  const int ns = (nb + a.C - 1) / a.C;
-  const int Lk = a.Lk, stride = Lk + 1, QH = a.Q * kHeads;
+  const int C = a.device_plan ? device_split_width(a.lens, a.batch, a.W, lane,
+                                                   device_blocks(a.lens, a.batch, a.W, lane))
+                              : a.C;
+  const int ns = (nb + C - 1) / C;
+  const int Lk = a.device_plan ? min(a.topk, C) : a.Lk, stride = Lk + 1, QH = a.Q * kHeads;
   const uint64_t* src = a.keys + ((size_t)b * a.S * QH + task) * Lk;
   uint64_t mine;
   if (ns <= 64 && a.topk <= kNetworkMaxM) {
@@ -1033,6 +1048,8 @@ struct VerifyArgs {
   int32_t W, bt_stride;
   int64_t num_pages;
   int32_t Q, S, C, Lk, topk, n_init, n_local;
+  int32_t batch;
+  int32_t device_plan;  // split modes: C and each workgroup's (row, split) chosen on the device
   uint64_t* keys;       // [batch][S][Q*4][Lk]
   uint32_t* err;        // device error word (may be null)
   float* scores;        // [batch][Q][4][W] (block-score mode)
@@ -1056,7 +1073,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4;
-  const int s = blockIdx.x, b = blockIdx.y, C = a.C, Lk = a.Lk;
+  int s = blockIdx.x, b = blockIdx.y, C = a.C, Lk = a.Lk;
+  if (MODE != kScores && a.device_plan) {
+    const DevicePlan dp = device_plan(a.lens, a.batch, a.W, blockIdx.x, lane);
+    if (!dp.active) return;
+    s = dp.s;
+    b = dp.b;
+    C = dp.C;
+    Lk = min(a.topk, C);
+  }
   const int L = row_tokens(a.lens, b, a.W);
   const int nb = (L + kBlock - 1) / kBlock;
   const int Lg = g < a.Q ? causal_len(L, a.Q, g) : 0;
@@ -1264,11 +1289,12 @@ int32_t make_plan(int32_t batch, int32_t W, int32_t topk, int32_t num_splits, Pl
   }
 }
 
-// The plan of msa_indexer_decode: with num_splits = 0, 0 < W <= 64 * 64, topk <= 16 and
-// batch * W >= kDeviceMinBlocks the device plan (fused, at most min(64, ceil(W/4)) splits per row, Lk <= topk keys per split
-// and head, a grid that covers any lengths: with C >= N/512 and C >= 4 the rows need at
-// most N/C + batch <= 512 + batch workgroups, or ceil(batch*W/64) + batch when C is held at
-// 64); otherwise the host plan above.
+// The plan of msa_indexer_decode and of the multi-token and FP8 calls: with num_splits = 0,
+// 0 < W <= 64 * 64, topk <= 16 and batch * W >= kDeviceMinBlocks the device plan (at most
+// min(64, ceil(W/4)) splits per row, Lk <= topk keys per split and head, a grid that covers
+// any lengths: with C >= N/512 and C >= 4 the rows need at most N/C + batch <= 512 + batch
+// workgroups, or ceil(batch*W/64) + batch when C is held at 64); otherwise the host plan
+// above.
 int32_t make_decode_plan(int32_t batch, int32_t W, int32_t topk, int32_t num_splits, Plan* p) {
   int32_t rc = make_plan(batch, W, topk, num_splits, p);
   if (rc != MSA_OK) return rc;
@@ -1411,6 +1437,8 @@ int32_t launch_merge(const uint64_t* keys, const int32_t* lens, int32_t W, int32
   a.bt_stride = bt_stride;
   a.out_pages = out_pages;
   a.out_tokens = out_tokens;
+  a.batch = batch;
+  a.device_plan = p.device ? 1 : 0;
   hipLaunchKernelGGL(merge_kernel, dim3(Q * kHeads, batch), dim3(64), merge_lds_bytes(p.S, p.Lk, topk), st, a);
   return hipGetLastError() == hipSuccess ? MSA_OK : MSA_ERR_HIP;
 }
@@ -1466,6 +1494,8 @@ VerifyArgs make_verify_args(const void* q, const void* k, const int32_t* bt, con
   a.scores = nullptr;
   a.out_ids = nullptr;
   a.out_scores = nullptr;
+  a.batch = batch;
+  a.device_plan = p.device ? 1 : 0;
   return a;
 }
 
@@ -1477,17 +1507,19 @@ bool valid_scale(float k_scale) { return k_scale > 0.0f && k_scale <= 3.40282346
 // runs every (row, head) at once (FP8 at batch 32 x 128K: 32 lists of 16, 89.8 vs 88.7 us).
 bool fuse_verify(const Plan& p, int topk) {
   if (p.S > 64 || topk > kNetworkMaxM) return false;
+  if (p.device) return true;  // at most 64 splits per row; the row's own count is only known on the device
   int lk2 = 1;
   while (lk2 < p.Lk) lk2 <<= 1;
   return ceil_div(p.S, 64 / lk2) <= 4;
 }
 
 template <int MODE>
-void launch_verify(const VerifyArgs& a, bool fp8, int32_t batch, hipStream_t st) {
+void launch_verify(const VerifyArgs& a, bool fp8, int32_t batch, hipStream_t st, int device_grid = 0) {
+  const dim3 grid = device_grid > 0 ? dim3(device_grid, 1) : dim3(a.S, batch);
   if (fp8)
-    hipLaunchKernelGGL((verify_kernel<MODE, true>), dim3(a.S, batch), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((verify_kernel<MODE, true>), grid, dim3(kThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((verify_kernel<MODE, false>), dim3(a.S, batch), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((verify_kernel<MODE, false>), grid, dim3(kThreads), 0, st, a);
 }
 
 int32_t verify_decode_impl(const void* q, const void* k_cache, bool fp8, float k_scale,
@@ -1501,20 +1533,21 @@ int32_t verify_decode_impl(const void* q, const void* k_cache, bool fp8, float k
   if (rc != MSA_OK) return rc;
   if ((rc = check_select(topk, n_init, n_local)) != MSA_OK) return rc;
   Plan p;
-  if ((rc = make_plan(batch, W, topk, num_splits, &p)) != MSA_OK) return rc;
+  if ((rc = make_decode_plan(batch, W, topk, num_splits, &p)) != MSA_OK) return rc;
   if (batch == 0) return MSA_OK;
   if (!out_ids || !out_scores || !aligned(out_ids, 4) || !aligned(out_scores, 4)) return MSA_ERR_INVALID_ARG;
   if (!workspace || !aligned(workspace, kAlign)) return MSA_ERR_INVALID_ARG;
   if (workspace_bytes < ws_bytes_multi(batch, qlen, p)) return MSA_ERR_WORKSPACE_TOO_SMALL;
   VerifyArgs a = make_verify_args(q, k_cache, block_table, seq_lens, W, bt_stride, num_pages, qlen,
                                   p, topk, n_init, n_local, workspace, batch, k_scale);
+  const int grid = p.device ? p.grid : 0;
   if (qlen == 1 && fuse_verify(p, topk)) {  // one position, few lists: merge in the same launch
     a.out_ids = out_ids;
     a.out_scores = out_scores;
-    launch_verify<kFused>(a, fp8, batch, st);
+    launch_verify<kFused>(a, fp8, batch, st, grid);
     return hipGetLastError() == hipSuccess ? MSA_OK : MSA_ERR_HIP;
   }
-  launch_verify<kSplit>(a, fp8, batch, st);
+  launch_verify<kSplit>(a, fp8, batch, st, grid);
   if (hipGetLastError() != hipSuccess) return MSA_ERR_HIP;
   return launch_merge(a.keys, seq_lens, W, qlen, p, topk, out_ids, out_scores, batch, st);
 }
@@ -1739,10 +1772,11 @@ int32_t msa_indexer_read_error(void* workspace, uint32_t* host_flags, void* stre
 
 size_t msa_indexer_workspace_bytes_multi(int32_t batch, int32_t max_blocks_per_seq, int32_t qlen,
                                          int32_t topk, int32_t num_splits) {
-  Plan p;
+  Plan p, d;
   if (qlen < 1 || qlen > MSA_MAX_QUERY_LEN) return 0;
   if (make_plan(batch, max_blocks_per_seq, topk, num_splits, &p) != MSA_OK) return 0;
-  return ws_bytes_multi(batch, qlen, p);
+  if (make_decode_plan(batch, max_blocks_per_seq, topk, num_splits, &d) != MSA_OK) return 0;
+  return std::max(ws_bytes_multi(batch, qlen, p), ws_bytes_multi(batch, qlen, d));
 }
 
 int32_t msa_indexer_decode_multi(const void* q, const void* k_cache, const int32_t* block_table,

@@ -264,8 +264,10 @@ def test_decode_multi_workspace_and_no_op(lib):
     ws = lib.msa_indexer_workspace_bytes_multi
     # header, counter lines, then keys [batch][S][qlen*4][Lk]: 8 blocks -> 2 splits of 4, Lk 4
     assert ws(2, 8, 4, 16, 0) == 256 + 2 * 256 + 2 * 2 * 16 * 4 * 8
-    assert ws(32, 1024, 4, 16, 0) == 256 + 32 * 256 + 32 * 32 * 16 * 16 * 8
-    assert ws(32, 1024, 1, 16, 0) == 256 + 32 * 256 + 32 * 32 * 4 * 16 * 8
+    # with num_splits = 0 the device plan (up to 64 splits per row, Lk <= topk) bounds the size
+    assert ws(32, 1024, 4, 16, 0) == 256 + 32 * 256 + 32 * 64 * 16 * 16 * 8
+    assert ws(32, 1024, 1, 16, 0) == 256 + 32 * 256 + 32 * 64 * 4 * 16 * 8
+    assert ws(32, 1024, 4, 16, 32) == 256 + 32 * 256 + 32 * 32 * 16 * 16 * 8
     assert ws(2, 8, 0, 16, 0) == 0 and ws(2, 8, 5, 16, 0) == 0
     assert _decode_multi(lib, ws_bytes=ws(2, 8, 4, 16, 0) - 1) == WS_SMALL
     assert _decode_multi(lib, batch=0, q=None, k=None, bt=None, lens=None, ids=None, scores=None,
