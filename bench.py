@@ -356,7 +356,8 @@ def bench_multi(args, msa, synth, np, torch) -> int:
                         "blocks of 128 tokens, 4 index heads x 128, top-16, 1 initial + 2 recent "
                         "blocks pinned",
             "batch": B, "qlen": Q, "seq_len": int(inp.seq_lens[0]), "topk": topk,
-            "num_splits": plan["splits"], "blocks_per_split": plan["blocks_per_split"],
+            "num_splits": plan["splits"] if plan["blocks_per_split"] else "chosen per call on the device",
+            "blocks_per_split": plan["blocks_per_split"] or "chosen per call on the device",
             "index_k_bytes": nbytes,
             "step_call": "msa_indexer_decode_fp8" if args.fp8 else "msa_indexer_decode_multi",
         },
@@ -548,7 +549,7 @@ def main() -> int:
                         "top-16, 1 initial + 2 recent blocks pinned",
             "batch": B, "seq_len": int(inp.seq_lens[0]), "index_heads": 4, "head_dim": 128,
             "block_tokens": 128, "topk": topk, "n_init": n_init, "n_local": n_local,
-            "num_splits": splits,
+            "num_splits": splits if plan["blocks_per_split"] else "chosen per call on the device",
             "blocks_per_split": plan["blocks_per_split"] or "chosen per call on the device",
             "fused_merge": plan["fused"], "engine": engine, "index_k_bytes": nbytes,
             "step_call": "msa_indexer_decode_pages" if args.step == "decode_pages" and plan["fused"]

@@ -97,10 +97,14 @@ int32_t msa_indexer_num_splits(int32_t batch, int32_t max_blocks_per_seq, int32_
  * min(topk, C) candidates kept per (split, head), and whether the merge runs inside the
  * split kernel (fused: one launch) or as a second launch. Any output pointer may be NULL.
  * Returns MSA_OK or a negative status. With num_splits = 0, topk <= 16 and batch *
- * max_blocks_per_seq >= 8192 the plan is the device plan: S is then the most splits a row
- * can have (min(64, ceil(W/4))), and the kernel itself picks C (a power of two >= 4) and
- * each workgroup's (row, split) from seq_lens, so that about 512 workgroups cover the
- * tokens actually present. The multi-token and FP8 calls use the same plan and merge in a
+ * max_blocks_per_seq >= 8192 the plan is the device plan: the kernel itself picks C (a
+ * power of two from 4 to 64) and each workgroup's (row, split) from seq_lens, so that about
+ * 512 workgroups cover the tokens actually present; *blocks_per_split is then 0 and *splits
+ * is S = min(64, ceil(W/4)), which sizes the workspace (S * topk keys per row and head). A
+ * row of nb blocks takes ceil(nb / C) splits of Lk = min(topk, C) keys per head, as many as
+ * fit those keys and the merge (at most 1024 keys, lists rounded up to a power of two): at
+ * topk = 16, up to 256 splits of 4 blocks, so that one long row among short ones is still
+ * spread over the whole chip. The multi-token and FP8 calls use the same plan and merge in a
  * second launch, except with qlen = 1, topk <= 16 and either the device plan or lists short
  * enough that a row's merge is cheap (S lists of Lk keys rounded up to a power of two, at
  * most 4 * 64 / Lk2 lists): then the last split of each row merges it in the same launch.

@@ -420,8 +420,9 @@ __device__ __forceinline__ uint64_t merge_rounds(const uint64_t* lk, int ns, int
   return mine;
 }
 
-// Top 16 of up to 64 sorted lists with a bitonic merge network held in registers (one
-// wave, all lanes active). Every list is best first with Lk <= 16 keys; rounded up to
+// Top 16 of sorted lists with a bitonic merge network held in registers (one wave, all
+// lanes active): ns lists with ns * Lk2 <= 1024 (network_fits). Every list is best first
+// with Lk <= 16 keys; rounded up to
 // Lk2 = 2^lg >= Lk (zero padded), 16 / Lk2 lists share a 16-lane row, so a register holds
 // 64 / Lk2 lists: lane l of register t reads element l % Lk2 of list
 // t * (64 / Lk2) + l / Lk2. Each row is first sorted from its runs of Lk2 into 16 (the
@@ -435,6 +436,18 @@ __device__ __forceinline__ uint64_t merge_rounds(const uint64_t* lk, int ns, int
 // extraction). The lists may have been written by other workgroups on other XCDs, so they
 // are read with agent-scope atomic loads (device-coherent), all in flight at once.
 constexpr int kNetworkMaxM = 16;
+constexpr int kNetworkKeys = 16 * 64;  // 16 registers of 64 lanes
+
+__device__ __host__ __forceinline__ int pow2_at_least(int x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+
+// Whether merge_top16 takes ns lists of Lk keys for a top-`topk` selection.
+__device__ __host__ __forceinline__ bool network_fits(int ns, int Lk, int topk) {
+  return topk <= kNetworkMaxM && ns * pow2_at_least(Lk) <= kNetworkKeys;
+}
 
 // One level of the register tree: r[t] takes the top 16 of r[t] and r[t + HALF], t < HALF.
 // The HALF merges are independent; each step is applied to all of them before the next, so
@@ -501,8 +514,9 @@ __device__ __forceinline__ uint64_t merge_top16(const uint64_t* __restrict__ lis
   }
   // Registers past R hold zeros: sorting or merging them changes nothing, so the stages
   // below run on power-of-two register counts without a branch per register.
-  if (lg < 4) {  // several lists per row (then R <= 8): sort each row first
-    if (R > 4) sort_rows<8>(r, lg, lane);
+  if (lg < 4) {  // several lists per row: sort each row first
+    if (R > 8) sort_rows<16>(r, lg, lane);
+    else if (R > 4) sort_rows<8>(r, lg, lane);
     else if (R > 2) sort_rows<4>(r, lg, lane);
     else if (R > 1) sort_rows<2>(r, lg, lane);
     else sort_rows<1>(r, lg, lane);
@@ -574,6 +588,27 @@ __device__ __forceinline__ void emit_pages(int id, bool valid, int topk, int lan
 
 enum Mode { kScores = 0, kSplit = 1, kFused = 2 };
 
+// The most splits of C blocks a row may have under the device plan: its lists (ns *
+// min(topk, C) keys per head) must fit the S * topk keys the workspace holds per row and
+// head, and the merge network. At topk = 16, S = 64: 256, 128, 64, 64, 64 for C = 4 .. 64,
+// i.e. rows of up to 1024 blocks at C <= 16, 2048 at 32 and 4096 at 64.
+__device__ __host__ __forceinline__ int device_max_splits(int C, int S, int topk) {
+  const int lk = min(topk, C);
+  return min(S * topk / lk, kNetworkKeys / pow2_at_least(lk));
+}
+
+// The longest row (in blocks) that splits of 4 << t blocks may cover, t = 0 .. 4; computed
+// on the host for the call's S and topk.
+struct SplitLimits {
+  int32_t blocks[5];
+};
+
+SplitLimits split_limits(int S, int topk) {
+  SplitLimits l;
+  for (int t = 0; t < 5; ++t) l.blocks[t] = device_max_splits(4 << t, S, topk) * (4 << t);
+  return l;
+}
+
 struct SplitArgs {
   const uint16_t* q;
   const uint16_t* k;
@@ -584,6 +619,7 @@ struct SplitArgs {
   int32_t S, C, Lk, topk, n_init, n_local;
   int32_t batch;
   int32_t device_plan;  // fused mode: C and each workgroup's (row, split) chosen on the device
+  SplitLimits lim;      // device plan: per-row block limits of each split width
   uint64_t* keys;       // [batch][S][4][Lk]
   uint32_t* err;        // device error word (may be null)
   uint32_t* counters;   // [batch][kCounterStride]: [0] workgroups finished; zero between calls
@@ -603,17 +639,17 @@ __device__ __forceinline__ int row_tokens(const int32_t* lens, int b, int W) {
 // its query positions; TensorRT-LLM PR #17008, Description: the causal clamp).
 __device__ __forceinline__ int causal_len(int L, int Q, int p) { return max(0, L - (Q - 1 - p)); }
 
-// Scores block j of the row for the four heads.
 // ---------------------------------------------------------------------------------------
-// The device plan of the fused single-token pass. The host launches a 1-D grid sized from
-// its arguments alone; every workgroup then reads the row lengths and picks the same split
-// width C: about 512 workgroups in all (measured best for uniform batches: 4..32 rows of
-// 128K tokens), at least 4 blocks per split, and at most 64 splits in any row (the fused
-// merge's fan-in), so a long row among short ones still gets 64 workgroups. Row b takes
+// The device plan (the fused single-token pass, and the split passes of the multi-token and
+// FP8 calls). The host launches a 1-D grid sized from its arguments alone; every workgroup
+// then reads the row lengths and picks the same split width C: about 512 workgroups in all
+// (measured best for uniform batches: 4..32 rows of 128K tokens), at least 4 blocks per
+// split, and no more splits in any row than its lists can hold (device_max_splits: up to
+// 256 at C = 4), so a long row among short ones still spreads over the chip. Row b takes
 // max(1, ceil(nb_b / C)) consecutive workgroup ids (an empty row one, to write its
 // padding); workgroups past the last row have nothing to do.
 constexpr int kDeviceTarget = 512;     // workgroups the device plan aims at
-constexpr int kDeviceMaxSplits = 64;   // splits per row (the fused merge's fan-in)
+constexpr int kDeviceMaxSplits = 64;   // splits per row at 16 or more blocks per split
 // Tables of fewer blocks (batch x W) keep the host plan: the device plan's prologue (the
 // row lengths read before any page) costs ~1 us, which only pays where a row can be long.
 constexpr int64_t kDeviceMinBlocks = 8192;
@@ -641,10 +677,11 @@ __device__ __forceinline__ int wave_sum_bits(int x) {
   return total;
 }
 
-__device__ __forceinline__ int pow2_ceil_dev(int x) {
-  int p = 1;
-  while (p < x) p <<= 1;
-  return p;
+// Where the list of split s, task t (position-head p * 4 + h) of row b starts in the
+// workspace keys: rows lie S * QH * LkMax keys apart (LkMax = the plan's Lk; topk under
+// the device plan), and a row's lists are [s][t][Lk] with this call's Lk = min(topk, C).
+__device__ __forceinline__ size_t list_offset(int b, int S, int QH, int LkMax, int s, int t, int Lk) {
+  return (size_t)b * S * QH * LkMax + ((size_t)s * QH + t) * Lk;
 }
 
 struct DevicePlan {
@@ -655,45 +692,48 @@ struct DevicePlan {
 // Wave-uniform: every lane of every wave computes the same plan. Lane l reads the lengths
 // of rows l, l+64, ... (rows past the first 64 are read again in the second pass; they are
 // cache hits); sums, the longest-row bound and prefix sums are ballots, without LDS. Block
-// counts are at most 4096 (13 bits) and split counts at most 64 (7 bits).
+// counts are at most 4096 (13 bits) and split counts at most 256 (9 bits).
 __device__ __forceinline__ int device_blocks(const int32_t* lens, int batch, int W, int r) {
   return r < batch ? (row_tokens(lens, r, W) + kBlock - 1) / kBlock : 0;
 }
 
 // The split width C of the device plan (the same in every lane); nb0 = this lane's row's
-// block count, device_blocks(lens, batch, W, lane).
-__device__ __forceinline__ int device_split_width(const int32_t* lens, int batch, int W, int lane, int nb0) {
+// block count, device_blocks(lens, batch, W, lane). A row fits C = 4 << t when it has at
+// most lim.blocks[t] blocks.
+__device__ __forceinline__ int device_split_width(const int32_t* lens, int batch, int W, int lane, int nb0,
+                                                  const SplitLimits& lim) {
   auto blocks = [&](int r) { return device_blocks(lens, batch, W, r); };
   int N = 0;
-  bool over[5] = {false, false, false, false, false};  // a row needs more than 64 splits of 4 << t blocks
+  bool over[5] = {false, false, false, false, false};  // a row does not fit splits of 4 << t blocks
   for (int r0 = 0; r0 < batch; r0 += 64) {
     const int nb = r0 == 0 ? nb0 : blocks(r0 + lane);
     N += wave_sum_bits<13>(nb);
 #pragma unroll
-    for (int t = 0; t < 5; ++t) over[t] = over[t] || __ballot(nb > (kDeviceMaxSplits << (2 + t))) != 0;
+    for (int t = 0; t < 5; ++t) over[t] = over[t] || __ballot(nb > lim.blocks[t]) != 0;
   }
   int C_min = 4;
 #pragma unroll
   for (int t = 0; t < 5; ++t) C_min = over[t] ? (4 << (t + 1)) : C_min;
-  return min(max(pow2_ceil_dev(max(1, (N + kDeviceTarget - 1) / kDeviceTarget)), C_min), kMaxSplitBlocks);
+  return min(max(pow2_at_least(max(1, (N + kDeviceTarget - 1) / kDeviceTarget)), C_min), kMaxSplitBlocks);
 }
 
-__device__ __forceinline__ DevicePlan device_plan(const int32_t* lens, int batch, int W, int g, int lane) {
+__device__ __forceinline__ DevicePlan device_plan(const int32_t* lens, int batch, int W,
+                                                  const SplitLimits& lim, int g, int lane) {
   auto blocks = [&](int r) { return device_blocks(lens, batch, W, r); };
   const int nb0 = blocks(lane);
-  const int C = device_split_width(lens, batch, W, lane, nb0);
+  const int C = device_split_width(lens, batch, W, lane, nb0, lim);
   int base = 0;
   for (int r0 = 0; r0 < batch; r0 += 64) {
     const int r = r0 + lane;
     const int nb = r0 == 0 ? nb0 : blocks(r);
     const int cnt = r < batch ? max(1, (nb + C - 1) / C) : 0;
-    const int first = base + wave_prefix_small<7>(cnt);
+    const int first = base + wave_prefix_small<9>(cnt);
     const uint64_t hit = __ballot(r < batch && g >= first && g < first + cnt);
     if (hit) {
       const int l = __builtin_ctzll(hit);
       return DevicePlan{C, r0 + l, g - __builtin_amdgcn_readlane(first, l), true};
     }
-    base += wave_sum_bits<7>(cnt);
+    base += wave_sum_bits<9>(cnt);
   }
   return DevicePlan{C, 0, 0, false};
 }
@@ -729,7 +769,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int s = blockIdx.x, b = blockIdx.y, C = a.C;
   if (MODE == kFused && a.device_plan) {
-    const DevicePlan dp = device_plan(a.lens, a.batch, a.W, blockIdx.x, lane);
+    const DevicePlan dp = device_plan(a.lens, a.batch, a.W, a.lim, blockIdx.x, lane);
     if (!dp.active) return;
     s = dp.s;
     b = dp.b;
@@ -805,7 +845,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
   key = sort_desc_first(key, lane, n);
   // Agent-scope atomic stores: written through to the device-coherent level, so the
   // row's last workgroup can read them from any XCD without an L2 writeback.
-  uint64_t* out = a.keys + ((size_t)(b * a.S + s) * kHeads + h) * Lk;
+  uint64_t* out = a.keys + list_offset(b, a.S, kHeads, a.Lk, s, h, Lk);
   if (lane < Lk) __hip_atomic_store(out + lane, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // Publish this workgroup's lists and count it in. Every wave waits until its list
@@ -831,10 +871,10 @@ __global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
   // head h's lists straight from it with the network; otherwise the lists are staged in
   // LDS, each workgroup's four lists with one pad key after them so that lanes reading
   // list s (stride 4 Lk + 1 keys) fall on different banks.
-  const uint64_t* row_keys = a.keys + (size_t)b * a.S * kHeads * Lk;
+  const uint64_t* row_keys = a.keys + list_offset(b, a.S, kHeads, a.Lk, 0, 0, Lk);
   const int m = min(a.topk, nb);
   uint64_t mine;
-  if (ns <= 64 && a.topk <= kNetworkMaxM) {
+  if (network_fits(ns, Lk, a.topk)) {
     mine = merge_top16(row_keys + h * Lk, (size_t)kHeads * Lk, ns, Lk, lane);
   } else {
     const int row_len = kHeads * Lk, stride = row_len + 1;
@@ -859,6 +899,7 @@ struct MergeArgs {
   int32_t W, Q, S, C, Lk, topk;
   int32_t batch;
   int32_t device_plan;  // C (and Lk = min(topk, C)) chosen on the device, as the split pass did
+  SplitLimits lim;
   const uint64_t* keys;
   int32_t* out_ids;     // [batch][Q][4][topk]
   float* out_scores;
@@ -882,13 +923,13 @@ __global__ __launch_bounds__(64) void merge_kernel(MergeArgs a) {
   const int Lp = causal_len(L, a.Q, p);
   const int m = min(a.topk, (Lp + kBlock - 1) / kBlock);
   const int C = a.device_plan ? device_split_width(a.lens, a.batch, a.W, lane,
-                                                   device_blocks(a.lens, a.batch, a.W, lane))
+                                                   device_blocks(a.lens, a.batch, a.W, lane), a.lim)
                               : a.C;
   const int ns = (nb + C - 1) / C;
   const int Lk = a.device_plan ? min(a.topk, C) : a.Lk, stride = Lk + 1, QH = a.Q * kHeads;
-  const uint64_t* src = a.keys + ((size_t)b * a.S * QH + task) * Lk;
+  const uint64_t* src = a.keys + list_offset(b, a.S, QH, a.Lk, 0, task, Lk);
   uint64_t mine;
-  if (ns <= 64 && a.topk <= kNetworkMaxM) {
+  if (network_fits(ns, Lk, a.topk)) {
     mine = merge_top16(src, (size_t)QH * Lk, ns, Lk, lane);
   } else {
     stage_keys(src, lk, ns * Lk, lane, 64, [Lk, QH](int e) { return (e / Lk) * QH * Lk + e % Lk; },
@@ -1050,6 +1091,7 @@ struct VerifyArgs {
   int32_t Q, S, C, Lk, topk, n_init, n_local;
   int32_t batch;
   int32_t device_plan;  // split modes: C and each workgroup's (row, split) chosen on the device
+  SplitLimits lim;
   uint64_t* keys;       // [batch][S][Q*4][Lk]
   uint32_t* err;        // device error word (may be null)
   float* scores;        // [batch][Q][4][W] (block-score mode)
@@ -1075,7 +1117,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   const int g = lane >> 4;
   int s = blockIdx.x, b = blockIdx.y, C = a.C, Lk = a.Lk;
   if (MODE != kScores && a.device_plan) {
-    const DevicePlan dp = device_plan(a.lens, a.batch, a.W, blockIdx.x, lane);
+    const DevicePlan dp = device_plan(a.lens, a.batch, a.W, a.lim, blockIdx.x, lane);
     if (!dp.active) return;
     s = dp.s;
     b = dp.b;
@@ -1211,7 +1253,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     const bool real = lane < n && jj < nbp;
     uint64_t key = real ? make_key(sc[lane][4 * p + h], jj, jj < a.n_init || jj >= nbp - a.n_local) : 0;
     key = sort_desc_first(key, lane, n);
-    uint64_t* out = a.keys + ((size_t)(b * a.S + s) * a.Q * kHeads + 4 * p + h) * Lk;
+    uint64_t* out = a.keys + list_offset(b, a.S, a.Q * kHeads, a.Lk, s, 4 * p + h, Lk);
     if (MODE == kFused) {
       if (lane < Lk) __hip_atomic_store(out + lane, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     } else {
@@ -1234,7 +1276,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   if (!s_last) return;
   if (threadIdx.x == 0) __hip_atomic_store(row_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int msel = min(a.topk, nb);
-  const uint64_t mine = merge_top16(a.keys + ((size_t)b * a.S * kHeads + h) * Lk, (size_t)kHeads * Lk,
+  const uint64_t mine = merge_top16(a.keys + list_offset(b, a.S, kHeads, a.Lk, 0, h, Lk), (size_t)kHeads * Lk,
                                     ns, Lk, lane);
   const size_t o = ((size_t)b * kHeads + h) * a.topk;
   write_selection(mine, msel, a.topk, lane, a.out_ids + o, a.out_scores + o);
@@ -1290,11 +1332,11 @@ int32_t make_plan(int32_t batch, int32_t W, int32_t topk, int32_t num_splits, Pl
 }
 
 // The plan of msa_indexer_decode and of the multi-token and FP8 calls: with num_splits = 0,
-// 0 < W <= 64 * 64, topk <= 16 and batch * W >= kDeviceMinBlocks the device plan (at most
-// min(64, ceil(W/4)) splits per row, Lk <= topk keys per split and head, a grid that covers
-// any lengths: with C >= N/512 and C >= 4 the rows need at most N/C + batch <= 512 + batch
-// workgroups, or ceil(batch*W/64) + batch when C is held at 64); otherwise the host plan
-// above.
+// 0 < W <= 64 * 64, topk <= 16 and batch * W >= kDeviceMinBlocks the device plan (S =
+// min(64, ceil(W/4)) sizes the workspace at S * topk keys per row and head; a row takes at
+// most device_max_splits(C, S, topk) splits, at most ceil(W/4) in all; a grid that covers any
+// lengths: with C >= N/512 the rows need at most N/C + batch <= 512 + batch workgroups, or
+// ceil(batch*W/64) + batch when C is held at 64); otherwise the host plan above.
 int32_t make_decode_plan(int32_t batch, int32_t W, int32_t topk, int32_t num_splits, Plan* p) {
   int32_t rc = make_plan(batch, W, topk, num_splits, p);
   if (rc != MSA_OK) return rc;
@@ -1378,6 +1420,7 @@ SplitArgs make_split_args(const void* q, const void* k, const int32_t* bt, const
   a.n_local = n_local;
   a.batch = batch;
   a.device_plan = p.device ? 1 : 0;
+  a.lim = split_limits(p.S, topk);
   char* w = static_cast<char*>(ws);
   a.err = w ? reinterpret_cast<uint32_t*>(w) : nullptr;
   a.counters = w ? reinterpret_cast<uint32_t*>(w + kHeaderBytes) : nullptr;
@@ -1439,6 +1482,7 @@ int32_t launch_merge(const uint64_t* keys, const int32_t* lens, int32_t W, int32
   a.out_tokens = out_tokens;
   a.batch = batch;
   a.device_plan = p.device ? 1 : 0;
+  a.lim = split_limits(p.S, topk);
   hipLaunchKernelGGL(merge_kernel, dim3(Q * kHeads, batch), dim3(64), merge_lds_bytes(p.S, p.Lk, topk), st, a);
   return hipGetLastError() == hipSuccess ? MSA_OK : MSA_ERR_HIP;
 }
@@ -1496,6 +1540,7 @@ VerifyArgs make_verify_args(const void* q, const void* k, const int32_t* bt, con
   a.out_scores = nullptr;
   a.batch = batch;
   a.device_plan = p.device ? 1 : 0;
+  a.lim = split_limits(p.S, topk);
   return a;
 }
 

@@ -1,7 +1,8 @@
 """GPU parity of the device plan: with num_splits = 0 (W <= 4096, topk <= 16, batch * W at
-least 8192 blocks) the fused
-single-token pass picks the split width and each workgroup's (row, split) on the device from
-the row lengths (about 512 workgroups in all, at most 64 splits per row). Scores do not depend
+least 8192 blocks) the fused single-token pass, and the multi-token and FP8 passes, pick the
+split width C and each workgroup's (row, split) on the device from the row lengths (about 512
+workgroups in all; a row may have as many splits as its lists fit the workspace and the merge
+network: at topk 16, 256 splits of 4 blocks, 128 of 8, or 64 of 16..64). Scores do not depend
 on the plan, so the selection must equal the oracle's selection on the GPU's own block scores,
 and the oracle's within the near-tie rule; exact-integer data must match bit for bit."""
 import numpy as np
@@ -50,7 +51,7 @@ def test_many_rows_cross_the_wave_scan(msa):
 
 def test_long_row_among_empty_rows(msa):
     # One 1024-block row and 47 empty rows: each empty row still gets a workgroup for its
-    # padding, and the long row gets 64 splits.
+    # padding, and the long row gets 256 splits of 4 blocks.
     lens = [0] * 48
     lens[17] = 128 * 1024
     inp = synth.paged_case(402, lens, 1024)
@@ -116,3 +117,32 @@ def test_split_width_changes_between_graph_replays(msa):
         gpu_s = msa.msa_indexer_block_scores(q, k, bt, lens).cpu().numpy()
         check_selection_exact_given_scores(ids.cpu().numpy(), sc.cpu().numpy(), gpu_s, cur.seq_lens,
                                            16, 1, 2)
+
+
+# Rows at the edges of the per-row split limit (topk 16: C = 4 up to 1024 blocks, then C = 32
+# up to 2048 and C = 64 up to 4096; topk 8: C = 16 up to 1024 blocks; topk 4: C = 4 up to 256
+# blocks, C = 8 up to 512), for the single-token, multi-token and FP8 passes.
+EDGE_CASES = [
+    ("c4-256-splits", 1024, [128 * 1024, 1, 0, 128 * 1023 + 5, 7, 128 * 3, 129, 2], 16),
+    ("c32-33-splits", 2048, [128 * 1024 + 1, 3, 128 * 700, 0], 16),
+    ("c32-64-splits", 2048, [128 * 2048, 128 * 2047 + 1, 5, 128 * 1025], 16),
+    ("c64", 4096, [128 * 2048 + 1, 5], 16),
+    ("topk8-c16", 1024, [128 * 1024, 128 * 513, 9, 0, 128 * 512, 1, 2, 3], 8),
+    ("topk4-c8", 1024, [128 * 512, 128 * 257, 9, 0, 128 * 256, 1, 2, 3], 4),
+]
+
+
+@pytest.mark.parametrize("name,W,lens,topk", EDGE_CASES, ids=[c[0] for c in EDGE_CASES])
+def test_split_limit_edges_single_token(msa, name, W, lens, topk):
+    inp = synth.paged_case(410, lens, W, poison=False, topk=topk)
+    check(msa, inp)
+
+
+@pytest.mark.parametrize("name,W,lens,topk", EDGE_CASES, ids=[c[0] for c in EDGE_CASES])
+def test_split_limit_edges_multi_and_fp8(msa, name, W, lens, topk):
+    from test_gpu_fp8 import run_fp8
+    from test_gpu_multi import run_multi
+
+    assert msa.plan(len(lens), W, topk)["blocks_per_split"] == 0
+    run_multi(msa, synth.multi_case(411, lens, W, 4, poison=False, topk=topk))
+    run_fp8(msa, synth.fp8_case(412, lens, W, 1, k_scale=0.5, poison=False, topk=topk), 1e-3 * 4.0 * 0.5)
