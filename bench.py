@@ -275,6 +275,59 @@ def bench_sweep(msa, np, torch) -> int:
     return 0
 
 
+def bench_shard(args, msa, synth, np, torch) -> int:
+    """One GPU's share of the benchmark workload under P-way context parallelism (round-robin
+    blocks j = local * P + rank, vLLM PR #57832, Solution): for each rank, the decode call on
+    its share of the batch 32 x 128K cache (bf16, or FP8 with --fp8, the cache the pages'
+    four-GPU figures use) under the graph protocol, one JSON line per rank.
+    The cache stays whole and resident (each rank holds it replicated); a rank reads 1/P of
+    it. The gathers of q and of the per-rank lists are not part of this single-GPU build."""
+    from sparse_attention_block_amd import shard
+    P = args.shard
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    kind = "FP8 E4M3" if args.fp8 else "bf16"
+    log(f"generating the batch 32 x 131072 workload ({kind} index-K) for {P} ranks")
+    inp = synth.fp8_config(1) if args.fp8 else synth.config3()
+    q = torch.from_numpy(np.ascontiguousarray(inp.q).view(np.int16)).to(dev).view(torch.bfloat16)
+    if args.fp8:
+        k = torch.from_numpy(inp.k_cache).to(dev)
+    else:
+        k = torch.from_numpy(inp.k_cache.view(np.int16)).to(dev).view(torch.bfloat16)
+    B = inp.batch
+    elem = 1 if args.fp8 else 2
+    for r in range(P):
+        bt_np, lens_np, ni, nl = shard.rank_share(inp.block_table, inp.seq_lens, P, r,
+                                                  inp.n_init, inp.n_local)
+        W = bt_np.shape[1]
+        bt = torch.from_numpy(bt_np).to(dev)
+        lens = torch.from_numpy(lens_np).to(dev)
+        if args.fp8:
+            ws = torch.zeros(msa.workspace_bytes_multi(B, W, 1, inp.topk), dtype=torch.uint8, device=dev)
+            ids = torch.empty((B, 1, 4, inp.topk), dtype=torch.int32, device=dev)
+            sc = torch.empty((B, 1, 4, inp.topk), dtype=torch.float32, device=dev)
+            fn = lambda: msa.msa_indexer_decode_fp8(q, k, inp.k_scale, bt, lens, inp.topk, ni, nl,
+                                                    out_ids=ids, out_scores=sc, workspace=ws)
+        else:
+            ws = msa.new_workspace(B, W, inp.topk, 0, dev)
+            ids = torch.empty((B, 4, inp.topk), dtype=torch.int32, device=dev)
+            sc = torch.empty((B, 4, inp.topk), dtype=torch.float32, device=dev)
+            fn = lambda: msa.msa_indexer_decode(q, k, bt, lens, inp.topk, ni, nl, out_ids=ids,
+                                                out_scores=sc, workspace=ws)
+        us = graph_us_per_call(torch, fn)
+        nbytes = int(lens_np.astype(np.int64).sum()) * 128 * elem
+        gbs = nbytes / (us * 1e-6) / 1e9
+        print(json.dumps({"workload": f"rank {r} of {P}: batch 32 x {int(lens_np[0])} tokens "
+                                      f"(every {P}th block of the 131072-token rows, {kind} index-K)",
+                          "rank": r, "ranks": P, "n_init": ni, "n_local": nl,
+                          "index_k_bytes": nbytes, "us_per_call": round(us, 2),
+                          "GBs": round(gbs, 1), "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+                          "plan": msa.plan(B, W, inp.topk),
+                          "protocol": "8 calls per HIP graph, 100 replays per round, median of 7 rounds"}),
+              flush=True)
+    return 0
+
+
 def bench_multi(args, msa, synth, np, torch) -> int:
     """Multi-token decode step (qlen draft positions per row) over the benchmark's cache."""
     Q = args.qlen
@@ -404,6 +457,9 @@ def main() -> int:
     ap.add_argument("--sweep", action="store_true",
                     help="time the decode call (bf16 and FP8 caches) over a batch x context grid "
                          "instead of the benchmark step")
+    ap.add_argument("--shard", type=int, default=0, metavar="P",
+                    help="time each rank's share of the benchmark workload under P-way context "
+                         "parallelism (round-robin blocks), on this one GPU")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip timing the page-table entry points")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -436,6 +492,8 @@ def main() -> int:
         return bench_configs(msa, synth, np, torch)
     if args.sweep:
         return bench_sweep(msa, np, torch)
+    if args.shard:
+        return bench_shard(args, msa, synth, np, torch)
     if args.qlen != 1 or args.fp8:
         return bench_multi(args, msa, synth, np, torch)
     log("generating the batch 32 x 131072 workload (1 GiB of bf16 index-K)")
