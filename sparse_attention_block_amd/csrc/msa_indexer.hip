@@ -1107,7 +1107,7 @@ struct VerifyArgs {
 // merge_top16 holds in at most 4 registers): kSplit, then the row's last workgroup merges
 // the lists as split_kernel does.
 template <int MODE, bool FP8>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void verify_kernel(VerifyArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void verify_kernel(VerifyArgs a) {
   using G = KvGeom<FP8>;
   __shared__ float sc[kMaxSplitBlocks][16];
   __shared__ uint4 stage[kWaves * kChunkSlots];  // one 8 KiB chunk region per wave
@@ -1205,15 +1205,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   };
   auto page_ptr = [&](const Cursor& u) { return a.k + (size_t)u.page * G::kPageBytes; };
 
-  // Two register buffers, two chunks in flight: the chunk in buffer A (landed) is copied to
-  // LDS, A is refilled at once with the chunk two ahead, and the MFMAs of the copied chunk
-  // run while that chunk and the next one (buffer B) are loading.
+  // Three register buffers, three chunks in flight: the chunk in the oldest buffer (landed)
+  // is copied to LDS, that buffer is refilled at once with the chunk three ahead, and the
+  // MFMAs of the copied chunk run while the next two chunks and that one are loading.
   float m[kHeads];
 #pragma unroll
   for (int h = 0; h < kHeads; ++h) m[h] = -__builtin_inff();
-  auto process = [&](const Cursor& cur, uint4 (&A)[kChunkLoads], const Cursor& ahead2) {
+  auto process = [&](const Cursor& cur, uint4 (&A)[kChunkLoads], const Cursor& ahead) {
     chunk_to_lds<FP8>(region, A, lane);
-    if (ahead2.j < j1) chunk_load(page_ptr(ahead2), ahead2.c, lane, A);
+    if (ahead.j < j1) chunk_load(page_ptr(ahead), ahead.c, lane, A);
     chunk_mfma<FP8>(region, Lg - cur.j * kBlock - cur.c * G::kChunkTokens, qr, lane, m);
     if (cur.c + 1 == cur.nch) {
 #pragma unroll
@@ -1225,19 +1225,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   };
   Cursor c0 = first();
   if (c0.j < j1) {
-    Cursor c1 = advance(c0);
-    uint4 A[kChunkLoads], B[kChunkLoads];
+    Cursor c1 = advance(c0), c2 = advance(c1);
+    uint4 A[kChunkLoads], B[kChunkLoads], D[kChunkLoads];
     chunk_load(page_ptr(c0), c0.c, lane, A);
     if (c1.j < j1) chunk_load(page_ptr(c1), c1.c, lane, B);
-    while (true) {  // two chunks per trip so that A and B trade roles without copies
-      Cursor c2 = advance(c1);
-      process(c0, A, c2);
-      if (c1.j >= j1) break;
+    if (c2.j < j1) chunk_load(page_ptr(c2), c2.c, lane, D);
+    while (true) {  // three chunks per trip so that the buffers rotate without copies
       Cursor c3 = advance(c2);
-      process(c1, B, c3);
+      process(c0, A, c3);
+      if (c1.j >= j1) break;
+      Cursor c4 = advance(c3);
+      process(c1, B, c4);
       if (c2.j >= j1) break;
-      c0 = c2;
-      c1 = c3;
+      Cursor c5 = advance(c4);
+      process(c2, D, c5);
+      if (c3.j >= j1) break;
+      c0 = c3;
+      c1 = c4;
+      c2 = c5;
     }
   }
   if (MODE == kScores) return;
