@@ -909,7 +909,8 @@ struct MergeArgs {
   int32_t* out_tokens;
 };
 
-// LDS for the lists when merge_rounds runs (more than 64 splits or topk above 16).
+// LDS for the lists when merge_rounds may run: topk above 16, or more than 64 splits (with
+// at most 64 splits and topk <= 16 the lists always fit merge_top16).
 size_t merge_lds_bytes(int S, int Lk, int topk) {
   return S <= 64 && topk <= kNetworkMaxM ? 0 : (size_t)S * (Lk + 1) * sizeof(uint64_t);
 }
@@ -1362,7 +1363,7 @@ size_t keys_offset(int32_t batch) {
   return kHeaderBytes + (size_t)batch * kCounterStride * sizeof(uint32_t);
 }
 
-// LDS for the fused merge when merge_rounds runs (more than 64 splits or topk above 16).
+// LDS for the fused merge when merge_rounds may run (as merge_lds_bytes, for all four heads).
 size_t fused_lds_bytes(const Plan& p, int topk) {
   return p.S <= 64 && topk <= kNetworkMaxM ? 0 : (size_t)p.S * (kHeads * p.Lk + 1) * sizeof(uint64_t);
 }
@@ -1557,7 +1558,7 @@ bool valid_scale(float k_scale) { return k_scale > 0.0f && k_scale <= 3.40282346
 // runs every (row, head) at once (FP8 at batch 32 x 128K: 32 lists of 16, 89.8 vs 88.7 us).
 bool fuse_verify(const Plan& p, int topk) {
   if (p.S > 64 || topk > kNetworkMaxM) return false;
-  if (p.device) return true;  // at most 64 splits per row; the row's own count is only known on the device
+  if (p.device) return true;  // the device plan keeps every row's lists within merge_top16
   int lk2 = 1;
   while (lk2 < p.Lk) lk2 <<= 1;
   return ceil_div(p.S, 64 / lk2) <= 4;

@@ -72,7 +72,8 @@ def test_split_plan(lib):
 def test_workspace_size(lib):
     ws = lib.msa_indexer_workspace_bytes
     # error word (256 B), one 256-byte counter line per row, then the keys: the larger of the
-    # device plan (up to 64 splits x topk keys per head) and the host plan (the stage calls)
+    # device plan (S = min(64, ceil(W/4)) lists of topk keys per row and head, which any of
+    # its split widths fits) and the host plan (the stage calls)
     assert ws(32, 1024, 16, 0) == 256 + 32 * 256 + 32 * 64 * 4 * 16 * 8
     assert ws(32, 1024, 16, 32) == 256 + 32 * 256 + 32 * 32 * 4 * 16 * 8
     # small tables (batch * W < 8192 blocks) keep the host plan: 4-block splits keep 4 keys
@@ -264,7 +265,7 @@ def test_decode_multi_workspace_and_no_op(lib):
     ws = lib.msa_indexer_workspace_bytes_multi
     # header, counter lines, then keys [batch][S][qlen*4][Lk]: 8 blocks -> 2 splits of 4, Lk 4
     assert ws(2, 8, 4, 16, 0) == 256 + 2 * 256 + 2 * 2 * 16 * 4 * 8
-    # with num_splits = 0 the device plan (up to 64 splits per row, Lk <= topk) bounds the size
+    # with num_splits = 0 the device plan (S = 64 list slots of topk keys per row and head)
     assert ws(32, 1024, 4, 16, 0) == 256 + 32 * 256 + 32 * 64 * 16 * 16 * 8
     assert ws(32, 1024, 1, 16, 0) == 256 + 32 * 256 + 32 * 64 * 4 * 16 * 8
     assert ws(32, 1024, 4, 16, 32) == 256 + 32 * 256 + 32 * 32 * 16 * 16 * 8
