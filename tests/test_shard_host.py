@@ -52,3 +52,36 @@ def test_rows_needing_different_pins_are_refused():
     lens = np.array([128 * 8, 128 * 7], dtype=np.int32)   # rank 3 holds block 7 of row 0 only
     with pytest.raises(ValueError):
         shard.rank_share(bt, lens, 4, 3, 1, 2)
+
+
+@pytest.mark.parametrize("P", [2, 3, 4])
+@pytest.mark.parametrize("L", [128 * 12, 128 * 11 + 40, 128 * 5 + 1])
+def test_oracle_on_the_shares_merges_to_the_oracle_on_the_rows(P, L):
+    # The pages' exactness argument, run with the oracle: each rank's top-k of its share
+    # (pins on the shard), merged per head with pins first, equals the top-k of the rows.
+    import oracle
+    from sparse_attention_block_amd import synth
+
+    B, W, topk, n_init, n_local = 3, 12, 4, 1, 2
+    inp = synth.paged_case(600 + P, [L] * B, W, poison=False, topk=topk, n_init=n_init,
+                           n_local=n_local)
+    want_ids, want_sc, _ = oracle.decode(inp)
+    nb = -(-L // 128)
+    cands = [[[] for _ in range(4)] for _ in range(B)]
+    for r in range(P):
+        bt_r, lens_r, ni, nl = shard.rank_share(inp.block_table, inp.seq_lens, P, r, n_init, n_local)
+        sub = synth.Inputs("share", inp.q, inp.k_cache, bt_r, lens_r, topk=topk, n_init=ni,
+                           n_local=nl)
+        ids, sc, _ = oracle.decode(sub)
+        gids = shard.global_ids(ids, P, r)
+        for b in range(B):
+            for h in range(4):
+                cands[b][h] += [(int(j), float(s)) for j, s in zip(gids[b, h], sc[b, h]) if j >= 0]
+    for b in range(B):
+        for h in range(4):
+            pinned = lambda j: j < n_init or j >= nb - n_local
+            got = sorted(cands[b][h], key=lambda c: (not pinned(c[0]), -c[1], c[0]))[:min(topk, nb)]
+            m = len(got)
+            assert [j for j, _ in got] == list(want_ids[b, h, :m])
+            assert [s for _, s in got] == list(want_sc[b, h, :m])
+            assert np.all(want_ids[b, h, m:] == -1)
