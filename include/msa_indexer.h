@@ -58,7 +58,7 @@ extern "C" {
 #define MSA_OK 0
 #define MSA_ERR_INVALID_ARG (-1)         /* null/misaligned pointer, bad size or parameter */
 #define MSA_ERR_WORKSPACE_TOO_SMALL (-2) /* workspace_bytes < msa_indexer_workspace_bytes(...) */
-#define MSA_ERR_UNSUPPORTED (-3)         /* shape beyond what this build handles */
+#define MSA_ERR_UNSUPPORTED (-3)         /* shape beyond what the library handles */
 #define MSA_ERR_HIP (-4)                 /* the HIP runtime refused a launch */
 
 /* Fixed model geometry (SGLang PR #41488, Modifications). */
@@ -66,7 +66,7 @@ extern "C" {
 #define MSA_HEAD_DIM 128
 #define MSA_BLOCK_TOKENS 128
 
-/* Limits of this build. */
+/* Limits of the library. */
 #define MSA_MAX_TOPK 64
 #define MSA_MAX_BLOCKS_PER_SEQ 16384     /* 2M tokens per row */
 #define MSA_MAX_QUERY_LEN 4              /* query positions per row in the multi-token calls */
