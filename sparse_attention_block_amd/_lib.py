@@ -116,7 +116,10 @@ def num_splits(batch: int, max_blocks: int, topk: int, splits: int = 0) -> int:
 
 
 def plan(batch: int, max_blocks: int, topk: int, splits: int = 0) -> dict:
-    """The library's plan: splits per row, blocks per split, candidates kept, fused merge."""
+    """The library's plan (msa_indexer_plan): splits per row, blocks per split, candidates
+    kept per split and head, fused merge. blocks_per_split = 0 marks the device plan, whose
+    split width is chosen per call from seq_lens; splits is then the list capacity per row
+    (the workspace holds splits * topk keys per row and head)."""
     out = [ctypes.c_int32() for _ in range(4)]
     rc = load().msa_indexer_plan(batch, max_blocks, topk, splits, *[ctypes.byref(o) for o in out])
     _check("msa_indexer_plan", rc)
