@@ -7,6 +7,7 @@ library is missing, or a tensor is not a suitable device tensor, the call raises
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 import re
 
@@ -154,6 +155,27 @@ def _dev(t, name, dtype, shape=None):
     return _P(t.data_ptr())
 
 
+def _on_tensor_device(fn):
+    """Runs a call with the device of its tensors current, so that its default stream and
+    the stream the kernels go to are that device's. Tensors on several devices, or a stream
+    of another device, are refused (a kernel would be handed another device's memory)."""
+    @functools.wraps(fn)
+    def call(*args, **kwargs):
+        torch = _torch()
+        devs = {a.device for a in (*args, *kwargs.values()) if isinstance(a, torch.Tensor) and a.is_cuda}
+        if not devs:
+            return fn(*args, **kwargs)  # host tensors: the marshalling refuses them
+        if len(devs) > 1:
+            raise ValueError(f"{fn.__name__}: tensors on several devices: {sorted(map(str, devs))}")
+        dev = devs.pop()
+        stream = kwargs.get("stream")
+        if stream is not None and stream.device != dev:
+            raise ValueError(f"{fn.__name__}: stream of {stream.device}, tensors on {dev}")
+        with torch.cuda.device(dev):
+            return fn(*args, **kwargs)
+    return call
+
+
 def _stream(stream):
     torch = _torch()
     s = torch.cuda.current_stream() if stream is None else stream
@@ -208,6 +230,7 @@ def new_workspace(batch: int, max_blocks: int, topk: int, splits: int = 0, devic
     return torch.zeros(n, dtype=torch.uint8, device=device)
 
 
+@_on_tensor_device
 def msa_indexer_decode(q, k_cache, block_table, seq_lens, topk=16, n_init=1, n_local=2,
                        out_ids=None, out_scores=None, workspace=None, num_splits=0, stream=None,
                        engine=None):
@@ -234,6 +257,7 @@ def msa_indexer_decode(q, k_cache, block_table, seq_lens, topk=16, n_init=1, n_l
     return out_ids, out_scores
 
 
+@_on_tensor_device
 def msa_indexer_decode_pages(q, k_cache, block_table, seq_lens, topk=16, n_init=1, n_local=2,
                              out_ids=None, out_scores=None, out_pages=None, out_tokens=None,
                              workspace=None, num_splits=0, engine=ENGINE_DEFAULT, stream=None):
@@ -263,6 +287,7 @@ def msa_indexer_decode_pages(q, k_cache, block_table, seq_lens, topk=16, n_init=
     return out_ids, out_scores, out_pages, out_tokens
 
 
+@_on_tensor_device
 def msa_indexer_expand_pages(ids, block_table, seq_lens, out_pages=None, out_tokens=None,
                              stream=None):
     """16-token page table of given selections ids int32 [B,4,topk]: (out_pages, out_tokens)."""
@@ -304,6 +329,7 @@ def _inputs_multi(q, k_cache, block_table, seq_lens, kv_dtype=None):
     return ptrs, B, Q, block_table.shape[1], block_table.stride(0), k_cache.shape[0]
 
 
+@_on_tensor_device
 def msa_indexer_decode_multi(q, k_cache, block_table, seq_lens, topk=16, n_init=1, n_local=2,
                              out_ids=None, out_scores=None, workspace=None, num_splits=0,
                              stream=None):
@@ -326,6 +352,7 @@ def msa_indexer_decode_multi(q, k_cache, block_table, seq_lens, topk=16, n_init=
     return out_ids, out_scores
 
 
+@_on_tensor_device
 def msa_indexer_block_scores_multi(q, k_cache, block_table, seq_lens, num_splits=0, out=None,
                                    stream=None):
     """fp32 block scores [B, Q, 4, W] of the multi-token pass; -inf where a position sees no block."""
@@ -340,6 +367,7 @@ def msa_indexer_block_scores_multi(q, k_cache, block_table, seq_lens, num_splits
     return out
 
 
+@_on_tensor_device
 def msa_indexer_decode_fp8(q, k_cache, k_scale, block_table, seq_lens, topk=16, n_init=1,
                            n_local=2, out_ids=None, out_scores=None, workspace=None, num_splits=0,
                            stream=None):
@@ -364,6 +392,7 @@ def msa_indexer_decode_fp8(q, k_cache, k_scale, block_table, seq_lens, topk=16, 
     return out_ids, out_scores
 
 
+@_on_tensor_device
 def msa_indexer_block_scores_fp8(q, k_cache, k_scale, block_table, seq_lens, num_splits=0,
                                  out=None, stream=None):
     """fp32 block scores [B, Q, 4, W] over an FP8 E4M3 cache."""
@@ -379,6 +408,7 @@ def msa_indexer_block_scores_fp8(q, k_cache, k_scale, block_table, seq_lens, num
     return out
 
 
+@_on_tensor_device
 def msa_indexer_expand_pages_multi(ids, block_table, seq_lens, out_pages=None, out_tokens=None,
                                    stream=None):
     """16-token page tables of multi-token selections ids int32 [B,Q,4,topk]:
@@ -403,6 +433,7 @@ def msa_indexer_expand_pages_multi(ids, block_table, seq_lens, out_pages=None, o
     return out_pages, out_tokens
 
 
+@_on_tensor_device
 def msa_indexer_split_topk(q, k_cache, block_table, seq_lens, workspace, topk=16, n_init=1,
                            n_local=2, num_splits=0, engine=ENGINE_DEFAULT, stream=None):
     """Stage 1 alone: per-split top-k candidate keys into `workspace`."""
@@ -414,6 +445,7 @@ def msa_indexer_split_topk(q, k_cache, block_table, seq_lens, workspace, topk=16
     _check("msa_indexer_split_topk", rc)
 
 
+@_on_tensor_device
 def msa_indexer_merge(seq_lens, max_blocks, workspace, out_ids, out_scores, topk=16,
                       num_splits=0, stream=None):
     """Stage 2 alone: exact merge of the split candidates into out_ids / out_scores."""
@@ -427,6 +459,7 @@ def msa_indexer_merge(seq_lens, max_blocks, workspace, out_ids, out_scores, topk
     _check("msa_indexer_merge", rc)
 
 
+@_on_tensor_device
 def msa_indexer_block_scores(q, k_cache, block_table, seq_lens, num_splits=0,
                              engine=ENGINE_DEFAULT, out=None, stream=None):
     """fp32 block scores [B, 4, W]; -inf past each row's end."""
@@ -441,6 +474,7 @@ def msa_indexer_block_scores(q, k_cache, block_table, seq_lens, num_splits=0,
     return out
 
 
+@_on_tensor_device
 def msa_indexer_read_error(workspace, stream=None) -> int:
     """Device error bits of `workspace` (synchronizes the stream, then clears them)."""
     torch = _torch()

@@ -170,6 +170,32 @@ def test_edges(msa):
     assert ids.shape == (0, 4, 16)
 
 
+def test_shared_pages_break_ties_by_id(msa):
+    # Logical blocks backed by one physical page (prefix sharing) score bit for bit alike
+    # whichever split, wave or engine reads them, and equal scores go to the lower block id.
+    inp = synth.paged_case(112, [128 * 40, 128 * 40, 128 * 37 + 9], 40, poison=False)
+    bt = inp.block_table.copy()
+    bt[0, :] = bt[0, 0]
+    bt[1, :] = bt[1, np.arange(40) % 10]
+    bt[2, :20] = bt[1, :20]  # row 2 reads row 1's first 20 pages (with its own query)
+    shared = synth.Inputs("shared pages", inp.q, inp.k_cache, bt, inp.seq_lens)
+    ref = oracle.block_scores(shared.q, shared.k_cache, shared.block_table, shared.seq_lens)
+    q, k, btd, lens = to_device(shared)
+    for ns in feasible((0, 3, 10), 40):
+        for engine in ENGINES:
+            s = msa.msa_indexer_block_scores(q, k, btd, lens, num_splits=ns, engine=engine).cpu().numpy()
+            check_scores(s, ref)
+            assert np.all(s[0] == s[0, :, :1])
+            assert np.array_equal(s[1], s[1][:, np.arange(40) % 10])
+        ids, sc = msa.msa_indexer_decode(q, k, btd, lens, num_splits=ns)
+        ids, sc = ids.cpu().numpy(), sc.cpu().numpy()
+        for h in range(4):
+            assert list(ids[0, h]) == [0, 38, 39] + list(range(1, 14)), (ns, h)
+        s = msa.msa_indexer_block_scores(q, k, btd, lens, num_splits=ns).cpu().numpy()  # decode's engine
+        check_selection_exact_given_scores(ids, sc, s, shared.seq_lens, 16, 1, 2)
+        check_selection_vs_oracle(ids, ref, shared.seq_lens, 16, 1, 2)
+
+
 def test_out_of_range_page_is_flagged_not_read(msa):
     inp = synth.paged_case(108, [128 * 6, 128 * 6], 6)
     q, k, bt, lens = to_device(inp)

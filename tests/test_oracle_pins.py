@@ -225,6 +225,32 @@ def pin_negative_zero_ties_with_positive_zero(orc):
     assert list(ids[0, 0]) == [0, 1, 2, 3]
 
 
+@pin
+def pin_shared_pages_tie_by_id(orc):
+    # Logical blocks backed by one physical page (prefix sharing) score exactly alike, and
+    # equal scores go to the lower block id. Row 0 keeps every block on one page: the pins
+    # (0, 38, 39) come first in id order, then blocks 1 .. 13. Row 1 spreads 40 blocks over
+    # 10 pages (block j on page j % 10): of each page's copies the selection holds the ones
+    # with the lowest ids, and pinned copies aside, a copy is left out only after every
+    # lower-id copy of its page is in.
+    inp = synth.paged_case(51, [128 * 40, 128 * 40], 40, poison=False)
+    bt = inp.block_table.copy()
+    bt[0, :] = bt[0, 0]
+    bt[1, :] = bt[1, np.arange(40) % 10]
+    s = orc.block_scores(inp.q, inp.k_cache, bt, inp.seq_lens)
+    assert np.all(s[0] == s[0, :, :1])
+    assert np.array_equal(s[1], s[1][:, np.arange(40) % 10])
+    ids, _ = orc.select(s, inp.seq_lens, 16, 1, 2)
+    pinned = {0, 38, 39}
+    for h in range(4):
+        assert list(ids[0, h]) == [0, 38, 39] + list(range(1, 14))
+        sel = set(int(j) for j in ids[1, h])
+        for page in range(10):
+            copies = [j for j in range(page, 40, 10) if j not in pinned]
+            taken = [j in sel for j in copies]
+            assert taken == sorted(taken, reverse=True), (h, page, taken)
+
+
 def _check_invariants(ids, sc, scores, lens, topk, n_init, n_local):
     B = scores.shape[0]
     for b in range(B):
