@@ -498,20 +498,9 @@ __device__ __forceinline__ void sort_rows(uint64_t (&r)[16], int lg, int lane) {
   for (int t = 0; t < N; ++t) r[t] = bitonic_step<1, 1>(r[t], lane);
 }
 
-__device__ __forceinline__ uint64_t merge_top16(const uint64_t* __restrict__ lists, size_t list_stride,
-                                                int ns, int Lk, int lane) {
-  const int lg = Lk <= 1 ? 0 : Lk <= 2 ? 1 : Lk <= 4 ? 2 : Lk <= 8 ? 3 : 4;
-  const int per_reg = 64 >> lg;
-  const int R = (ns + per_reg - 1) / per_reg;  // registers that hold a list
-  const int e = lane & ((1 << lg) - 1), sub = lane >> lg;
-  uint64_t r[16];
-#pragma unroll
-  for (int t = 0; t < 16; ++t) {
-    const int sp = t * per_reg + sub;
-    r[t] = (t < R && sp < ns && e < Lk)
-               ? __hip_atomic_load(lists + sp * list_stride + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-               : 0;
-  }
+// The 16 largest keys of registers r[0 .. R) (R <= 16; the registers past R hold zeros),
+// whose 16-lane rows hold sorted runs of 2^lg keys: best first in lanes 0..15.
+__device__ __forceinline__ uint64_t network_top16(uint64_t (&r)[16], int R, int lg, int lane) {
   // Registers past R hold zeros: sorting or merging them changes nothing, so the stages
   // below run on power-of-two register counts without a branch per register.
   if (lg < 4) {  // several lists per row: sort each row first
@@ -529,6 +518,59 @@ __device__ __forceinline__ uint64_t merge_top16(const uint64_t* __restrict__ lis
   x = bitonic_clean16(umax64(x, partner_u64<31>(x)), lane);
   x = bitonic_clean16(umax64(x, partner_u64<63>(x)), lane);
   return x;
+}
+
+// The 16 largest keys of ns lists of Lk keys (each sorted best first, zero padded; list sp
+// at lists[sp * list_stride], written by split sp, which owns blocks [sp * C, sp * C + C)),
+// best first in lanes 0..15. Lists are padded to Lk2 = 2^ceil(log2 Lk) keys and 64 / Lk2
+// of them share a register: lane l of register t holds element l % Lk2 of list
+// t * 64 / Lk2 + l / Lk2.
+// Many short lists (more than 8 registers of lists of at most 8 keys, e.g. 256 splits of 4
+// blocks) are pruned first: the 16th largest list head is at most the 16th largest key (the
+// 16 best heads are 16 keys), and a list's keys are at most its head, so every key of the
+// top 16 lies in one of the 16 lists with the best heads. The heads (at most 256, 4
+// registers) are ranked first, and only those 16 lists (16 Lk2 keys, 1 or 2 registers) are
+// read and merged: a second round of loads, but about a third of the network's steps
+// (sorting 16 registers of short runs is its largest part). A head names its list: its
+// block id divided by C.
+__device__ __forceinline__ uint64_t merge_top16(const uint64_t* __restrict__ lists, size_t list_stride,
+                                                int ns, int Lk, int C, int lane) {
+  const int lg = Lk <= 1 ? 0 : Lk <= 2 ? 1 : Lk <= 4 ? 2 : Lk <= 8 ? 3 : 4;
+  const int per_reg = 64 >> lg;
+  const int R = (ns + per_reg - 1) / per_reg;  // registers that hold a list
+  const int e = lane & ((1 << lg) - 1);
+  uint64_t r[16];
+  if (lg < 4 && R > 8) {
+    const int RH = (ns + 63) / 64;  // registers of list heads, one head per lane
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int sp = t * 64 + lane;
+      r[t] = (t < RH && sp < ns)
+                 ? __hip_atomic_load(lists + sp * list_stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                 : 0;
+    }
+    const uint64_t head = network_top16(r, RH, 0, lane);
+    const int src = head != 0 ? key_id(head) / C : -1;  // lane i < 16: the list of the i-th best head
+    const int R2 = max(1, (16 << lg) / 64);             // registers of the 16 lists' keys
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int i = (t * 64 + lane) >> lg;  // rank of the list this slot holds
+      const int sp = t < R2 ? __shfl(src, i & 15) : -1;
+      r[t] = (t < R2 && i < 16 && e < Lk && sp >= 0)
+                 ? __hip_atomic_load(lists + sp * list_stride + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                 : 0;
+    }
+    return network_top16(r, R2, lg, lane);
+  }
+  const int sub = lane >> lg;
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    const int sp = t * per_reg + sub;
+    r[t] = (t < R && sp < ns && e < Lk)
+               ? __hip_atomic_load(lists + sp * list_stride + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+               : 0;
+  }
+  return network_top16(r, R, lg, lane);
 }
 
 __device__ __forceinline__ void write_selection(uint64_t mine, int m, int topk, int lane,
@@ -875,7 +917,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
   const int m = min(a.topk, nb);
   uint64_t mine;
   if (network_fits(ns, Lk, a.topk)) {
-    mine = merge_top16(row_keys + h * Lk, (size_t)kHeads * Lk, ns, Lk, lane);
+    mine = merge_top16(row_keys + h * Lk, (size_t)kHeads * Lk, ns, Lk, C, lane);
   } else {
     const int row_len = kHeads * Lk, stride = row_len + 1;
     stage_keys(row_keys, lk, ns * row_len, threadIdx.x, kThreads, [](int e) { return e; },
@@ -931,7 +973,7 @@ __global__ __launch_bounds__(64) void merge_kernel(MergeArgs a) {
   const uint64_t* src = a.keys + list_offset(b, a.S, QH, a.Lk, 0, task, Lk);
   uint64_t mine;
   if (network_fits(ns, Lk, a.topk)) {
-    mine = merge_top16(src, (size_t)QH * Lk, ns, Lk, lane);
+    mine = merge_top16(src, (size_t)QH * Lk, ns, Lk, C, lane);
   } else {
     stage_keys(src, lk, ns * Lk, lane, 64, [Lk, QH](int e) { return (e / Lk) * QH * Lk + e % Lk; },
                [Lk, stride](int e) { return (e / Lk) * stride + e % Lk; });
@@ -1283,7 +1325,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   if (threadIdx.x == 0) __hip_atomic_store(row_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int msel = min(a.topk, nb);
   const uint64_t mine = merge_top16(a.keys + list_offset(b, a.S, kHeads, a.Lk, 0, h, Lk), (size_t)kHeads * Lk,
-                                    ns, Lk, lane);
+                                    ns, Lk, C, lane);
   const size_t o = ((size_t)b * kHeads + h) * a.topk;
   write_selection(mine, msel, a.topk, lane, a.out_ids + o, a.out_scores + o);
 }
