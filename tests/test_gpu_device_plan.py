@@ -129,6 +129,11 @@ EDGE_CASES = [
     ("c64", 4096, [128 * 2048 + 1, 5], 16),
     ("topk8-c16", 1024, [128 * 1024, 128 * 513, 9, 0, 128 * 512, 1, 2, 3], 8),
     ("topk4-c8", 1024, [128 * 512, 128 * 257, 9, 0, 128 * 256, 1, 2, 3], 4),
+    # The merge is pruned to the 16 lists with the best heads past 8 registers of lists:
+    # 128 lists of 4 keys (full network) against 129 (pruned) at C = 4, and 64 lists of 8
+    # against 65 and 128 at C = 8.
+    ("prune-c4-128-129", 1024, [128 * 512, 128 * 516, 5, 0, 128 * 3 + 7, 1, 2, 3], 16),
+    ("prune-c8-64-65", 1024, [128 * 520, 128 * 512, 128 * 1024, 128 * 100 + 3, 0, 1, 2, 3], 16),
 ]
 
 

@@ -258,6 +258,18 @@ def test_unfused_plan_parity(msa):
     run_case(msa, inp, ref, engine_list=[1], splits=(0,))
 
 
+def test_pruned_merge_host_plans(msa):
+    # Host plans whose lists go to the merge kernel: 128 lists of 4 keys (full network), 129
+    # (pruned to the 16 lists with the best heads), 172 lists of 3 keys padded to 4, and 104
+    # lists of 5 padded to 8 (pruned).
+    for W, lens, cases in ((512, [128 * 512, 128 * 511 + 9, 128 * 300, 1], ((128, 4),)),
+                           (516, [128 * 516, 128 * 515 + 9, 128 * 300, 1], ((129, 4), (172, 3), (128, 5)))):
+        inp = synth.paged_case(113, lens, W)
+        for ns, C in cases:
+            assert msa.plan(4, W, 16, ns)["blocks_per_split"] == C
+        ref = oracle.block_scores(inp.q, inp.k_cache, inp.block_table, inp.seq_lens)
+        run_case(msa, inp, ref, engine_list=[1], splits=tuple(ns for ns, _ in cases))
+
 def test_workspace_reuse_and_counter_reset(msa):
     # One workspace across calls with changing lengths and split counts: the per-row
     # counters must come back to zero after every fused call.
