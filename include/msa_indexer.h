@@ -95,7 +95,10 @@ int32_t msa_indexer_num_splits(int32_t batch, int32_t max_blocks_per_seq, int32_
 /*
  * The plan a call with these arguments uses: S splits per row, C blocks per split, Lk =
  * min(topk, C) candidates kept per (split, head), and whether the merge runs inside the
- * split kernel (fused: one launch) or as a second launch. Any output pointer may be NULL.
+ * split kernel (fused: one launch) or as a second launch. The single-token decode fuses
+ * when topk <= 16 and the S lists of Lk keys, each rounded up to a power of two, hold at
+ * most 1024 keys per head (e.g. 256 splits of 4 blocks), or when S <= 64 and S * Lk <=
+ * 1024; otherwise it takes two launches. Any output pointer may be NULL.
  * Returns MSA_OK or a negative status. With num_splits = 0, topk <= 16 and batch *
  * max_blocks_per_seq >= 8192 the plan is the device plan: the kernel itself picks C (a
  * power of two from 4 to 64) and each workgroup's (row, split) from seq_lens, so that about

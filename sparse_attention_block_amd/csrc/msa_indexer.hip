@@ -1353,8 +1353,10 @@ int pow2_ceil(int x) {
 // ranking). Each workgroup keeps Lk = min(topk, C) candidates per head. Automatic C:
 // about batch*W/1024 blocks per workgroup, at least 4: 32 at batch 32 x 1024 blocks,
 // which keeps 4 workgroups of 4 waves on each of the 256 CUs. The merge is fused into
-// the split kernel when a row has at most 64 workgroups whose lists fit in LDS
-// (S * topk <= 1024 keys per head).
+// the split kernel (the last workgroup of each row merges it) when the lists fit the merge
+// network (topk <= 16 and S lists of Lk keys rounded up to a power of two hold at most 1024
+// keys: up to 256 splits of 4 blocks, merged from the workspace), or when a row has at
+// most 64 workgroups whose lists fit in LDS (S * Lk <= 1024 keys per head).
 int32_t make_plan(int32_t batch, int32_t W, int32_t topk, int32_t num_splits, Plan* p) {
   if (batch < 0 || W < 0 || topk < 1 || topk > MSA_MAX_TOPK || num_splits < 0) return MSA_ERR_INVALID_ARG;
   if (W > MSA_MAX_BLOCKS_PER_SEQ) return MSA_ERR_UNSUPPORTED;
@@ -1373,7 +1375,7 @@ int32_t make_plan(int32_t batch, int32_t W, int32_t topk, int32_t num_splits, Pl
     if (C > kMaxSplitBlocks) return MSA_ERR_UNSUPPORTED;
     const int S = ceil_div(W, C), Lk = std::min(topk, C);
     if (S <= kMaxSplits && (int64_t)S * Lk <= kMaxMergeKeys) {
-      *p = Plan{S, C, Lk, S <= 64 && (int64_t)S * Lk <= kMaxFusedKeys};
+      *p = Plan{S, C, Lk, network_fits(S, Lk, topk) || (S <= 64 && (int64_t)S * Lk <= kMaxFusedKeys)};
       return MSA_OK;
     }
   }
@@ -1407,7 +1409,7 @@ size_t keys_offset(int32_t batch) {
 
 // LDS for the fused merge when merge_rounds may run (as merge_lds_bytes, for all four heads).
 size_t fused_lds_bytes(const Plan& p, int topk) {
-  return p.S <= 64 && topk <= kNetworkMaxM ? 0 : (size_t)p.S * (kHeads * p.Lk + 1) * sizeof(uint64_t);
+  return network_fits(p.S, p.Lk, topk) ? 0 : (size_t)p.S * (kHeads * p.Lk + 1) * sizeof(uint64_t);
 }
 // (For the device plan p.S and p.Lk bound the per-call values: S splits, Lk <= topk.)
 

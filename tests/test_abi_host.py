@@ -92,6 +92,12 @@ def test_plan_fuses_the_merge_when_it_fits(lib):
                                       "candidates_per_split": 16, "fused": True}
     assert plan(1, 64, 16)["fused"] and plan(16, 68, 16)["fused"] and plan(8, 256, 16)["fused"]
     assert plan(16, 1024, 16)["fused"]
+    # Host plans past 64 splits fuse while the lists fit the merge network (S * Lk2 <= 1024).
+    assert plan(1, 1024, 16) == {"splits": 256, "blocks_per_split": 4,
+                                 "candidates_per_split": 4, "fused": True}
+    assert plan(1, 1024, 16, 129)["fused"] and plan(6, 1024, 16)["fused"]
+    assert not plan(1, 2048, 16)["fused"]  # 256 splits x 8 candidates: 2048 keys per head
+    assert not plan(1, 1024, 17)["fused"]  # topk past the network, more than 64 splits
     big = plan(1, 16384, 16)          # 256 splits x 16 candidates: merged by a second kernel
     assert big["splits"] == 256 and not big["fused"]
 
