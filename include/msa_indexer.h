@@ -118,15 +118,16 @@ int32_t msa_indexer_plan(int32_t batch, int32_t max_blocks_per_seq, int32_t topk
 
 /*
  * Workspace bytes a call with these arguments needs (0 on invalid arguments).
- * Layout: a 256-byte header whose first uint32 is the device error word; then one 256-byte
- * line per row whose first uint32 counts the row's finished splits (uint32 [batch][64]);
+ * Layout: a 256-byte header whose first uint32 is the device error word; then 17 256-byte
+ * lines per row (uint32 [batch][17][64]) whose first uint32s count the row's finished splits
+ * (line 0; rows of more than 128 splits count 16 splits per group in lines 1..16 first);
  * then the per-split candidate keys, uint64 [batch][S][4][Lk]. The whole workspace must be
  * zero before its first use (e.g. hipMemset once after allocation). The library leaves the
  * counters at zero at the end of every call, so the same workspace can be reused, and
  * replayed in a graph, without clearing it again, by calls with the same batch; the error
  * word only ever gains bits (msa_indexer_read_error clears it). Before a call with a larger
  * batch than the workspace last served, clear the counter lines of the extra rows (they
- * held keys): the lines sit at fixed offsets, the keys right after batch lines.
+ * held keys): the lines sit at fixed offsets, the keys right after batch * 17 lines.
  */
 size_t msa_indexer_workspace_bytes(int32_t batch, int32_t max_blocks_per_seq, int32_t topk,
                                    int32_t num_splits);

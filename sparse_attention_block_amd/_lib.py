@@ -203,7 +203,7 @@ _WS_CACHE = {}
 def _default_workspace(nbytes: int, batch: int, device, stream):
     """The workspace of a call that passes none: one zeroed buffer per (device, stream, batch,
     size), reused, since the library leaves its per-row counters at zero at the end of every
-    call. The counter lines sit right after the header, one per row, so a buffer is only
+    call. The counter lines sit right after the header, 17 per row, so a buffer is only
     reused for the same batch (with another batch they would overlap the last call's keys).
     Calls on one stream run in order, so they never use it at the same time. Under graph
     capture a fresh buffer is made instead (it then belongs to the graph's memory)."""

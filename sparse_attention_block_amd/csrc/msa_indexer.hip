@@ -45,10 +45,13 @@ constexpr int kMaxMergeKeys = 4096;             // S * Lk keys of one (row, head
 constexpr int kMaxFusedKeys = 1024;             // fused merge: S * topk keys per head, 4 heads in LDS
 constexpr size_t kHeaderBytes = 256;            // workspace header (error word first)
 constexpr size_t kAlign = 256;
-// Each row's counter gets a 256-byte line of its own: atomics on one cache line serialize
-// like atomics on one address (measured ~10 ns each under contention), so rows sharing a
-// line would queue behind each other.
-constexpr int kCounterStride = 64;
+// Each counter gets a 256-byte line of its own: atomics on one cache line serialize like
+// atomics on one address (measured ~10 ns each under contention), so counters sharing a
+// line would queue behind each other. A row has a row counter and 16 group counters.
+constexpr int kCounterLine = 64;                // uint32 per counter line (256 B)
+constexpr int kCounterGroup = 16;               // workgroups per group counter
+constexpr int kCounterTwoLevel = 128;           // rows of more splits count in two levels
+constexpr int kCounterStride = kCounterLine * (1 + kMaxSplits / kCounterGroup);  // uint32 per row
 constexpr int kPageElems = kBlock * kDim;       // elements per page (bf16: 32 KiB, E4M3: 16 KiB)
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -664,7 +667,7 @@ struct SplitArgs {
   SplitLimits lim;      // device plan: per-row block limits of each split width
   uint64_t* keys;       // [batch][S][4][Lk]
   uint32_t* err;        // device error word (may be null)
-  uint32_t* counters;   // [batch][kCounterStride]: [0] workgroups finished; zero between calls
+  uint32_t* counters;   // [batch][kCounterStride]: row and group counters (count_in); zero between calls
   int32_t* out_ids;     // [batch][4][topk] (fused mode)
   float* out_scores;    // [batch][4][topk] (fused mode)
   int32_t* out_pages;   // [batch][4][8 topk] 16-token page table (fused mode; may be null)
@@ -724,6 +727,29 @@ __device__ __forceinline__ int wave_sum_bits(int x) {
 // the device plan), and a row's lists are [s][t][Lk] with this call's Lk = min(topk, C).
 __device__ __forceinline__ size_t list_offset(int b, int S, int QH, int LkMax, int s, int t, int Lk) {
   return (size_t)b * S * QH * LkMax + ((size_t)s * QH + t) * Lk;
+}
+
+// Thread 0 of a workgroup that has published its lists (split s of the row's ns): whether it
+// is the last of them, i.e. whether it merges the row. row points at the row's counter
+// block: the row counter in its first 256-byte line, group counters in the next 16. A row of
+// more than 128 splits counts in two levels, 16 splits per group counter and then the
+// groups' last workgroups on the row counter, because increments of one line serialize:
+// 256 workgroups finishing together on one counter cost ~1.2 us more than 16 groups (the
+// second level adds one atomic round trip, which only pays past 128 splits). Every counter
+// is back at zero when the call ends.
+__device__ __forceinline__ bool count_in(uint32_t* row, int s, int ns) {
+  if (ns > kCounterTwoLevel) {
+    const int g = s / kCounterGroup;
+    const int members = min(kCounterGroup, ns - g * kCounterGroup);
+    uint32_t* group = row + kCounterLine * (1 + g);
+    if (__hip_atomic_fetch_add(group, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != (uint32_t)(members - 1))
+      return false;
+    __hip_atomic_store(group, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    ns = (ns + kCounterGroup - 1) / kCounterGroup;
+  }
+  if (__hip_atomic_fetch_add(row, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != (uint32_t)(ns - 1)) return false;
+  __hip_atomic_store(row, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return true;
 }
 
 struct DevicePlan {
@@ -892,21 +918,16 @@ __global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
 
   // Publish this workgroup's lists and count it in. Every wave waits until its list
   // stores have completed (reached the device-coherent level) before the barrier, so the
-  // counter increment after it cannot overtake them. A release fence would do the same
-  // plus a writeback of the whole L2, which measured ~0.17 us per workgroup here; the
-  // lists are the only data other workgroups read.
+  // counter increment after it cannot overtake them (and a group's last workgroup counts
+  // the group in only after every member has). A release fence would do the same plus a
+  // writeback of the whole L2, which measured ~0.17 us per workgroup here; the lists are
+  // the only data other workgroups read. The last workgroup leaves the counters at zero
+  // for the next call (and for graph replays).
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  uint32_t* row_done = a.counters + (size_t)b * kCounterStride;
-  if (threadIdx.x == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(row_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = prev == (uint32_t)(ns - 1);
-  }
+  if (threadIdx.x == 0) s_last = count_in(a.counters + (size_t)b * kCounterStride, s, ns);
   __syncthreads();
   if (!s_last) return;
-  // Every workgroup of the row has counted in: ready the counter for the next call (and
-  // for graph replays).
-  if (threadIdx.x == 0) __hip_atomic_store(row_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (MODE != kFused) return;
 
   // Row b's lists are one contiguous range [s][h][i] of the workspace. Wave h merges
@@ -1315,14 +1336,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   const int ns = (nb + C - 1) / C;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  uint32_t* row_done = a.counters + (size_t)b * kCounterStride;
-  if (threadIdx.x == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(row_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = prev == (uint32_t)(ns - 1);
-  }
+  if (threadIdx.x == 0) s_last = count_in(a.counters + (size_t)b * kCounterStride, s, ns);
   __syncthreads();
   if (!s_last) return;
-  if (threadIdx.x == 0) __hip_atomic_store(row_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int msel = min(a.topk, nb);
   const uint64_t mine = merge_top16(a.keys + list_offset(b, a.S, kHeads, a.Lk, 0, h, Lk), (size_t)kHeads * Lk,
                                     ns, Lk, C, lane);
@@ -1402,7 +1418,7 @@ int32_t make_decode_plan(int32_t batch, int32_t W, int32_t topk, int32_t num_spl
   return MSA_OK;
 }
 
-// Workspace: [error word (256 B) | counters uint32 [batch][64] | keys uint64 [batch][S][4][Lk]]
+// Workspace: [error word (256 B) | counters uint32 [batch][17 lines][64] | keys uint64 [batch][S][4][Lk]]
 size_t keys_offset(int32_t batch) {
   return kHeaderBytes + (size_t)batch * kCounterStride * sizeof(uint32_t);
 }

@@ -15,6 +15,7 @@ OK, INVALID, WS_SMALL, UNSUPPORTED = 0, -1, -2, -3
 # Aligned, never-dereferenced stand-ins for device pointers: every call below must be
 # refused by the host-side checks, so nothing ever reaches the device.
 FAKE = 1 << 20
+CTR = 17 * 256  # counter bytes per row: the row counter and 16 group counters, a 256-byte line each
 
 
 @pytest.fixture(scope="module")
@@ -71,14 +72,14 @@ def test_split_plan(lib):
 
 def test_workspace_size(lib):
     ws = lib.msa_indexer_workspace_bytes
-    # error word (256 B), one 256-byte counter line per row, then the keys: the larger of the
-    # device plan (S = min(64, ceil(W/4)) lists of topk keys per row and head, which any of
-    # its split widths fits) and the host plan (the stage calls)
-    assert ws(32, 1024, 16, 0) == 256 + 32 * 256 + 32 * 64 * 4 * 16 * 8
-    assert ws(32, 1024, 16, 32) == 256 + 32 * 256 + 32 * 32 * 4 * 16 * 8
+    # error word (256 B), 17 256-byte counter lines per row (CTR), then the keys: the larger
+    # of the device plan (S = min(64, ceil(W/4)) lists of topk keys per row and head, which
+    # any of its split widths fits) and the host plan (the stage calls)
+    assert ws(32, 1024, 16, 0) == 256 + 32 * CTR + 32 * 64 * 4 * 16 * 8
+    assert ws(32, 1024, 16, 32) == 256 + 32 * CTR + 32 * 32 * 4 * 16 * 8
     # small tables (batch * W < 8192 blocks) keep the host plan: 4-block splits keep 4 keys
-    assert ws(16, 68, 16, 0) == 256 + 16 * 256 + 16 * 17 * 4 * 4 * 8
-    assert ws(16, 68, 16, 17) == 256 + 16 * 256 + 16 * 17 * 4 * 4 * 8   # 4-block splits keep 4 keys
+    assert ws(16, 68, 16, 0) == 256 + 16 * CTR + 16 * 17 * 4 * 4 * 8
+    assert ws(16, 68, 16, 17) == 256 + 16 * CTR + 16 * 17 * 4 * 4 * 8   # 4-block splits keep 4 keys
     assert ws(0, 1024, 16, 0) == 256
     assert ws(1, 8, 0, 0) == 0
 
@@ -261,7 +262,7 @@ def _decode_multi(lib, **kw):
     (dict(topk=65), INVALID),
     (dict(n_init=9, n_local=8), INVALID),
     (dict(W=16385, stride=16385), UNSUPPORTED),
-    (dict(ws_bytes=256 + 2 * 256 + 2 * 2 * 16 * 4 * 8 - 1), WS_SMALL),
+    (dict(ws_bytes=256 + 2 * CTR + 2 * 2 * 16 * 4 * 8 - 1), WS_SMALL),
 ])
 def test_decode_multi_rejects_on_host(lib, kw, code):
     assert _decode_multi(lib, **kw) == code
@@ -270,11 +271,11 @@ def test_decode_multi_rejects_on_host(lib, kw, code):
 def test_decode_multi_workspace_and_no_op(lib):
     ws = lib.msa_indexer_workspace_bytes_multi
     # header, counter lines, then keys [batch][S][qlen*4][Lk]: 8 blocks -> 2 splits of 4, Lk 4
-    assert ws(2, 8, 4, 16, 0) == 256 + 2 * 256 + 2 * 2 * 16 * 4 * 8
+    assert ws(2, 8, 4, 16, 0) == 256 + 2 * CTR + 2 * 2 * 16 * 4 * 8
     # with num_splits = 0 the device plan (S = 64 list slots of topk keys per row and head)
-    assert ws(32, 1024, 4, 16, 0) == 256 + 32 * 256 + 32 * 64 * 16 * 16 * 8
-    assert ws(32, 1024, 1, 16, 0) == 256 + 32 * 256 + 32 * 64 * 4 * 16 * 8
-    assert ws(32, 1024, 4, 16, 32) == 256 + 32 * 256 + 32 * 32 * 16 * 16 * 8
+    assert ws(32, 1024, 4, 16, 0) == 256 + 32 * CTR + 32 * 64 * 16 * 16 * 8
+    assert ws(32, 1024, 1, 16, 0) == 256 + 32 * CTR + 32 * 64 * 4 * 16 * 8
+    assert ws(32, 1024, 4, 16, 32) == 256 + 32 * CTR + 32 * 32 * 16 * 16 * 8
     assert ws(2, 8, 0, 16, 0) == 0 and ws(2, 8, 5, 16, 0) == 0
     assert _decode_multi(lib, ws_bytes=ws(2, 8, 4, 16, 0) - 1) == WS_SMALL
     assert _decode_multi(lib, batch=0, q=None, k=None, bt=None, lens=None, ids=None, scores=None,

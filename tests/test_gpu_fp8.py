@@ -208,7 +208,7 @@ def test_fp8_single_position_workspace_reuse(msa):
         ids, sc = msa.msa_indexer_decode_fp8(q, k, 0.5, bt, lens, num_splits=ns, workspace=ws)
         s = msa.msa_indexer_block_scores_fp8(q, k, 0.5, bt, lens, num_splits=ns).cpu().numpy()
         torch.cuda.synchronize()
-        assert np.all(ws[:256 + 6 * 256].view(torch.int32).cpu().numpy() == 0), it
+        assert np.all(ws[:256 + 6 * 17 * 256].view(torch.int32).cpu().numpy() == 0), it  # header, 17 counter lines per row
         cur = synth.Inputs("reuse", inp.q, inp.k_cache, inp.block_table, new_lens, k_scale=0.5)
         gi, gs = oracle.select(s[:, 0].astype(np.float64), position_lens(cur, 0, 1), 16, 1, 2)
         assert np.array_equal(ids.cpu().numpy()[:, 0], gi), it

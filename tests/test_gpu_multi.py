@@ -190,7 +190,7 @@ def test_multi_workspace_reuse_and_graph_replay(msa, Q):
         lens.copy_(torch.from_numpy(new_lens))
         ids, sc = msa.msa_indexer_decode_multi(q, k, bt, lens, num_splits=ns, workspace=ws)
         torch.cuda.synchronize()
-        assert np.all(ws[:256 + 5 * 256].view(torch.int32).cpu().numpy() == 0), it
+        assert np.all(ws[:256 + 5 * 17 * 256].view(torch.int32).cpu().numpy() == 0), it  # header, 17 counter lines per row
         cur = synth.Inputs("reuse", inp.q, inp.k_cache, inp.block_table, new_lens)
         want_ids, _, ref = oracle.decode(cur)
         for p in range(Q):

@@ -22,6 +22,8 @@ from gpu_util import (check_scores, check_selection_exact_given_scores, check_se
 
 pytestmark = pytest.mark.gpu
 
+CTR = 17 * 256  # workspace counter bytes per row (a row counter and 16 group counters)
+
 torch = pytest.importorskip("torch")
 
 
@@ -285,11 +287,11 @@ def test_workspace_reuse_and_counter_reset(msa):
         lens.copy_(torch.from_numpy(new_lens))
         ids, sc = msa.msa_indexer_decode(q, k, bt, lens, num_splits=ns, workspace=ws)
         torch.cuda.synchronize()
-        # error word in the 256-byte header, then one 256-byte counter line per row
+        # error word in the 256-byte header, then 17 256-byte counter lines per row
         header = ws[:256].view(torch.int32).cpu().numpy()
-        counters = ws[256:256 + 6 * 256].view(torch.int32).cpu().numpy().reshape(6, 64)
+        counters = ws[256:256 + 6 * CTR].view(torch.int32).cpu().numpy().reshape(6, 17, 64)
         assert np.all(header == 0), (it, header[:4])
-        assert np.all(counters == 0), (it, counters[:, 0])
+        assert np.all(counters == 0), (it, counters[:, :, 0])
         cur = synth.Inputs("reuse", inp.q, inp.k_cache, inp.block_table, new_lens)
         ref = oracle.block_scores(cur.q, cur.k_cache, cur.block_table, cur.seq_lens)
         gpu_s = msa.msa_indexer_block_scores(q, k, bt, lens).cpu().numpy()
@@ -318,7 +320,7 @@ def test_default_workspace_is_reused(msa):
     torch.cuda.synchronize()
     assert torch.equal(ids2, ids) and torch.equal(sc2, sc)
     for (_, _, batch, _), ws in _lib._WS_CACHE.items():  # every cached counter line is zero
-        assert int(ws[256:256 + 256 * batch].view(torch.int32).abs().sum()) == 0
+        assert int(ws[256:256 + CTR * batch].view(torch.int32).abs().sum()) == 0
 
 
 def test_decode_engines_agree_on_exact_data(msa):
