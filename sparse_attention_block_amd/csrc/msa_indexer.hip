@@ -911,6 +911,17 @@ __global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
     key = make_key(sc[lane][h], jj, jj < a.n_init || jj >= nb - a.n_local);
   }
   key = sort_desc_first(key, lane, n);
+  if (MODE == kFused && ns == 1) {
+    // The row's only split: its sorted keys are the selection (m <= n of them), so it is
+    // written at once, without the publication, count and reload of the lists.
+    const int m = min(a.topk, nb);
+    const size_t o = ((size_t)b * kHeads + h) * a.topk;
+    write_selection(key, m, a.topk, lane, a.out_ids + o, a.out_scores + o);
+    if (a.out_pages != nullptr)
+      emit_pages(key_id(key), lane < m, a.topk, lane, btrow, L, a.out_pages + o * 8,
+                 a.out_tokens + (size_t)b * kHeads + h);
+    return;
+  }
   // Agent-scope atomic stores: written through to the device-coherent level, so the
   // row's last workgroup can read them from any XCD without an L2 writeback.
   uint64_t* out = a.keys + list_offset(b, a.S, kHeads, a.Lk, s, h, Lk);
@@ -1322,6 +1333,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     const bool real = lane < n && jj < nbp;
     uint64_t key = real ? make_key(sc[lane][4 * p + h], jj, jj < a.n_init || jj >= nbp - a.n_local) : 0;
     key = sort_desc_first(key, lane, n);
+    if (MODE == kFused && a.Q == 1 && nb <= C) {
+      // The row's only split (one position): its sorted keys are the selection.
+      const size_t o = ((size_t)b * kHeads + h) * a.topk;
+      write_selection(key, min(a.topk, nb), a.topk, lane, a.out_ids + o, a.out_scores + o);
+      return;
+    }
     uint64_t* out = a.keys + list_offset(b, a.S, a.Q * kHeads, a.Lk, s, 4 * p + h, Lk);
     if (MODE == kFused) {
       if (lane < Lk) __hip_atomic_store(out + lane, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -272,6 +272,27 @@ def test_pruned_merge_host_plans(msa):
         ref = oracle.block_scores(inp.q, inp.k_cache, inp.block_table, inp.seq_lens)
         run_case(msa, inp, ref, engine_list=[1], splits=tuple(ns for ns, _ in cases))
 
+@pytest.mark.parametrize("topk,n_init,n_local", [(16, 1, 2), (2, 1, 1), (3, 0, 0)])
+def test_single_split_rows(msa, topk, n_init, n_local):
+    # Every row fits one split (at most 4 blocks under the host plan's 4-block splits), so
+    # each workgroup writes its row's selection and page table directly, without publishing
+    # its lists: the decode, page-table and FP8 calls against the oracle, with empty, partial
+    # and full rows, and fewer blocks than topk as well as more.
+    from test_gpu_fp8 import run_fp8
+    lens = [0, 1, 127, 128, 129, 300, 511, 512, 64, 256 + 3, 1, 0]
+    inp = synth.paged_case(114, lens, 4, topk=topk, n_init=n_init, n_local=n_local)
+    assert msa.plan(len(lens), 4, topk)["blocks_per_split"] == 4
+    ref = oracle.block_scores(inp.q, inp.k_cache, inp.block_table, inp.seq_lens)
+    ids, sc = run_case(msa, inp, ref, engine_list=[1], splits=(0,))
+    q, k, bt, dl = to_device(inp)
+    ids_p, sc_p, pages, tokens = msa.msa_indexer_decode_pages(q, k, bt, dl, topk, n_init, n_local)
+    assert np.array_equal(ids_p.cpu().numpy(), ids) and np.array_equal(sc_p.cpu().numpy(), sc)
+    want_p, want_t = oracle.expand_pages(ids, inp.block_table, inp.seq_lens)
+    assert np.array_equal(pages.cpu().numpy(), want_p) and np.array_equal(tokens.cpu().numpy(), want_t)
+    run_fp8(msa, synth.fp8_case(115, lens, 4, 1, k_scale=0.5, topk=topk, n_init=n_init, n_local=n_local),
+            1e-3 * 4.0 * 0.5)
+
+
 def test_workspace_reuse_and_counter_reset(msa):
     # One workspace across calls with changing lengths and split counts: the per-row
     # counters must come back to zero after every fused call.
