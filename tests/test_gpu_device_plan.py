@@ -119,6 +119,44 @@ def test_split_width_changes_between_graph_replays(msa):
                                            16, 1, 2)
 
 
+def test_two_level_count_and_single_splits_under_graph_replays(msa):
+    # Replays of one captured call whose lengths switch between rows of 256 splits (counted
+    # in two levels), rows that fit one split (written without the merge) and a mix; each
+    # replay equals an eager call, and every counter line is back at zero after it.
+    B, W = 8, 1024
+    inp = synth.paged_case(405, [128 * W] * B, W, poison=False)
+    q, k, bt, lens = to_device(inp)
+    ws = msa.new_workspace(B, W, 16)
+    ids = torch.empty((B, 4, 16), dtype=torch.int32, device="cuda")
+    sc = torch.empty((B, 4, 16), dtype=torch.float32, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        msa.msa_indexer_decode(q, k, bt, lens, out_ids=ids, out_scores=sc, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        msa.msa_indexer_decode(q, k, bt, lens, out_ids=ids, out_scores=sc, workspace=ws)
+    one_long = np.zeros(B, np.int64); one_long[3] = 128 * W
+    two_long = np.zeros(B, np.int64); two_long[[0, 7]] = [128 * W, 128 * W - 5]
+    short = np.array([1, 128, 129, 512, 0, 300, 511, 64])
+    mixed = short.copy(); mixed[5] = 128 * W
+    for it, new in enumerate([one_long, two_long, short, mixed, one_long, short, two_long]):
+        lens.copy_(torch.from_numpy(new.astype(np.int32)))
+        g.replay()
+        torch.cuda.synchronize()
+        counters = ws[256:256 + B * 17 * 256].view(torch.int32)
+        assert int(counters.abs().sum()) == 0, it
+        got_ids, got_sc = ids.clone(), sc.clone()
+        eager_ids, eager_sc = msa.msa_indexer_decode(q, k, bt, lens)
+        assert torch.equal(got_ids, eager_ids) and torch.equal(got_sc, eager_sc), it
+        cur = synth.Inputs("replay", inp.q, inp.k_cache, inp.block_table, new.astype(np.int32))
+        gpu_s = msa.msa_indexer_block_scores(q, k, bt, lens).cpu().numpy()
+        check_selection_exact_given_scores(got_ids.cpu().numpy(), got_sc.cpu().numpy(), gpu_s,
+                                           cur.seq_lens, 16, 1, 2)
+
+
 # Rows at the edges of the per-row split limit (topk 16: C = 4 up to 1024 blocks, then C = 32
 # up to 2048 and C = 64 up to 4096; topk 8: C = 16 up to 1024 blocks; topk 4: C = 4 up to 256
 # blocks, C = 8 up to 512), for the single-token, multi-token and FP8 passes.
