@@ -271,6 +271,14 @@ def test_pruned_merge_host_plans(msa):
             assert msa.plan(4, W, 16, ns)["blocks_per_split"] == C
         ref = oracle.block_scores(inp.q, inp.k_cache, inp.block_table, inp.seq_lens)
         run_case(msa, inp, ref, engine_list=[1], splits=tuple(ns for ns, _ in cases))
+    # Smaller topk through the pruned path (the first m of its top 16): 256 splits of 4
+    # blocks (automatic, or asked for) and 128 of 8; the short row fits one split.
+    for topk, n_init, n_local in ((8, 1, 2), (3, 0, 1)):
+        inp = synth.paged_case(116, [128 * 1024, 128 * 700 + 1, 5], 1024, topk=topk, n_init=n_init,
+                               n_local=n_local)
+        assert msa.plan(3, 1024, topk, 256)["blocks_per_split"] == 4
+        ref = oracle.block_scores(inp.q, inp.k_cache, inp.block_table, inp.seq_lens)
+        run_case(msa, inp, ref, engine_list=[1], splits=(0, 129, 256))
 
 @pytest.mark.parametrize("topk,n_init,n_local", [(16, 1, 2), (2, 1, 1), (3, 0, 0)])
 def test_single_split_rows(msa, topk, n_init, n_local):
