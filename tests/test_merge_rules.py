@@ -13,7 +13,9 @@ def top16(keys):
 
 def make_lists(rng, ns, lk, fill):
     """ns lists of lk slots, distinct positive keys best first, each with 1..lk real keys."""
-    keys = rng.choice(np.arange(1, 1 << 40), size=ns * lk, replace=False)
+    keys = np.unique(rng.integers(1, 1 << 40, size=2 * ns * lk))[: ns * lk]  # distinct
+    assert keys.size == ns * lk
+    rng.shuffle(keys)
     lists = []
     for i in range(ns):
         real = lk if fill else int(rng.integers(1, lk + 1))
@@ -29,8 +31,7 @@ def test_top16_lies_in_the_lists_with_the_best_heads(ns, lk):
     for trial in range(60):
         lists = make_lists(rng, ns, lk, fill=trial % 2 == 0)
         if trial % 3 == 0:  # adversarial: one list holds all the large keys
-            big = sorted(rng.choice(np.arange(1 << 41, 1 << 42), size=lk, replace=False).tolist(),
-                         reverse=True)
+            big = sorted(np.unique(rng.integers(1 << 41, 1 << 42, size=4 * lk))[:lk].tolist(), reverse=True)
             lists[int(rng.integers(ns))] = big
         everything = [k for l in lists for k in l if k]
         best = sorted(range(ns), key=lambda i: lists[i][0], reverse=True)[:16]
