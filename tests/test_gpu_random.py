@@ -64,6 +64,31 @@ def test_random_single_token(msa, seed):
     check_selection_vs_oracle(ids, ref, L, topk, n_init, n_local)
 
 
+@pytest.mark.parametrize("seed", range(700, 712))
+def test_random_long_rows_small_batch(msa, seed):
+    # Small batches of long rows among short ones, where rows take up to 256 splits: the
+    # pruned merge, the two-level count and single-split rows, under automatic and asked-for
+    # split counts and several topk.
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 5))
+    W = int(rng.choice([513, 700, 1024]))
+    kind = rng.random(B)
+    lens = np.where(kind < 0.2, rng.integers(0, 513, size=B),
+                    np.where(kind < 0.6, 128 * W, rng.integers(1, 128 * W + 1, size=B))).astype(np.int32)
+    topk = int(rng.choice([2, 3, 8, 16, 16]))
+    n_init, n_local = (1, 1) if topk >= 2 else (0, 0)
+    ns = int(rng.choice([0, 0, 129, 200, 256]))
+    inp = synth.paged_case(seed, lens.tolist(), W, topk=topk, n_init=n_init, n_local=n_local)
+    q, k, bt, lens_d = to_device(inp)
+    ref = oracle.block_scores(inp.q, inp.k_cache, inp.block_table, inp.seq_lens)
+    s = msa.msa_indexer_block_scores(q, k, bt, lens_d).cpu().numpy()
+    check_scores(s, ref)
+    ids, sc = msa.msa_indexer_decode(q, k, bt, lens_d, topk, n_init, n_local, num_splits=ns)
+    ids, sc = ids.cpu().numpy(), sc.cpu().numpy()
+    check_selection_exact_given_scores(ids, sc, s, inp.seq_lens, topk, n_init, n_local)
+    check_selection_vs_oracle(ids, ref, inp.seq_lens, topk, n_init, n_local)
+
+
 @pytest.mark.parametrize("seed", range(600, 615))
 def test_random_multi_and_fp8(msa, seed):
     B, W, lens, topk, n_init, n_local, splits = draw_case(seed)
