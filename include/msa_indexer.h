@@ -116,18 +116,31 @@ int32_t msa_indexer_plan(int32_t batch, int32_t max_blocks_per_seq, int32_t topk
                          int32_t *splits, int32_t *blocks_per_split, int32_t *candidates_per_split,
                          int32_t *fused);
 
+/* Workspace layout (msa_indexer_workspace_bytes). */
+#define MSA_WORKSPACE_HEADER_BYTES 256   /* the device error word first */
+#define MSA_WORKSPACE_ROW_BYTES 4352     /* 17 counter lines of 256 B per row */
+
 /*
- * Workspace bytes a call with these arguments needs (0 on invalid arguments).
- * Layout: a 256-byte header whose first uint32 is the device error word; then 17 256-byte
- * lines per row (uint32 [batch][17][64]) whose first uint32s count the row's finished splits
- * (line 0; rows of more than 128 splits count 16 splits per group in lines 1..16 first);
- * then the per-split candidate keys, uint64 [batch][S][4][Lk]. The whole workspace must be
- * zero before its first use (e.g. hipMemset once after allocation). The library leaves the
- * counters at zero at the end of every call, so the same workspace can be reused, and
- * replayed in a graph, without clearing it again, by calls with the same batch; the error
- * word only ever gains bits (msa_indexer_read_error clears it). Before a call with a larger
- * batch than the workspace last served, clear the counter lines of the extra rows (they
- * held keys): the lines sit at fixed offsets, the keys right after batch * 17 lines.
+ * Workspace bytes a call with these arguments needs (0 on invalid arguments): the persistent,
+ * allocation-free buffer of vLLM PR #57832 (Problem and CUDA graph capture: buffers sized from
+ * the launch bounds, reused by every replay), sized from (batch, max_blocks_per_seq, topk,
+ * num_splits) only.
+ * Layout of a buffer of N bytes (the size the caller passes as workspace_bytes):
+ *   [0, 256)                           header; its first uint32 is the device error word;
+ *   [256 + 4352 b, 256 + 4352 (b+1))   the counter lines of row b (uint32 [17][64]: line 0
+ *                                      counts the row's finished splits, lines 1..16 count
+ *                                      groups of 16 splits for rows of more than 128 splits);
+ *   the last K bytes (256-aligned)     the per-split candidate keys, uint64 [batch][S][4][Lk],
+ *                                      K = this size minus 256 minus 4352 * batch.
+ * The whole buffer must be zero before its first use (e.g. hipMemset once after allocation).
+ * Every call leaves the counters at zero when it ends, and a row's counter lines sit at an
+ * offset that depends on nothing but the row, while a call's keys fill the end of the buffer.
+ * So one buffer can serve any sequence of calls, and graph replays, without being cleared
+ * again, provided every call passes the buffer's full size N and N holds the largest batch's
+ * counter lines plus the largest key region of those calls. Calls with the same
+ * max_blocks_per_seq, topk and num_splits (and qlen, for msa_indexer_workspace_bytes_multi)
+ * meet this whatever their batch sizes, with N the size the largest batch needs. The error
+ * word only ever gains bits (msa_indexer_read_error takes and clears them).
  */
 size_t msa_indexer_workspace_bytes(int32_t batch, int32_t max_blocks_per_seq, int32_t topk,
                                    int32_t num_splits);
@@ -156,7 +169,8 @@ size_t msa_indexer_workspace_bytes(int32_t batch, int32_t max_blocks_per_seq, in
  *   out_scores   fp32 [batch][4][topk]: the selected blocks' scores (-0.0 reads as +0.0);
  *                slots past m hold -inf.
  *   workspace    device memory of at least msa_indexer_workspace_bytes(...) bytes, 256-byte
- *                aligned, zeroed once before its first use (see msa_indexer_workspace_bytes).
+ *                aligned, zeroed once before its first use; workspace_bytes is its full size
+ *                (see msa_indexer_workspace_bytes).
  *   num_splits   0 = automatic; see msa_indexer_num_splits.
  * When the plan is fused (msa_indexer_plan) this is one kernel launch: the last split of
  * each row to finish merges the row. Otherwise stage 1 and stage 2 are two launches.
@@ -239,9 +253,10 @@ int32_t msa_indexer_expand_pages_multi(const int32_t *ids, const int32_t *block_
                                        void *stream);
 
 /*
- * Workspace bytes of msa_indexer_decode_multi (0 on invalid arguments): the layout of
- * msa_indexer_workspace_bytes with keys uint64 [batch][S][qlen*4][Lk]. Zeroed once before
- * its first use, like the single-token workspace.
+ * Workspace bytes of msa_indexer_decode_multi and msa_indexer_decode_fp8 (0 on invalid
+ * arguments): the layout of msa_indexer_workspace_bytes with keys uint64
+ * [batch][S][qlen*4][Lk]. Zeroed once before its first use, like the single-token workspace,
+ * and shareable with it under the same rule.
  */
 size_t msa_indexer_workspace_bytes_multi(int32_t batch, int32_t max_blocks_per_seq, int32_t qlen,
                                          int32_t topk, int32_t num_splits);
@@ -357,8 +372,10 @@ int32_t msa_indexer_block_scores(const void *q, const void *k_cache, const int32
                                  int32_t engine, void *stream);
 
 /*
- * Copies the workspace's device error word to *host_flags after synchronizing `stream`,
- * then clears it on the device. Returns MSA_ERR_HIP if a HIP call fails.
+ * Takes the workspace's device error bits: a one-thread kernel on `stream` reads and clears
+ * the error word in one atomic step (so it is ordered after every earlier call on the stream
+ * and before every later one), then the bits are copied to *host_flags and the stream is
+ * synchronized. workspace must be 256-byte aligned. Returns MSA_ERR_HIP if a HIP call fails.
  */
 int32_t msa_indexer_read_error(void *workspace, uint32_t *host_flags, void *stream);
 

@@ -197,15 +197,20 @@ def _inputs(q, k_cache, block_table, seq_lens):
     return ptrs, B, block_table.shape[1], block_table.stride(0), k_cache.shape[0]
 
 
+WS_HEADER_BYTES = 256   # MSA_WORKSPACE_HEADER_BYTES
+WS_ROW_BYTES = 4352     # MSA_WORKSPACE_ROW_BYTES: the counter lines of one row
+
 _WS_CACHE = {}
 
 
 def _default_workspace(nbytes: int, batch: int, device, stream):
-    """The workspace of a call that passes none: one zeroed buffer per (device, stream, batch,
-    size), reused, since the library leaves its per-row counters at zero at the end of every
-    call. The counter lines sit right after the header, 17 per row, so a buffer is only
-    reused for the same batch (with another batch they would overlap the last call's keys).
-    Calls on one stream run in order, so they never use it at the same time. Under graph
+    """The workspace of a call that passes none: one zeroed buffer per (device, stream),
+    reused by every such call on that stream. The library keeps each row's counter lines at
+    a fixed offset and a call's keys at the end of the buffer, so a buffer serves any call
+    whose batch's counter lines plus key region fit it; it is replaced by a larger zeroed one
+    when a call needs more (the largest batch seen times the counter lines per row, plus the
+    largest key region seen). Calls on one stream run in order, so they never use it at the
+    same time, and the old buffer goes back to torch's allocator on that stream. Under graph
     capture a fresh buffer is made instead (it then belongs to the graph's memory)."""
     torch = _torch()
     if nbytes == 0:
@@ -213,11 +218,15 @@ def _default_workspace(nbytes: int, batch: int, device, stream):
     if torch.cuda.is_current_stream_capturing():
         return torch.zeros(nbytes, dtype=torch.uint8, device=device)
     s = torch.cuda.current_stream(device) if stream is None else stream
-    key = (device.index, s.cuda_stream, batch, nbytes)
-    ws = _WS_CACHE.get(key)
-    if ws is None:
-        ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
-        _WS_CACHE[key] = ws
+    key = (device.index, s.cuda_stream)
+    rows, keys = batch, nbytes - WS_HEADER_BYTES - WS_ROW_BYTES * batch
+    ent = _WS_CACHE.get(key)
+    if ent is not None and ent[1] >= rows and ent[2] >= keys:
+        return ent[0]
+    if ent is not None:
+        rows, keys = max(rows, ent[1]), max(keys, ent[2])
+    ws = torch.zeros(WS_HEADER_BYTES + WS_ROW_BYTES * rows + keys, dtype=torch.uint8, device=device)
+    _WS_CACHE[key] = (ws, rows, keys)
     return ws
 
 

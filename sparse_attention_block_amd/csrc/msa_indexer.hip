@@ -1363,6 +1363,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   write_selection(mine, msel, a.topk, lane, a.out_ids + o, a.out_scores + o);
 }
 
+// The error word's bits, taken (read and cleared atomically) into the header's next word.
+__global__ void take_error_kernel(uint32_t* hdr) {
+  hdr[1] = __hip_atomic_exchange(hdr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // ---------------------------------------------------------------------------------------
 // Host side.
 
@@ -1390,6 +1395,8 @@ int pow2_ceil(int x) {
 // network (topk <= 16 and S lists of Lk keys rounded up to a power of two hold at most 1024
 // keys: up to 256 splits of 4 blocks, merged from the workspace), or when a row has at
 // most 64 workgroups whose lists fit in LDS (S * Lk <= 1024 keys per head).
+int32_t plan_from_width(int32_t W, int32_t topk, int C, Plan* p);
+
 int32_t make_plan(int32_t batch, int32_t W, int32_t topk, int32_t num_splits, Plan* p) {
   if (batch < 0 || W < 0 || topk < 1 || topk > MSA_MAX_TOPK || num_splits < 0) return MSA_ERR_INVALID_ARG;
   if (W > MSA_MAX_BLOCKS_PER_SEQ) return MSA_ERR_UNSUPPORTED;
@@ -1404,6 +1411,11 @@ int32_t make_plan(int32_t batch, int32_t W, int32_t topk, int32_t num_splits, Pl
     C = pow2_ceil(std::max(1, ceil_div((int64_t)batch * W, 1024)));
     C = std::min(std::max(C, 4), kMaxSplitBlocks);
   }
+  return plan_from_width(W, topk, C, p);
+}
+
+// The host plan with the smallest split width C >= C0 that the limits allow (W > 0).
+int32_t plan_from_width(int32_t W, int32_t topk, int C, Plan* p) {
   for (;; ++C) {
     if (C > kMaxSplitBlocks) return MSA_ERR_UNSUPPORTED;
     const int S = ceil_div(W, C), Lk = std::min(topk, C);
@@ -1435,9 +1447,23 @@ int32_t make_decode_plan(int32_t batch, int32_t W, int32_t topk, int32_t num_spl
   return MSA_OK;
 }
 
-// Workspace: [error word (256 B) | counters uint32 [batch][17 lines][64] | keys uint64 [batch][S][4][Lk]]
-size_t keys_offset(int32_t batch) {
-  return kHeaderBytes + (size_t)batch * kCounterStride * sizeof(uint32_t);
+// Workspace layout (the caller's buffer of ws_size bytes, 256-byte aligned):
+//   [0, 256)                   header: the device error word, then the word read_error stages
+//   [256 + 4352 b, + 4352)     row b's 17 counter lines (row counter, 16 group counters)
+//   the last keys_bytes        keys uint64 [batch][S][Q*4][Lk], starting 256-byte aligned
+// A row's counter lines sit at an offset that depends on nothing but the row, and a call's
+// keys fill the end of the buffer. So calls that share one buffer and pass its full size
+// never write keys over a counter line another of them counts on, whatever their batch sizes
+// (for calls of one table width, topk, split count and qlen; in general when the buffer holds
+// the largest batch's counter lines plus the largest key region). The counters return to zero
+// at the end of every call; the keys need no initial state.
+constexpr size_t kRowCounterBytes = kCounterStride * sizeof(uint32_t);  // 17 lines of 256 B
+
+size_t counters_end(int32_t batch) { return kHeaderBytes + (size_t)batch * kRowCounterBytes; }
+
+size_t keys_bytes(int32_t batch, int32_t Q, const Plan& p) {
+  const size_t n = (size_t)batch * p.S * Q * kHeads * p.Lk * sizeof(uint64_t);
+  return (n + kAlign - 1) / kAlign * kAlign;
 }
 
 // LDS for the fused merge when merge_rounds may run (as merge_lds_bytes, for all four heads).
@@ -1446,8 +1472,47 @@ size_t fused_lds_bytes(const Plan& p, int topk) {
 }
 // (For the device plan p.S and p.Lk bound the per-call values: S splits, Lk <= topk.)
 
-size_t ws_bytes(int32_t batch, const Plan& p) {
-  return keys_offset(batch) + (size_t)batch * p.S * kHeads * p.Lk * sizeof(uint64_t);
+// Key bytes per row that a call with these (W, topk, num_splits, Q) may use at any batch size:
+// an explicit split count fixes the width; the automatic one takes a width of 4 .. 64 blocks
+// from the batch, or the device plan (S * topk keys per head). Sizing every call's workspace
+// with this bound (workspace_bytes) is what lets calls of any batch share one buffer: a call of
+// batch B writes at most B times this many key bytes at the buffer's end, which stay clear of
+// the counter lines of any batch the buffer holds.
+size_t row_key_bytes(int32_t W, int32_t topk, int32_t num_splits, int32_t Q) {
+  size_t best = 0;
+  auto consider = [&](const Plan& p) {
+    best = std::max(best, (size_t)p.S * Q * kHeads * p.Lk * sizeof(uint64_t));
+  };
+  Plan p;
+  if (W == 0 || num_splits > 0) {
+    if (make_plan(1, W, topk, num_splits, &p) == MSA_OK) consider(p);
+    return best;
+  }
+  for (int c0 = 4; c0 <= kMaxSplitBlocks; c0 *= 2)
+    if (plan_from_width(W, topk, c0, &p) == MSA_OK) consider(p);
+  if (make_decode_plan(kDeviceMinBlocks, W, topk, 0, &p) == MSA_OK && p.device) consider(p);
+  return best;
+}
+
+// Workspace bytes of a call (the size check of every call, and workspace_bytes).
+size_t ws_bytes(int32_t batch, int32_t W, int32_t topk, int32_t num_splits, int32_t Q = 1) {
+  const size_t kb = (size_t)batch * row_key_bytes(W, topk, num_splits, Q);
+  return counters_end(batch) + (kb + kAlign - 1) / kAlign * kAlign;
+}
+
+// The error word, counters and keys of a call in a buffer of ws_size bytes whose keys take
+// kb bytes (ws_size >= counters_end(batch) + kb, checked by the caller).
+struct WsView {
+  uint32_t* err;
+  uint32_t* counters;
+  uint64_t* keys;
+};
+
+WsView ws_view(void* ws, size_t ws_size, size_t kb) {
+  if (ws == nullptr) return WsView{nullptr, nullptr, nullptr};
+  char* w = static_cast<char*>(ws);
+  return WsView{reinterpret_cast<uint32_t*>(w), reinterpret_cast<uint32_t*>(w + kHeaderBytes),
+                reinterpret_cast<uint64_t*>(w + ((ws_size - kb) & ~(kAlign - 1)))};
 }
 
 bool aligned(const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
@@ -1486,7 +1551,7 @@ int32_t launch_split(const SplitArgs& a, int32_t batch, int32_t engine, size_t l
 
 SplitArgs make_split_args(const void* q, const void* k, const int32_t* bt, const int32_t* lens,
                           int32_t W, int32_t bt_stride, int64_t num_pages, const Plan& p,
-                          int32_t topk, int32_t n_init, int32_t n_local, void* ws, int32_t batch) {
+                          int32_t topk, int32_t n_init, int32_t n_local, const WsView& w, int32_t batch) {
   SplitArgs a;
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
@@ -1504,10 +1569,9 @@ SplitArgs make_split_args(const void* q, const void* k, const int32_t* bt, const
   a.batch = batch;
   a.device_plan = p.device ? 1 : 0;
   a.lim = split_limits(p.S, topk);
-  char* w = static_cast<char*>(ws);
-  a.err = w ? reinterpret_cast<uint32_t*>(w) : nullptr;
-  a.counters = w ? reinterpret_cast<uint32_t*>(w + kHeaderBytes) : nullptr;
-  a.keys = w ? reinterpret_cast<uint64_t*>(w + keys_offset(batch)) : nullptr;
+  a.err = w.err;
+  a.counters = w.counters;
+  a.keys = w.keys;
   a.out_ids = nullptr;
   a.out_scores = nullptr;
   a.out_pages = nullptr;
@@ -1528,7 +1592,7 @@ int32_t check_call(const void* q, const void* k, const int32_t* bt, const int32_
   if (rc != MSA_OK) return rc;
   if (batch == 0) return MSA_OK;
   if (!ws || !aligned(ws, kAlign)) return MSA_ERR_INVALID_ARG;
-  if (ws_size < ws_bytes(batch, *p)) return MSA_ERR_WORKSPACE_TOO_SMALL;
+  if (ws_size < ws_bytes(batch, W, topk, num_splits)) return MSA_ERR_WORKSPACE_TOO_SMALL;
   return MSA_OK;
 }
 
@@ -1583,21 +1647,18 @@ int32_t merge_impl(const int32_t* lens, int32_t batch, int32_t W, int32_t topk, 
   if (!lens || !out_ids || !out_scores || !ws) return MSA_ERR_INVALID_ARG;
   if (!aligned(lens, 4) || !aligned(out_ids, 4) || !aligned(out_scores, 4) || !aligned(ws, kAlign))
     return MSA_ERR_INVALID_ARG;
-  if (ws_size < ws_bytes(batch, p)) return MSA_ERR_WORKSPACE_TOO_SMALL;
-  const uint64_t* keys = reinterpret_cast<const uint64_t*>(static_cast<const char*>(ws) + keys_offset(batch));
+  if (ws_size < ws_bytes(batch, W, topk, num_splits)) return MSA_ERR_WORKSPACE_TOO_SMALL;
+  const uint64_t* keys = ws_view(const_cast<void*>(ws), ws_size, keys_bytes(batch, 1, p)).keys;
   return launch_merge(keys, lens, W, 1, p, topk, out_ids, out_scores, batch, st, bt, bt_stride,
                       out_pages, out_tokens);
 }
 
 
-size_t ws_bytes_multi(int32_t batch, int32_t Q, const Plan& p) {
-  return keys_offset(batch) + (size_t)batch * p.S * Q * kHeads * p.Lk * sizeof(uint64_t);
-}
 
 VerifyArgs make_verify_args(const void* q, const void* k, const int32_t* bt, const int32_t* lens,
                             int32_t W, int32_t bt_stride, int64_t num_pages, int32_t Q, const Plan& p,
-                            int32_t topk, int32_t n_init, int32_t n_local, void* ws, int32_t batch,
-                            float k_scale = 1.0f) {
+                            int32_t topk, int32_t n_init, int32_t n_local, const WsView& w,
+                            int32_t batch, float k_scale = 1.0f) {
   VerifyArgs a;
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint8_t*>(k);
@@ -1614,10 +1675,9 @@ VerifyArgs make_verify_args(const void* q, const void* k, const int32_t* bt, con
   a.topk = topk;
   a.n_init = n_init;
   a.n_local = n_local;
-  char* w = static_cast<char*>(ws);
-  a.err = w ? reinterpret_cast<uint32_t*>(w) : nullptr;
-  a.keys = w ? reinterpret_cast<uint64_t*>(w + keys_offset(batch)) : nullptr;
-  a.counters = w ? reinterpret_cast<uint32_t*>(w + kHeaderBytes) : nullptr;
+  a.err = w.err;
+  a.keys = w.keys;
+  a.counters = w.counters;
   a.scores = nullptr;
   a.out_ids = nullptr;
   a.out_scores = nullptr;
@@ -1665,9 +1725,11 @@ int32_t verify_decode_impl(const void* q, const void* k_cache, bool fp8, float k
   if (batch == 0) return MSA_OK;
   if (!out_ids || !out_scores || !aligned(out_ids, 4) || !aligned(out_scores, 4)) return MSA_ERR_INVALID_ARG;
   if (!workspace || !aligned(workspace, kAlign)) return MSA_ERR_INVALID_ARG;
-  if (workspace_bytes < ws_bytes_multi(batch, qlen, p)) return MSA_ERR_WORKSPACE_TOO_SMALL;
+  if (workspace_bytes < ws_bytes(batch, W, topk, num_splits, qlen)) return MSA_ERR_WORKSPACE_TOO_SMALL;
   VerifyArgs a = make_verify_args(q, k_cache, block_table, seq_lens, W, bt_stride, num_pages, qlen,
-                                  p, topk, n_init, n_local, workspace, batch, k_scale);
+                                  p, topk, n_init, n_local,
+                                  ws_view(workspace, workspace_bytes, keys_bytes(batch, qlen, p)), batch,
+                                  k_scale);
   const int grid = p.device ? p.grid : 0;
   if (qlen == 1 && fuse_verify(p, topk)) {  // one position, few lists: merge in the same launch
     a.out_ids = out_ids;
@@ -1692,7 +1754,7 @@ int32_t verify_scores_impl(const void* q, const void* k_cache, bool fp8, float k
   if (batch == 0 || W == 0) return MSA_OK;
   if (!out || !aligned(out, 4)) return MSA_ERR_INVALID_ARG;
   VerifyArgs a = make_verify_args(q, k_cache, block_table, seq_lens, W, bt_stride, num_pages, qlen, p,
-                                  16, 0, 0, nullptr, batch, k_scale);
+                                  16, 0, 0, WsView{nullptr, nullptr, nullptr}, batch, k_scale);
   a.scores = out;
   launch_verify<kScores>(a, fp8, batch, st);
   return hipGetLastError() == hipSuccess ? MSA_OK : MSA_ERR_HIP;
@@ -1715,8 +1777,10 @@ int32_t decode_impl(const void* q, const void* k_cache, const int32_t* block_tab
   if (batch > 0 && (rc = check_pages(out_pages, out_tokens, block_table, W, num_pages)) != MSA_OK)
     return rc;
   if (batch == 0) return MSA_OK;
+  const size_t kb = keys_bytes(batch, 1, p);
+  const WsView w = ws_view(workspace, workspace_bytes, kb);
   SplitArgs a = make_split_args(q, k_cache, block_table, seq_lens, W, bt_stride, num_pages, p, topk,
-                                n_init, n_local, workspace, batch);
+                                n_init, n_local, w, batch);
   if (p.fused) {
     a.out_ids = out_ids;
     a.out_scores = out_scores;
@@ -1725,8 +1789,8 @@ int32_t decode_impl(const void* q, const void* k_cache, const int32_t* block_tab
     return launch_split<kFused>(a, batch, engine, fused_lds_bytes(p, topk), st, p.device ? p.grid : 0);
   }
   if ((rc = launch_split<kSplit>(a, batch, engine, 0, st)) != MSA_OK) return rc;
-  return merge_impl(seq_lens, batch, W, topk, out_ids, out_scores, workspace, workspace_bytes,
-                    num_splits, st, block_table, bt_stride, out_pages, out_tokens);
+  return launch_merge(w.keys, seq_lens, W, 1, p, topk, out_ids, out_scores, batch, st, block_table,
+                      bt_stride, out_pages, out_tokens);
 }
 
 }  // namespace
@@ -1766,10 +1830,9 @@ int32_t msa_indexer_plan(int32_t batch, int32_t max_blocks_per_seq, int32_t topk
 
 size_t msa_indexer_workspace_bytes(int32_t batch, int32_t max_blocks_per_seq, int32_t topk,
                                    int32_t num_splits) {
-  Plan p, d;
-  if (make_plan(batch, max_blocks_per_seq, topk, num_splits, &p) != MSA_OK) return 0;
-  if (make_decode_plan(batch, max_blocks_per_seq, topk, num_splits, &d) != MSA_OK) return 0;
-  return std::max(ws_bytes(batch, p), ws_bytes(batch, d));  // the decode and the stage calls
+  Plan p;
+  if (make_decode_plan(batch, max_blocks_per_seq, topk, num_splits, &p) != MSA_OK) return 0;
+  return ws_bytes(batch, max_blocks_per_seq, topk, num_splits);
 }
 
 int32_t msa_indexer_split_topk(const void* q, const void* k_cache, const int32_t* block_table,
@@ -1784,8 +1847,9 @@ int32_t msa_indexer_split_topk(const void* q, const void* k_cache, const int32_t
   if (rc != MSA_OK) return rc;
   if (engine < MSA_ENGINE_DEFAULT || engine > MSA_ENGINE_MFMA) return MSA_ERR_INVALID_ARG;
   if (batch == 0) return MSA_OK;
-  const SplitArgs a = make_split_args(q, k_cache, block_table, seq_lens, max_blocks_per_seq,
-                                      bt_stride, num_pages, p, topk, n_init, n_local, workspace, batch);
+  const SplitArgs a = make_split_args(q, k_cache, block_table, seq_lens, max_blocks_per_seq, bt_stride,
+                                      num_pages, p, topk, n_init, n_local,
+                                      ws_view(workspace, workspace_bytes, keys_bytes(batch, 1, p)), batch);
   return launch_split<kSplit>(a, batch, engine, 0, static_cast<hipStream_t>(stream));
 }
 
@@ -1884,27 +1948,31 @@ int32_t msa_indexer_block_scores(const void* q, const void* k_cache, const int32
   if (batch == 0 || max_blocks_per_seq == 0) return MSA_OK;
   if (!out || !aligned(out, 4)) return MSA_ERR_INVALID_ARG;
   SplitArgs a = make_split_args(q, k_cache, block_table, seq_lens, max_blocks_per_seq, bt_stride,
-                                num_pages, p, 16, 0, 0, nullptr, batch);
+                                num_pages, p, 16, 0, 0, WsView{nullptr, nullptr, nullptr}, batch);
   a.scores = out;
   return launch_split<kScores>(a, batch, engine, 0, static_cast<hipStream_t>(stream));
 }
 
 int32_t msa_indexer_read_error(void* workspace, uint32_t* host_flags, void* stream) {
-  if (!workspace || !host_flags) return MSA_ERR_INVALID_ARG;
-  if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return MSA_ERR_HIP;
-  if (hipMemcpy(host_flags, workspace, sizeof(uint32_t), hipMemcpyDeviceToHost) != hipSuccess)
+  if (!workspace || !host_flags || !aligned(workspace, kAlign)) return MSA_ERR_INVALID_ARG;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  uint32_t* hdr = static_cast<uint32_t*>(workspace);
+  // Read and clear in one atomic step on the caller's stream (so a bit a kernel sets between
+  // the read and the clear cannot be lost, and the clear is ordered before the stream's next
+  // kernel), then copy the staged word out.
+  hipLaunchKernelGGL(take_error_kernel, dim3(1), dim3(1), 0, st, hdr);
+  if (hipGetLastError() != hipSuccess) return MSA_ERR_HIP;
+  if (hipMemcpyAsync(host_flags, hdr + 1, sizeof(uint32_t), hipMemcpyDeviceToHost, st) != hipSuccess)
     return MSA_ERR_HIP;
-  if (hipMemset(workspace, 0, sizeof(uint32_t)) != hipSuccess) return MSA_ERR_HIP;
-  return MSA_OK;
+  return hipStreamSynchronize(st) == hipSuccess ? MSA_OK : MSA_ERR_HIP;
 }
 
 size_t msa_indexer_workspace_bytes_multi(int32_t batch, int32_t max_blocks_per_seq, int32_t qlen,
                                          int32_t topk, int32_t num_splits) {
-  Plan p, d;
+  Plan p;
   if (qlen < 1 || qlen > MSA_MAX_QUERY_LEN) return 0;
-  if (make_plan(batch, max_blocks_per_seq, topk, num_splits, &p) != MSA_OK) return 0;
-  if (make_decode_plan(batch, max_blocks_per_seq, topk, num_splits, &d) != MSA_OK) return 0;
-  return std::max(ws_bytes_multi(batch, qlen, p), ws_bytes_multi(batch, qlen, d));
+  if (make_decode_plan(batch, max_blocks_per_seq, topk, num_splits, &p) != MSA_OK) return 0;
+  return ws_bytes(batch, max_blocks_per_seq, topk, num_splits, qlen);
 }
 
 int32_t msa_indexer_decode_multi(const void* q, const void* k_cache, const int32_t* block_table,

@@ -72,16 +72,38 @@ def test_split_plan(lib):
 
 def test_workspace_size(lib):
     ws = lib.msa_indexer_workspace_bytes
-    # error word (256 B), 17 256-byte counter lines per row (CTR), then the keys: the larger
-    # of the device plan (S = min(64, ceil(W/4)) lists of topk keys per row and head, which
-    # any of its split widths fits) and the host plan (the stage calls)
+    # error word (256 B), 17 256-byte counter lines per row (CTR), then the keys: per row, the
+    # most any plan of this (W, topk, num_splits) may write at any batch size. Automatic split
+    # counts: the device plan (S = min(64, ceil(W/4)) lists of topk keys per row and head, which
+    # any of its split widths fits) or a host plan of 4 .. 64 blocks per split.
     assert ws(32, 1024, 16, 0) == 256 + 32 * CTR + 32 * 64 * 4 * 16 * 8
     assert ws(32, 1024, 16, 32) == 256 + 32 * CTR + 32 * 32 * 4 * 16 * 8
-    # small tables (batch * W < 8192 blocks) keep the host plan: 4-block splits keep 4 keys
-    assert ws(16, 68, 16, 0) == 256 + 16 * CTR + 16 * 17 * 4 * 4 * 8
+    # batch 16 x 68 blocks runs the host plan, but a larger batch of the same width would
+    # take the device plan (17 lists of 16 keys per head), so the rows are sized for it
+    assert ws(16, 68, 16, 0) == 256 + 16 * CTR + 16 * 17 * 4 * 16 * 8
     assert ws(16, 68, 16, 17) == 256 + 16 * CTR + 16 * 17 * 4 * 4 * 8   # 4-block splits keep 4 keys
+    # past the device plan's widths (W > 4096): the host plan of the smallest split width
+    assert ws(1, 8192, 16, 0) == 256 + CTR + 256 * 4 * 16 * 8
     assert ws(0, 1024, 16, 0) == 256
     assert ws(1, 8, 0, 0) == 0
+
+
+@pytest.mark.parametrize("W,topk,splits", [(1024, 16, 0), (68, 16, 0), (200, 16, 7), (4097, 16, 0),
+                                           (300, 64, 0), (5, 3, 0), (16384, 16, 0), (0, 16, 0)])
+def test_workspace_keys_grow_linearly_with_batch(lib, W, topk, splits):
+    # The key region is batch times a per-row bound that does not depend on the batch (rounded
+    # up to 256 bytes), single-token and multi-token alike: a buffer sized for the largest batch
+    # of a shape then holds every smaller batch's keys clear of the larger batch's counter lines.
+    for qlen in (0, 1, 4):
+        if qlen == 0:
+            size = lambda b: lib.msa_indexer_workspace_bytes(b, W, topk, splits)
+        else:
+            size = lambda b, q=qlen: lib.msa_indexer_workspace_bytes_multi(b, W, q, topk, splits)
+        per_row = (size(256) - 256 - 256 * CTR) // 256
+        assert per_row > 0
+        for b in (1, 2, 3, 4, 7, 8, 31, 64, 100):
+            keys = size(b) - 256 - b * CTR
+            assert keys == -(-b * per_row // 256) * 256, (qlen, b)
 
 
 def test_plan_fuses_the_merge_when_it_fits(lib):
@@ -270,8 +292,11 @@ def test_decode_multi_rejects_on_host(lib, kw, code):
 
 def test_decode_multi_workspace_and_no_op(lib):
     ws = lib.msa_indexer_workspace_bytes_multi
-    # header, counter lines, then keys [batch][S][qlen*4][Lk]: 8 blocks -> 2 splits of 4, Lk 4
-    assert ws(2, 8, 4, 16, 0) == 256 + 2 * CTR + 2 * 2 * 16 * 4 * 8
+    # header, counter lines, then keys [batch][S][qlen*4][Lk]: an 8-block table runs 2 splits of
+    # 4 blocks (Lk 4) at batch 2, but the rows are sized for the device plan a larger batch of
+    # the same width takes (2 lists of topk keys per task)
+    assert ws(2, 8, 4, 16, 0) == 256 + 2 * CTR + 2 * 2 * 16 * 16 * 8
+    assert ws(2, 8, 4, 16, 2) == 256 + 2 * CTR + 2 * 2 * 16 * 4 * 8
     # with num_splits = 0 the device plan (S = 64 list slots of topk keys per row and head)
     assert ws(32, 1024, 4, 16, 0) == 256 + 32 * CTR + 32 * 64 * 16 * 16 * 8
     assert ws(32, 1024, 1, 16, 0) == 256 + 32 * CTR + 32 * 64 * 4 * 16 * 8

@@ -329,8 +329,8 @@ def test_workspace_reuse_and_counter_reset(msa):
 
 
 def test_default_workspace_is_reused(msa):
-    # Calls that pass no workspace share one per (device, stream, size); the library leaves
-    # its counters at zero, so repeated calls with changing lengths stay exact.
+    # Calls that pass no workspace share one per (device, stream); the library leaves its
+    # counters at zero, so repeated calls with changing lengths stay exact.
     from sparse_attention_block_amd import _lib
     inp = synth.paged_case(112, [128 * 40] * 5, 40)
     q, k, bt, lens = to_device(inp)
@@ -348,8 +348,8 @@ def test_default_workspace_is_reused(msa):
         ids2, sc2 = msa.msa_indexer_decode(q, k, bt, lens)
     torch.cuda.synchronize()
     assert torch.equal(ids2, ids) and torch.equal(sc2, sc)
-    for (_, _, batch, _), ws in _lib._WS_CACHE.items():  # every cached counter line is zero
-        assert int(ws[256:256 + CTR * batch].view(torch.int32).abs().sum()) == 0
+    for ws, rows, _ in _lib._WS_CACHE.values():  # every cached counter line is zero
+        assert int(ws[256:256 + CTR * rows].view(torch.int32).abs().sum()) == 0
 
 
 def test_decode_engines_agree_on_exact_data(msa):
