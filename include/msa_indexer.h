@@ -181,6 +181,34 @@ int32_t msa_indexer_decode(const void *q, const void *k_cache, const int32_t *bl
                            int32_t n_local, int32_t *out_ids, float *out_scores, void *workspace,
                            size_t workspace_bytes, int32_t num_splits, void *stream);
 
+/* Limits of msa_indexer_decode_noalloc's scratch array (one per GPU). */
+#define MSA_NOALLOC_SCRATCH_BYTES (16u << 20)  /* 16 MiB */
+#define MSA_NOALLOC_MAX_BATCH 256
+
+/*
+ * msa_indexer_decode for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same pass and results,
+ * with the library's own scratch array in place of the workspace. Allocates nothing (no
+ * hipMalloc, hipFree or allocating library routine). The array is a file-scope device array of
+ * MSA_NOALLOC_SCRATCH_BYTES on each GPU, held until the process ends: the first
+ * MSA_WORKSPACE_HEADER_BYTES + MSA_NOALLOC_MAX_BATCH * MSA_WORKSPACE_ROW_BYTES bytes are the
+ * row counters, the rest holds the keys. Calls with batch > MSA_NOALLOC_MAX_BATCH, or whose
+ * keys (batch * S * 4 * Lk * 8 bytes for the call's plan) exceed the rest, return
+ * MSA_ERR_WORKSPACE_TOO_SMALL and enqueue nothing; at the default plan this admits batch 256 at
+ * up to 4096 blocks per row (a row's keys are at most 32 KiB under the device plan).
+ * The first call on a device looks the array up and clears its counters on `stream`. Every
+ * call on a GPU shares that GPU's array and leaves its counters at zero, so calls that overlap
+ * on one GPU (concurrent streams, threads or processes' graphs) race: serialize them.
+ *   error_flags  optional device uint32 (NULL: not kept): MSA_DEVERR_* bits are OR-ed into it,
+ *                as into a workspace's error word; the caller reads and clears it.
+ * Every other argument as in msa_indexer_decode.
+ */
+int32_t msa_indexer_decode_noalloc(const void *q, const void *k_cache, const int32_t *block_table,
+                                   const int32_t *seq_lens, int32_t batch, int32_t max_blocks_per_seq,
+                                   int32_t bt_stride, int64_t num_pages, int32_t topk, int32_t n_init,
+                                   int32_t n_local, int32_t *out_ids, float *out_scores,
+                                   uint32_t *error_flags, int32_t num_splits, void *stream);
+
 /*
  * msa_indexer_decode with an explicit scoring engine (MSA_ENGINE_*): for measuring the
  * engines against each other on the whole pass. msa_indexer_decode uses MSA_ENGINE_DEFAULT,

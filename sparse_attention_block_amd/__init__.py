@@ -16,6 +16,7 @@ from ._lib import (  # noqa: F401
     msa_indexer_decode,
     msa_indexer_decode_fp8,
     msa_indexer_decode_multi,
+    msa_indexer_decode_noalloc,
     msa_indexer_decode_pages,
     msa_indexer_expand_pages,
     msa_indexer_expand_pages_multi,

@@ -43,6 +43,8 @@ _SIGNATURES = {
     "msa_indexer_plan": ([_I32, _I32, _I32, _I32, _P, _P, _P, _P], _I32),
     "msa_indexer_decode": ([_P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32, _I32, _P, _P, _P,
                             _SZ, _I32, _P], _I32),
+    "msa_indexer_decode_noalloc": ([_P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32, _I32, _P, _P,
+                                    _P, _I32, _P], _I32),
     "msa_indexer_decode_engine": ([_P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32, _I32, _P, _P,
                                    _P, _SZ, _I32, _I32, _P], _I32),
     "msa_indexer_decode_pages": ([_P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32, _I32, _P, _P,
@@ -263,6 +265,30 @@ def msa_indexer_decode(q, k_cache, block_table, seq_lens, topk=16, n_init=1, n_l
     else:
         rc = load().msa_indexer_decode_engine(*args, engine, _stream(stream))
         _check("msa_indexer_decode_engine", rc)
+    return out_ids, out_scores
+
+
+@_on_tensor_device
+def msa_indexer_decode_noalloc(q, k_cache, block_table, seq_lens, topk=16, n_init=1, n_local=2,
+                               out_ids=None, out_scores=None, error_flags=None, num_splits=0,
+                               stream=None):
+    """The decode pass on the library's own scratch array instead of a workspace (the library
+    allocates nothing; pass out_ids / out_scores to allocate nothing here either).
+    error_flags: optional int32 [1] device tensor the device error bits are OR-ed into.
+    Returns (out_ids, out_scores)."""
+    torch = _torch()
+    (pq, pk, pbt, pl), B, W, stride, pages = _inputs(q, k_cache, block_table, seq_lens)
+    if out_ids is None:
+        out_ids = torch.empty((B, HEADS, topk), dtype=torch.int32, device=q.device)
+    if out_scores is None:
+        out_scores = torch.empty((B, HEADS, topk), dtype=torch.float32, device=q.device)
+    flags = _P(None) if error_flags is None else _dev(error_flags, "error_flags", torch.int32, (1,))
+    rc = load().msa_indexer_decode_noalloc(
+        pq, pk, pbt, pl, B, W, stride, pages, topk, n_init, n_local,
+        _dev(out_ids, "out_ids", torch.int32, (B, HEADS, topk)),
+        _dev(out_scores, "out_scores", torch.float32, (B, HEADS, topk)), flags, num_splits,
+        _stream(stream))
+    _check("msa_indexer_decode_noalloc", rc)
     return out_ids, out_scores
 
 

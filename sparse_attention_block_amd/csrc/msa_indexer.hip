@@ -28,9 +28,16 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "msa_indexer.h"
+
+// The workspace of the allocation-free decode (msa_indexer_decode_noalloc): one copy of this
+// array on every GPU the library runs on, held until the process ends, shared by every such
+// call on that GPU. In host code the name stands for a host-side shadow, not device memory:
+// host code only ever uses the address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[MSA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -1584,13 +1591,13 @@ SplitArgs make_split_args(const void* q, const void* k, const int32_t* bt, const
 int32_t check_call(const void* q, const void* k, const int32_t* bt, const int32_t* lens,
                    int32_t batch, int32_t W, int32_t bt_stride, int64_t num_pages, int32_t topk,
                    int32_t n_init, int32_t n_local, const void* ws, size_t ws_size,
-                   int32_t num_splits, Plan* p, bool decode = false) {
+                   int32_t num_splits, Plan* p, bool decode = false, bool check_ws = true) {
   int32_t rc = check_inputs(q, k, bt, lens, batch, W, bt_stride, num_pages);
   if (rc != MSA_OK) return rc;
   if ((rc = check_select(topk, n_init, n_local)) != MSA_OK) return rc;
   rc = decode ? make_decode_plan(batch, W, topk, num_splits, p) : make_plan(batch, W, topk, num_splits, p);
   if (rc != MSA_OK) return rc;
-  if (batch == 0) return MSA_OK;
+  if (batch == 0 || !check_ws) return MSA_OK;
   if (!ws || !aligned(ws, kAlign)) return MSA_ERR_INVALID_ARG;
   if (ws_size < ws_bytes(batch, W, topk, num_splits)) return MSA_ERR_WORKSPACE_TOO_SMALL;
   return MSA_OK;
@@ -1760,25 +1767,75 @@ int32_t verify_scores_impl(const void* q, const void* k_cache, bool fp8, float k
   return hipGetLastError() == hipSuccess ? MSA_OK : MSA_ERR_HIP;
 }
 
+// The allocation-free decode: the library's scratch array stands in for the workspace.
+struct ScratchUse {
+  uint32_t* err;  // the caller's device error word (may be null: bits are then not kept)
+};
+
+constexpr int kMaxDevices = 64;
+constexpr size_t kNoallocBytes = MSA_NOALLOC_SCRATCH_BYTES;
+constexpr int32_t kNoallocMaxBatch = MSA_NOALLOC_MAX_BATCH;
+
+std::mutex g_scratch_mu;
+char* g_scratch[kMaxDevices];  // the scratch array's device address, per device (null: not set up)
+
+__global__ void zero_words_kernel(uint32_t* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+// The scratch array's address on the current device. The first call on a device looks it up
+// with that device current and clears the header and every counter line on `st` (the loader
+// zero-fills the array too; the counters then return to zero at the end of every call).
+int32_t scratch_on_current_device(hipStream_t st, char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MSA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MSA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return MSA_ERR_HIP;
+    const size_t words = counters_end(kNoallocMaxBatch) / sizeof(uint32_t);
+    hipLaunchKernelGGL(zero_words_kernel, dim3(256), dim3(256), 0, st, static_cast<uint32_t*>(ptr), words);
+    if (hipGetLastError() != hipSuccess) return MSA_ERR_HIP;
+    g_scratch[dev] = static_cast<char*>(ptr);
+  }
+  *out = g_scratch[dev];
+  return MSA_OK;
+}
+
 int32_t decode_impl(const void* q, const void* k_cache, const int32_t* block_table,
                     const int32_t* seq_lens, int32_t batch, int32_t W, int32_t bt_stride,
                     int64_t num_pages, int32_t topk, int32_t n_init, int32_t n_local,
                     int32_t* out_ids, float* out_scores, int32_t* out_pages, int32_t* out_tokens,
                     void* workspace, size_t workspace_bytes, int32_t num_splits, int32_t engine,
-                    hipStream_t st) {
-  // Check everything (outputs included) before the first launch.
+                    hipStream_t st, const ScratchUse* scratch = nullptr) {
+  // Check everything (outputs included) before the first HIP call.
   if (batch > 0 && (!out_ids || !out_scores || !aligned(out_ids, 4) || !aligned(out_scores, 4)))
     return MSA_ERR_INVALID_ARG;
   if (engine < MSA_ENGINE_DEFAULT || engine > MSA_ENGINE_MFMA) return MSA_ERR_INVALID_ARG;
   Plan p;
   int32_t rc = check_call(q, k_cache, block_table, seq_lens, batch, W, bt_stride, num_pages, topk,
-                          n_init, n_local, workspace, workspace_bytes, num_splits, &p, true);
+                          n_init, n_local, workspace, workspace_bytes, num_splits, &p, true,
+                          scratch == nullptr);
   if (rc != MSA_OK) return rc;
   if (batch > 0 && (rc = check_pages(out_pages, out_tokens, block_table, W, num_pages)) != MSA_OK)
     return rc;
   if (batch == 0) return MSA_OK;
   const size_t kb = keys_bytes(batch, 1, p);
-  const WsView w = ws_view(workspace, workspace_bytes, kb);
+  WsView w;
+  if (scratch != nullptr) {
+    // The scratch keeps counter lines for kNoallocMaxBatch rows and the keys after them, a
+    // fixed split, so no shape can lay keys over another's counters.
+    if (batch > kNoallocMaxBatch || kb > kNoallocBytes - counters_end(kNoallocMaxBatch))
+      return MSA_ERR_WORKSPACE_TOO_SMALL;
+    char* base = nullptr;
+    if ((rc = scratch_on_current_device(st, &base)) != MSA_OK) return rc;
+    w = ws_view(base, kNoallocBytes, kb);
+    w.err = scratch->err;
+  } else {
+    w = ws_view(workspace, workspace_bytes, kb);
+  }
   SplitArgs a = make_split_args(q, k_cache, block_table, seq_lens, W, bt_stride, num_pages, p, topk,
                                 n_init, n_local, w, batch);
   if (p.fused) {
@@ -1883,6 +1940,19 @@ int32_t msa_indexer_decode(const void* q, const void* k_cache, const int32_t* bl
                      num_pages, topk, n_init, n_local, out_ids, out_scores, nullptr, nullptr,
                      workspace, workspace_bytes, num_splits, MSA_ENGINE_DEFAULT,
                      static_cast<hipStream_t>(stream));
+}
+
+int32_t msa_indexer_decode_noalloc(const void* q, const void* k_cache, const int32_t* block_table,
+                                   const int32_t* seq_lens, int32_t batch, int32_t max_blocks_per_seq,
+                                   int32_t bt_stride, int64_t num_pages, int32_t topk, int32_t n_init,
+                                   int32_t n_local, int32_t* out_ids, float* out_scores,
+                                   uint32_t* error_flags, int32_t num_splits, void* stream) {
+  if (error_flags != nullptr && !aligned(error_flags, 4)) return MSA_ERR_INVALID_ARG;
+  const ScratchUse use{error_flags};
+  return decode_impl(q, k_cache, block_table, seq_lens, batch, max_blocks_per_seq, bt_stride,
+                     num_pages, topk, n_init, n_local, out_ids, out_scores, nullptr, nullptr,
+                     nullptr, kNoallocBytes, num_splits, MSA_ENGINE_DEFAULT,
+                     static_cast<hipStream_t>(stream), &use);
 }
 
 int32_t msa_indexer_decode_pages(const void* q, const void* k_cache, const int32_t* block_table,

@@ -170,6 +170,40 @@ def test_batch_zero_is_a_no_op(lib):
                    ws=None, ws_bytes=0) == OK
 
 
+def _decode_noalloc(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, bt=FAKE, lens=FAKE, batch=2, W=8, stride=8, pages=16, topk=16,
+             n_init=1, n_local=2, ids=FAKE, scores=FAKE, flags=None, splits=0, stream=None)
+    a.update(kw)
+    return lib.msa_indexer_decode_noalloc(a["q"], a["k"], a["bt"], a["lens"], a["batch"], a["W"],
+                                          a["stride"], a["pages"], a["topk"], a["n_init"],
+                                          a["n_local"], a["ids"], a["scores"], a["flags"],
+                                          a["splits"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INVALID),
+    (dict(lens=None), INVALID),
+    (dict(ids=None), INVALID),
+    (dict(scores=FAKE + 2), INVALID),
+    (dict(flags=FAKE + 2), INVALID),        # the optional error word must be 4-byte aligned
+    (dict(topk=65), INVALID),
+    (dict(n_init=10, n_local=7), INVALID),
+    (dict(W=16385, stride=16385), UNSUPPORTED),
+    # the scratch array's limits: 256 rows, and the keys after their counter lines
+    (dict(batch=257), WS_SMALL),
+    (dict(batch=200, W=16384, stride=16384), WS_SMALL),  # 128 KiB of keys per row
+])
+def test_decode_noalloc_rejects_on_host(lib, kw, code):
+    # The allocation-free decode checks every argument, and its scratch limits, before it
+    # touches the device (its scratch set-up included).
+    assert _decode_noalloc(lib, **kw) == code
+
+
+def test_decode_noalloc_batch_zero_is_a_no_op(lib):
+    assert _decode_noalloc(lib, batch=0, q=None, k=None, bt=None, lens=None, ids=None,
+                           scores=None) == OK
+
+
 def test_stage_entry_points_reject_on_host(lib):
     st = lib.msa_indexer_split_topk(FAKE, FAKE, FAKE, FAKE, 2, 8, 8, 16, 16, 1, 2, FAKE, 1 << 20,
                                     0, 7, None)
