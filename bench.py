@@ -2,22 +2,29 @@
 """Decode-step benchmark of the MiniMax-M3 lightning-indexer pass on one MI355X.
 
 One step = one msa_indexer_decode call (a single kernel launch: split scoring, per-split
-top-16, and the exact merge by each row's last split) over batch 32 x 131072-token rows (1024 blocks of 128
-tokens each, 1 GiB of bf16 index-K behind a shuffled block table), 4 index heads x 128,
-top-16 with 1 initial and 2 recent blocks pinned. Inputs are seeded synthetic data,
+top-16, and the exact merge by each row's last split) over batch 32 x 131072-token rows (1024
+blocks of 128 tokens each, 1 GiB of bf16 index-K behind a shuffled block table), 4 index heads
+x 128, top-16 with 1 initial and 2 recent blocks pinned. Inputs are seeded synthetic data,
 resident in HBM before timing starts.
 
-Prints one JSON line: the metric is index-K GB/s (bytes = sum seq_len * 128 * 2 per step)
-with us/step beside it, a roofline object for the dominant kernel (the fused decode kernel,
-timed with HIP events on the launch stream), and the CPU oracle's rate on the same workload.
+Prints one JSON line: the metric is index-K GB/s (bytes = sum seq_len * 128 * 2 per step) with
+us/step beside it; a roofline object for the dominant kernel (the fused decode kernel: HIP
+events on its launch stream around the same K back-to-back launches the step time covers);
+`extra` rows timed the same way for the other passes the pages measure (the FP8 cache, four
+draft positions, the four smaller workloads, the streaming ceiling); and the CPU oracle's rate
+on the same workload. Every timed pass's last outputs are checked against the selection the
+pass defines over the GPU's own block scores (ids and scores), and the headline's against the
+fp64 oracle in the CPU leg; a failed check makes the run exit non-zero.
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
 import statistics
+import subprocess
 import sys
 import time
 
@@ -28,6 +35,9 @@ METRIC = "µs/decode step + index-K GB/s (% of 8 TB/s) at batch 32 × 128K ctx"
 HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCE = os.path.join(ROOT, "sparse_attention_block_amd", "csrc", "msa_indexer.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_split_kernel_b32_128k.json")
+GRAPH_PROTOCOL = "8 calls per HIP graph, 100 replays per round, median of 7 rounds"
+
+FAILED_CHECKS: list[str] = []
 
 
 def log(msg: str) -> None:
@@ -48,8 +58,8 @@ def kernel_source_hash() -> str:
 
 
 def measured_traffic(engine: int):
-    """HBM bytes per stage-1 launch from the committed rocprofv3 counter runs, if they were
-    taken on the current kernel source; otherwise None."""
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they were taken on
+    the current kernel source; otherwise None."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
@@ -86,7 +96,40 @@ def graph_us_per_call(torch, fn, calls: int = 8, replays: int = 100, rounds: int
     return statistics.median(per_call)
 
 
+def timed_steps(torch, step, steps: int, warmup: int):
+    """`warmup` untimed steps, then exactly `steps` back-to-back steps bracketed by device
+    synchronizations, with one HIP event pair on the launch stream around them (nothing is
+    enqueued between the launches). Returns (wall us per step, event us per step): the event
+    time covers the launches alone, so it cannot exceed the wall time."""
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall * 1e6 / steps, e0.elapsed_time(e1) * 1e3 / steps
+
+
+def rate(nbytes: int, us: float) -> dict:
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"us": round(us, 2), "GBs": round(gbs, 1), "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2)}
+
+
 def cpu_model() -> str:
+    """The host CPU's model name as lscpu reports it (/proc/cpuinfo if lscpu is missing)."""
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.strip().startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
     try:
         for line in open("/proc/cpuinfo"):
             if line.startswith("model name"):
@@ -96,28 +139,115 @@ def cpu_model() -> str:
     return "unknown"
 
 
+# ---------------------------------------------------------------------------
+# Output checks (no oracle): the selection the pass defines over the GPU's own fp32 block scores.
+
+def selection_mismatches(ids, sc, scores, lens, topk: int, n_init: int, n_local: int) -> int:
+    """Rows (b, h) whose ids / scores differ from the selection over `scores` [B, 4, W] (fp32
+    block scores of the same call): the first m = min(topk, nb) blocks in the order (pinned
+    first, then higher score, then lower id; -0 equals +0), reported scores equal to those block
+    scores bit for bit, then -1 / -inf."""
+    import numpy as np
+    B, H, W = scores.shape
+    L = np.clip(np.asarray(lens, dtype=np.int64), 0, W * 128)
+    bad = 0
+    for b in range(B):
+        n = int((L[b] + 127) // 128)
+        m = min(topk, n)
+        j = np.arange(n)
+        not_pinned = ~((j < n_init) | (j >= n - n_local))
+        for h in range(H):
+            s = scores[b, h, :n].astype(np.float64)
+            want = np.lexsort((j, -s, not_pinned))[:m]
+            ok = (np.array_equal(ids[b, h, :m], want) and np.all(ids[b, h, m:] == -1)
+                  and np.array_equal(sc[b, h, :m], scores[b, h, want])  # values: -0 equals +0
+                  and np.all(np.isneginf(sc[b, h, m:])))
+            bad += int(not ok)
+    return bad
+
+
+def check(name: str, bad: int, rows: int) -> dict:
+    ok = bad == 0
+    if not ok:
+        FAILED_CHECKS.append(f"{name}: {bad} of {rows} (row, head) selections differ")
+        log(f"OUTPUT CHECK FAILED: {FAILED_CHECKS[-1]}")
+    return {"ok": ok, "rows_checked": rows, "rows_differing": bad,
+            "against": "the selection over the GPU's own fp32 block scores"}
+
+
+def check_single(msa, q, k, bt, lens, ids, sc, topk, n_init, n_local, name):
+    s = msa.msa_indexer_block_scores(q, k, bt, lens).cpu().numpy()
+    bad = selection_mismatches(ids.cpu().numpy(), sc.cpu().numpy(), s, lens.cpu().numpy(), topk,
+                               n_init, n_local)
+    return check(name, bad, s.shape[0] * 4)
+
+
+def check_multi(scores_fn, ids, sc, lens, topk, n_init, n_local, name):
+    """Each position p of a multi-token / FP8 call over its causal length L - (Q-1-p)."""
+    import numpy as np
+    s = scores_fn().cpu().numpy()  # [B, Q, 4, W]
+    Q = s.shape[1]
+    ids, sc, L = ids.cpu().numpy(), sc.cpu().numpy(), lens.cpu().numpy().astype(np.int64)
+    bad = sum(selection_mismatches(ids[:, p], sc[:, p], s[:, p], np.maximum(L - (Q - 1 - p), 0), topk,
+                                   n_init, n_local) for p in range(Q))
+    return check(name, bad, s.shape[0] * Q * 4)
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline (the oracle) and its agreement with the GPU's headline outputs.
+
 def _oracle_passes(inp, budget_s: float, min_repeats: int):
     import oracle
-    times = []
+    times, last = [], None
     t_start = time.perf_counter()
     while len(times) < min_repeats or time.perf_counter() - t_start < budget_s:
         t0 = time.perf_counter()
-        oracle.decode(inp)
+        last = oracle.decode(inp)
         times.append(time.perf_counter() - t0)
-    return len(times), statistics.median(times)
+    return len(times), statistics.median(times), last
 
 
-def cpu_baseline(inp, budget_s: float = 10.0, min_repeats: int = 3):
+def oracle_agreement(gpu_ids, ref, lens, topk, n_init, n_local, tol=1e-3) -> dict:
+    """GPU ids against the fp64 oracle: exact sets, except where the oracle's scores at the cut
+    lie within tol (then the GPU's picks must be within tol of the oracle's)."""
+    import numpy as np
+    ids_ref, _, s_ref = ref
+    B, H, W = s_ref.shape
+    nb = (np.clip(lens.astype(np.int64), 0, W * 128) + 127) // 128
+    exact, near, bad = 0, 0, 0
+    for b in range(B):
+        m = int(min(topk, nb[b]))
+        pinned = {j for j in range(int(nb[b])) if j < n_init or j >= nb[b] - n_local}
+        for h in range(H):
+            got = [int(x) for x in gpu_ids[b, h, :m]]
+            if set(got) == set(int(x) for x in ids_ref[b, h, :m]):
+                exact += 1
+                continue
+            chosen = [j for j in got if j not in pinned]
+            left = [j for j in range(int(nb[b])) if j not in set(got)]
+            ok = pinned <= set(got) and len(set(got)) == m
+            if ok and chosen and left:
+                ok = s_ref[b, h, chosen].min() >= s_ref[b, h, left].max() - tol
+            near += int(ok)
+            bad += int(not ok)
+    if bad:
+        FAILED_CHECKS.append(f"headline vs fp64 oracle: {bad} (row, head) selections beyond the near-tie rule")
+        log(f"OUTPUT CHECK FAILED: {FAILED_CHECKS[-1]}")
+    return {"ok": bad == 0, "rows_exact": exact, "rows_near_tie": near, "rows_failing": bad,
+            "rule": "equal id sets, or unselected unpinned blocks within 1e-3 of the cut"}
+
+
+def cpu_baseline(inp, gpu_ids=None, budget_s: float = 10.0, min_repeats: int = 3):
     """The oracle as it is, on this host's cores: whole passes over the workload, repeated
     until about budget_s seconds of wall time (at least min_repeats), median pass time; then
-    the same on one thread."""
+    the same on one thread. The last pass's selection is compared with the GPU's (gpu_ids)."""
     import oracle
     threads = oracle.num_threads()
-    repeats, t = _oracle_passes(inp, budget_s, min_repeats)
+    repeats, t, last = _oracle_passes(inp, budget_s, min_repeats)
     oracle.set_num_threads(1)
-    repeats1, t1 = _oracle_passes(inp, budget_s, min_repeats)
+    repeats1, t1, _ = _oracle_passes(inp, budget_s, min_repeats)
     oracle.set_num_threads(threads)
-    return {
+    out = {
         "value": round(inp.index_k_bytes / t / 1e9, 3),
         "unit": "GB/s",
         "cores": threads,
@@ -130,57 +260,81 @@ def cpu_baseline(inp, budget_s: float = 10.0, min_repeats: int = 3):
                           "ms_per_step": round(t1 * 1e3, 3), "passes": repeats1},
         "cpu_model": cpu_model(),
     }
+    if gpu_ids is not None:
+        out["gpu_vs_oracle"] = oracle_agreement(gpu_ids, last, inp.seq_lens, inp.topk, inp.n_init,
+                                                inp.n_local)
+    return out
 
 
-def time_page_table(msa, torch, args, q, k, bt, lens, ids, ws, stream, topk, n_init, n_local,
-                    engine, B):
-    """The 16-token page table on the same workload: the decode step that also writes it
-    (msa_indexer_decode_pages, one launch), and the table alone from given selections
-    (msa_indexer_expand_pages). Both are timed like the main step."""
+# ---------------------------------------------------------------------------
+# Extra rows of the default run.
+
+def probe_lib():
+    from sparse_attention_block_amd.build import probe_library_path
+    path = probe_library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build with __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    fn = lib.msa_probe_stream_pages
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                   ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    fn.restype = ctypes.c_int32
+    return fn
+
+
+def streaming_ceiling(torch, k, bt, page_bytes: int, pattern: int, blocks_per_wg: int = 64) -> float:
+    """Per-call us of the streaming probe (msa_probe.h) over the pages of k through bt, under
+    the graph protocol: the time HBM takes to serve the decode kernels' access pattern."""
+    fn = probe_lib()
+    B, W = bt.shape
+    S = -(-W // blocks_per_wg)
+    out = torch.empty(B * S * 256, dtype=torch.int32, device=k.device)
+
+    def call():
+        rc = fn(k.data_ptr(), page_bytes, bt.data_ptr(), B, W, bt.stride(0), blocks_per_wg, pattern,
+                out.data_ptr(), torch.cuda.current_stream().cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"msa_probe_stream_pages returned {rc}")
+    return graph_us_per_call(torch, call)
+
+
+def leg_multi(msa, torch, name, q, k, bt, lens, nbytes, topk, n_init, n_local, steps, warmup,
+              fp8_scale=None):
+    """A multi-token (bf16) or FP8 decode step over the benchmark's shape: back-to-back wall and
+    event time, the graph protocol, and the output check."""
+    B, Q = q.shape[0], q.shape[1]
+    W = bt.shape[1]
     dev = q.device
-    sc = torch.empty((B, 4, topk), dtype=torch.float32, device=dev)
-    pages = torch.empty((B, 4, 8 * topk), dtype=torch.int32, device=dev)
-    tokens = torch.empty((B, 4), dtype=torch.int32, device=dev)
-
-    def dp():
-        msa.msa_indexer_decode_pages(q, k, bt, lens, topk, n_init, n_local, out_ids=ids,
-                                     out_scores=sc, out_pages=pages, out_tokens=tokens,
-                                     workspace=ws, engine=engine or 0)
-
-    def ex():
-        msa.msa_indexer_expand_pages(ids, bt, lens, out_pages=pages, out_tokens=tokens)
-
-    res = {}
-    for name, fn in (("decode_pages", dp), ("expand_pages", ex)):
-        for _ in range(args.warmup):
-            fn()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            fn()
-        torch.cuda.synchronize()
-        wall_us = (time.perf_counter() - t0) * 1e6 / args.steps
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
-        for e0, e1 in ev:
-            e0.record(stream)
-            fn()
-            e1.record(stream)
-        torch.cuda.synchronize()
-        res[name] = {"us_per_call": round(wall_us, 2),
-                     "kernel_us": round(statistics.mean(e0.elapsed_time(e1) for e0, e1 in ev) * 1e3, 2)}
-    # The table alone moves ids (read), table entries (gathered), pages and counts (written).
-    res["expand_pages"]["bytes_per_call"] = B * 4 * (topk * 4 + topk * 4 + topk * 32 + 4)
-    log(f"page table: {res}")
+    ws = torch.zeros(msa.workspace_bytes_multi(B, W, Q, topk), dtype=torch.uint8, device=dev)
+    ids = torch.empty((B, Q, 4, topk), dtype=torch.int32, device=dev)
+    sc = torch.empty((B, Q, 4, topk), dtype=torch.float32, device=dev)
+    # the call marshalled once (one ctypes call per step keeps the launch queue full)
+    step = msa.bind_decode_multi(q, k, bt, lens, topk, n_init, n_local, ids, sc, ws, k_scale=fp8_scale)
+    if fp8_scale is None:  # the plain binding calls (on the current stream: graph capture)
+        call = lambda: msa.msa_indexer_decode_multi(q, k, bt, lens, topk, n_init, n_local, out_ids=ids,
+                                                    out_scores=sc, workspace=ws)
+        scores = lambda: msa.msa_indexer_block_scores_multi(q, k, bt, lens)
+    else:
+        call = lambda: msa.msa_indexer_decode_fp8(q, k, fp8_scale, bt, lens, topk, n_init, n_local,
+                                                  out_ids=ids, out_scores=sc, workspace=ws)
+        scores = lambda: msa.msa_indexer_block_scores_fp8(q, k, fp8_scale, bt, lens)
+    wall_us, ev_us = timed_steps(torch, step, steps, warmup)
+    res = {"step": rate(nbytes, wall_us), "kernels_back_to_back": rate(nbytes, ev_us)}
+    res["output_check"] = check_multi(scores, ids, sc, lens, topk, n_init, n_local, name)
+    if msa.msa_indexer_read_error(ws) != 0:
+        FAILED_CHECKS.append(f"{name}: device error flag set")
+    res["graph"] = rate(nbytes, graph_us_per_call(torch, call))
+    res["index_k_bytes"] = nbytes
+    log(f"{name}: {res['graph']}")
     return res
 
 
-def bench_configs(msa, synth, np, torch) -> int:
-    """The four smaller workloads, one JSON line each: the decode call under the graph
-    protocol on warm inputs, and cycling through enough copies of the inputs (at least 8,
-    more than 512 MB together) that no call finds its cache lines left by the previous one."""
+def leg_configs(msa, synth, np, torch) -> dict:
+    """The four smaller workloads: the decode call under the graph protocol on warm inputs and
+    cycling through enough copies of the cache (at least 8, more than 512 MB together) that no
+    call finds its lines left by the previous one."""
     dev = torch.device("cuda", 0)
-    torch.cuda.set_device(dev)
+    out = {}
     for i in (1, 2, 4, 5):
         inp = synth.config(i)
         B, W = inp.batch, inp.max_blocks
@@ -194,24 +348,64 @@ def bench_configs(msa, synth, np, torch) -> int:
         ids = torch.empty((B, 4, inp.topk), dtype=torch.int32, device=dev)
         sc = torch.empty((B, 4, inp.topk), dtype=torch.float32, device=dev)
 
-        def call(k):
-            msa.msa_indexer_decode(q, k, bt, lens, inp.topk, inp.n_init, inp.n_local, out_ids=ids,
+        def call(kc):
+            msa.msa_indexer_decode(q, kc, bt, lens, inp.topk, inp.n_init, inp.n_local, out_ids=ids,
                                    out_scores=sc, workspace=ws)
 
-        warm = graph_us_per_call(torch, lambda: call(ks[0]))
-
         def rotating():
-            for k in ks:
-                call(k)
+            for kc in ks:
+                call(kc)
+        warm = graph_us_per_call(torch, lambda: call(ks[0]))
         rot = graph_us_per_call(torch, rotating, calls=1, replays=max(1, 800 // copies)) / copies
         nbytes = inp.index_k_bytes
-        print(json.dumps({"config": i, "workload": inp.name, "index_k_bytes": nbytes,
-                          "warm_us": round(warm, 2), "rotating_us": round(rot, 2),
-                          "rotating_GBs": round(nbytes / (rot * 1e-6) / 1e9, 1),
-                          "copies": copies, "plan": msa.plan(B, W, inp.topk)}), flush=True)
+        res = {"workload": inp.name, "index_k_bytes": nbytes, "warm": rate(nbytes, warm),
+               "rotating": rate(nbytes, rot), "copies": copies, "plan": msa.plan(B, W, inp.topk)}
+        res["output_check"] = check_single(msa, q, ks[-1], bt, lens, ids, sc, inp.topk, inp.n_init,
+                                           inp.n_local, f"cfg{i}")
+        out[f"cfg{i}"] = res
+        log(f"cfg{i}: warm {res['warm']['us']} us, rotating {res['rotating']['us']} us")
         del ks
         torch.cuda.empty_cache()
-    return 0
+    return out
+
+
+def time_page_table(msa, torch, q, k, bt, lens, topk, n_init, n_local, steps, warmup):
+    """The 16-token page table on the headline workload: the decode step that also writes it
+    (msa_indexer_decode_pages, one launch), and the table alone from given selections
+    (msa_indexer_expand_pages)."""
+    B = q.shape[0]
+    dev = q.device
+    ids = torch.empty((B, 4, topk), dtype=torch.int32, device=dev)
+    sc = torch.empty((B, 4, topk), dtype=torch.float32, device=dev)
+    pages = torch.empty((B, 4, 8 * topk), dtype=torch.int32, device=dev)
+    tokens = torch.empty((B, 4), dtype=torch.int32, device=dev)
+    ws = msa.new_workspace(B, bt.shape[1], topk, 0, dev)
+
+    def dp():
+        msa.msa_indexer_decode_pages(q, k, bt, lens, topk, n_init, n_local, out_ids=ids, out_scores=sc,
+                                     out_pages=pages, out_tokens=tokens, workspace=ws)
+
+    def ex():
+        msa.msa_indexer_expand_pages(ids, bt, lens, out_pages=pages, out_tokens=tokens)
+
+    res = {}
+    for name, fn in (("decode_pages", dp), ("expand_pages", ex)):
+        wall_us, ev_us = timed_steps(torch, fn, steps, warmup)
+        res[name] = {"us_per_call": round(wall_us, 2), "kernels_back_to_back_us": round(ev_us, 2)}
+    # The table alone moves ids (read), table entries (gathered), pages and counts (written).
+    res["expand_pages"]["bytes_per_call"] = B * 4 * (topk * 4 + topk * 4 + topk * 32 + 4)
+    log(f"page table: {res}")
+    return res
+
+
+# ---------------------------------------------------------------------------
+# Other modes (one JSON line per shape).
+
+def bench_configs(msa, synth, np, torch) -> int:
+    torch.cuda.set_device(0)
+    for name, res in leg_configs(msa, synth, np, torch).items():
+        print(json.dumps({"config": name, **res}), flush=True)
+    return 0 if not FAILED_CHECKS else 1
 
 
 def bench_sweep(msa, np, torch) -> int:
@@ -270,8 +464,7 @@ def bench_sweep(msa, np, torch) -> int:
         print(json.dumps({"workload": name, "batch": B, "tokens": tokens,
                           "bf16_us": round(us, 2), "bf16_GBs": round(tokens * 256 / (us * 1e-6) / 1e9, 1),
                           "fp8_us": round(us8, 2), "fp8_GBs": round(tokens * 128 / (us8 * 1e-6) / 1e9, 1),
-                          "protocol": "8 calls per HIP graph, 100 replays per round, median of 7 rounds"}),
-              flush=True)
+                          "protocol": GRAPH_PROTOCOL}), flush=True)
     return 0
 
 
@@ -322,20 +515,18 @@ def bench_shard(args, msa, synth, np, torch) -> int:
                           "rank": r, "ranks": P, "n_init": ni, "n_local": nl,
                           "index_k_bytes": nbytes, "us_per_call": round(us, 2),
                           "GBs": round(gbs, 1), "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
-                          "plan": msa.plan(B, W, inp.topk),
-                          "protocol": "8 calls per HIP graph, 100 replays per round, median of 7 rounds"}),
+                          "plan": msa.plan(B, W, inp.topk), "protocol": GRAPH_PROTOCOL}),
               flush=True)
     return 0
 
 
 def bench_multi(args, msa, synth, np, torch) -> int:
-    """Multi-token decode step (qlen draft positions per row) over the benchmark's cache."""
+    """A multi-token (draft verify) or FP8 decode step over the benchmark's cache, as its own
+    JSON line (the rocprofv3 runs of these passes use it)."""
     Q = args.qlen
     kind = "FP8 E4M3" if args.fp8 else "bf16"
-    log(f"generating the batch 32 x 131072 workload ({kind} cache) with {Q} query positions per row")
+    log(f"generating the batch 32 x 131072 workload ({kind} cache) with {Q} query position(s) per row")
     inp = synth.fp8_config(Q) if args.fp8 else synth.multi_config(Q)
-    B, W, topk, n_init, n_local = inp.batch, inp.max_blocks, inp.topk, inp.n_init, inp.n_local
-    nbytes = inp.index_k_bytes
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     q = torch.from_numpy(inp.q.view(np.int16)).to(dev).view(torch.bfloat16)
@@ -345,96 +536,27 @@ def bench_multi(args, msa, synth, np, torch) -> int:
         k = torch.from_numpy(inp.k_cache.view(np.int16)).to(dev).view(torch.bfloat16)
     bt = torch.from_numpy(inp.block_table).to(dev)
     lens = torch.from_numpy(inp.seq_lens).to(dev)
-    plan = msa.plan(B, W, topk, args.splits)
-    ws = torch.zeros(msa.workspace_bytes_multi(B, W, Q, topk, args.splits), dtype=torch.uint8,
-                     device=dev)
-    ids = torch.empty((B, Q, 4, topk), dtype=torch.int32, device=dev)
-    sc = torch.empty((B, Q, 4, topk), dtype=torch.float32, device=dev)
-    stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
-    log(f"inputs resident in HBM; plan {plan}")
-
-    def step():
-        if args.fp8:
-            msa.msa_indexer_decode_fp8(q, k, inp.k_scale, bt, lens, topk, n_init, n_local,
-                                       out_ids=ids, out_scores=sc, workspace=ws,
-                                       num_splits=args.splits)
-        else:
-            msa.msa_indexer_decode_multi(q, k, bt, lens, topk, n_init, n_local, out_ids=ids,
-                                         out_scores=sc, workspace=ws, num_splits=args.splits)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    for e0, e1 in ev:
-        e0.record(stream)
-        step()
-        e1.record(stream)
-    torch.cuda.synchronize()
-    k_ms = statistics.mean(e0.elapsed_time(e1) for e0, e1 in ev)
-    if msa.msa_indexer_read_error(ws) != 0:
-        log("device error flag set")
-        return 1
-    graph_us = graph_us_per_call(torch, step)
-    ms_per_step = elapsed * 1e3 / args.steps
-    gbs = nbytes / (ms_per_step * 1e-3) / 1e9
-    k_gbs = nbytes / (k_ms * 1e-3) / 1e9
+    res = leg_multi(msa, torch, f"{kind} Q={Q}", q, k, bt, lens, inp.index_k_bytes, inp.topk, inp.n_init,
+                    inp.n_local, args.steps, args.warmup, inp.k_scale if args.fp8 else None)
     out = {
         "metric": (f"µs/verify step ({Q} draft positions per row)" if Q > 1 else "µs/decode step")
                   + f" + index-K GB/s (% of 8 TB/s) at batch 32 × 128K ctx, {kind} index cache",
-        "value": round(gbs, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
-        "us_per_step": round(ms_per_step * 1e3, 2),
-        "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "fp8e4m3 x bf16" if args.fp8 else "bf16",
-        "data": ("synthetic (seeded N(0,1) bf16 q, E4M3 codes of 4 N(0,1) index-K, shuffled page "
-                 "table)") if args.fp8 else
-                "synthetic (seeded N(0,1) bf16 q and index-K, shuffled page table)",
-        "config": {
-            "workload": f"batch 32 x 131072-token rows ({kind} index-K), {Q} query position(s) each (causal), 1024 "
-                        "blocks of 128 tokens, 4 index heads x 128, top-16, 1 initial + 2 recent "
-                        "blocks pinned",
-            "batch": B, "qlen": Q, "seq_len": int(inp.seq_lens[0]), "topk": topk,
-            "num_splits": plan["splits"] if plan["blocks_per_split"] else "chosen per call on the device",
-            "blocks_per_split": plan["blocks_per_split"] or "chosen per call on the device",
-            "index_k_bytes": nbytes,
-            "step_call": "msa_indexer_decode_fp8" if args.fp8 else "msa_indexer_decode_multi",
-        },
-        "roofline": {
-            "kernel": "verify_kernel + verify_merge_kernel (the whole step, timed together)",
-            "bound": "hbm",
-            "achieved": round(k_gbs, 2),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(k_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
-            "kernel_us": round(k_ms * 1e3, 2),
-            "algorithmic_bytes_per_launch": nbytes,
-        },
-        "graph": {"us_per_step": round(graph_us, 2),
-                  "GBs": round(nbytes / (graph_us * 1e-6) / 1e9, 2),
-                  "protocol": "8 calls per HIP graph, 100 replays per round, median of 7 rounds"},
+        "value": res["step"]["GBs"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(res["step"]["us"] / 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8e4m3 x bf16" if args.fp8 else "bf16", "data": "synthetic",
+        "config": {"workload": f"batch 32 x 131072-token rows ({kind} index-K), {Q} query position(s)",
+                   "step_call": "msa_indexer_decode_fp8" if args.fp8 else "msa_indexer_decode_multi"},
+        **res,
     }
     if not args.no_cpu_baseline:
-        log("timing the CPU oracle on the same workload")
         out["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(out), flush=True)
-    return 0
+    return 0 if not FAILED_CHECKS else 1
 
+
+# ---------------------------------------------------------------------------
 
 def main() -> int:
     ap = argparse.ArgumentParser()
@@ -446,29 +568,28 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--step", choices=("decode", "decode_pages"), default="decode",
                     help="the call timed as one step (decode_pages also writes the 16-token page table)")
-    ap.add_argument("--qlen", type=int, default=1,
-                    help="query positions per row; above 1 the step is a multi-token (draft verify) "
-                         "decode of the same cache, msa_indexer_decode_multi")
+    ap.add_argument("--qlen", type=int, default=0,
+                    help="time a multi-token (draft verify) step with this many query positions per "
+                         "row over the same cache instead (msa_indexer_decode_multi; 1 = the verify "
+                         "kernel on one position)")
     ap.add_argument("--fp8", action="store_true",
-                    help="an FP8 E4M3 index-K cache (msa_indexer_decode_fp8, 512 MiB at this shape)")
+                    help="time the step over an FP8 E4M3 index-K cache instead (msa_indexer_decode_fp8)")
     ap.add_argument("--configs", action="store_true",
-                    help="time the four smaller workloads (graph protocol, warm and with rotating "
-                         "input copies) instead of the benchmark step")
+                    help="time only the four smaller workloads (graph protocol, warm and rotating)")
     ap.add_argument("--sweep", action="store_true",
-                    help="time the decode call (bf16 and FP8 caches) over a batch x context grid "
-                         "instead of the benchmark step")
+                    help="time the decode call (bf16 and FP8 caches) over a batch x context grid")
     ap.add_argument("--shard", type=int, default=0, metavar="P",
                     help="time each rank's share of the benchmark workload under P-way context "
                          "parallelism (round-robin blocks), on this one GPU")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip timing the page-table entry points")
+                    help="time the headline step alone (no extra rows)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a 1 GiB device copy (for scaling HBM counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the library has no multi-GPU path "
-              "(run with --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path, and this box has "
+              "one GPU (run with --gpus 1)", file=sys.stderr)
         return 2
 
     import numpy as np
@@ -487,15 +608,17 @@ def main() -> int:
     import sparse_attention_block_amd as msa
     from sparse_attention_block_amd import synth
 
-    lib = msa.load()  # raises if the HIP library is not built
+    msa.load()  # raises if the HIP library is not built
     if args.configs:
         return bench_configs(msa, synth, np, torch)
     if args.sweep:
         return bench_sweep(msa, np, torch)
     if args.shard:
         return bench_shard(args, msa, synth, np, torch)
-    if args.qlen != 1 or args.fp8:
+    if args.qlen or args.fp8:
+        args.qlen = args.qlen or 1
         return bench_multi(args, msa, synth, np, torch)
+
     log("generating the batch 32 x 131072 workload (1 GiB of bf16 index-K)")
     t0 = time.time()
     inp = synth.config3()
@@ -510,83 +633,48 @@ def main() -> int:
     bt = torch.from_numpy(inp.block_table).to(dev)
     lens = torch.from_numpy(inp.seq_lens).to(dev)
     plan = msa.plan(B, W, topk, args.splits)
-    splits = plan["splits"]
     ws = msa.new_workspace(B, W, topk, args.splits, dev)
     ids = torch.empty((B, 4, topk), dtype=torch.int32, device=dev)
     sc = torch.empty((B, 4, topk), dtype=torch.float32, device=dev)
-    torch.cuda.synchronize()
-    log(f"inputs resident in HBM; plan {plan}, engine {args.engine}")
-
-    stream = torch.cuda.current_stream()
-    engine_arg = args.engine if args.engine else None
-
     pt = torch.empty((B, 4, 8 * topk), dtype=torch.int32, device=dev)
     ptok = torch.empty((B, 4), dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    log(f"inputs resident in HBM; plan {plan}, engine {args.engine}")
+    engine_arg = args.engine if args.engine else None
+    # The default step, marshalled once: one ctypes call per step, so the host stays far ahead
+    # of the GPU and the launches run back to back from the first.
+    bound = (msa.bind_decode(q, k, bt, lens, topk, n_init, n_local, ids, sc, ws, args.splits)
+             if args.step == "decode" and engine_arg is None else None)
 
-    def step(ev0=None, ev1=None):
-        # A fused plan is one kernel launch per step (the last split of each row merges
-        # it); otherwise stage 1 is timed alone and stage 2 follows it.
-        if ev0 is not None:
-            ev0.record(stream)
+    def step():
+        if bound is not None:
+            bound()
+        else:
+            call()
+
+    def call():  # through the binding, on the current stream (also under graph capture)
         if plan["fused"] and args.step == "decode_pages":
             msa.msa_indexer_decode_pages(q, k, bt, lens, topk, n_init, n_local, out_ids=ids,
                                          out_scores=sc, out_pages=pt, out_tokens=ptok,
-                                         workspace=ws, num_splits=args.splits,
-                                         engine=args.engine)
-        elif plan["fused"]:
+                                         workspace=ws, num_splits=args.splits, engine=args.engine)
+        else:
             msa.msa_indexer_decode(q, k, bt, lens, topk, n_init, n_local, out_ids=ids, out_scores=sc,
                                    workspace=ws, num_splits=args.splits, engine=engine_arg)
-        else:
-            msa.msa_indexer_split_topk(q, k, bt, lens, ws, topk, n_init, n_local,
-                                       num_splits=args.splits, engine=args.engine)
-        if ev1 is not None:
-            ev1.record(stream)
-        if not plan["fused"]:
-            msa.msa_indexer_merge(lens, W, ws, ids, sc, topk, num_splits=args.splits)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    log(f"warmup done ({args.warmup} steps)")
-
-    # Timed region: K back-to-back steps, bracketed by synchronizations, with nothing else
-    # in the stream (event markers between launches would add a few us of queue gap each).
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t_start
-    log(f"timed {args.steps} steps in {elapsed:.3f} s")
-
-    # Kernel timing: the same K steps again, each launch of the dominant kernel bracketed
-    # by HIP events on the stream it is launched on.
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    for e0, e1 in ev:
-        step(e0, e1)
-    torch.cuda.synchronize()
-    kernel_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+    # Timed region: warmup, then exactly K back-to-back steps between synchronizations; the
+    # event pair on the launch stream around the same K launches gives the kernel time.
+    us_per_step, kernel_us = timed_steps(torch, step, args.steps, args.warmup)
+    log(f"timed {args.steps} steps: {us_per_step:.2f} us/step wall, {kernel_us:.2f} us/launch on the stream")
+    headline_check = check_single(msa, q, k, bt, lens, ids, sc, topk, n_init, n_local, "headline")
+    gpu_ids = ids.cpu().numpy()
     if msa.msa_indexer_read_error(ws) != 0:
-        log("device error flag set")
-        return 1
-
-    graph_us = graph_us_per_call(torch, step)
+        FAILED_CHECKS.append("headline: device error flag set")
+    graph_us = graph_us_per_call(torch, call)
     log(f"graph protocol: {graph_us:.2f} us per call")
 
-    extra = {}
-    if plan["fused"] and not args.no_extra:
-        extra = time_page_table(msa, torch, args, q, k, bt, lens, ids, ws, stream, topk, n_init,
-                                n_local, engine_arg, B)
-
-    ms_per_step = elapsed * 1e3 / args.steps
-    us_per_step = ms_per_step * 1e3
-    gbs = nbytes / (ms_per_step * 1e-3) / 1e9
-    k_ms = statistics.mean(kernel_ms)
-    k_gbs = nbytes / (k_ms * 1e-3) / 1e9
+    gbs = nbytes / (us_per_step * 1e-6) / 1e9
+    k_gbs = nbytes / (kernel_us * 1e-6) / 1e9
     engine = args.engine if args.engine else 1
-    traffic = measured_traffic(engine)
-
     out = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -594,7 +682,7 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": round(us_per_step / 1e3, 5),
         "us_per_step": round(us_per_step, 2),
         "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "higher_is_better": True,
@@ -607,7 +695,7 @@ def main() -> int:
                         "top-16, 1 initial + 2 recent blocks pinned",
             "batch": B, "seq_len": int(inp.seq_lens[0]), "index_heads": 4, "head_dim": 128,
             "block_tokens": 128, "topk": topk, "n_init": n_init, "n_local": n_local,
-            "num_splits": splits if plan["blocks_per_split"] else "chosen per call on the device",
+            "num_splits": plan["splits"] if plan["blocks_per_split"] else "chosen per call on the device",
             "blocks_per_split": plan["blocks_per_split"] or "chosen per call on the device",
             "fused_merge": plan["fused"], "engine": engine, "index_k_bytes": nbytes,
             "step_call": "msa_indexer_decode_pages" if args.step == "decode_pages" and plan["fused"]
@@ -615,28 +703,65 @@ def main() -> int:
         },
         "roofline": {
             "kernel": ("split_kernel, fused: block scores + per-split top-16 + merge by each row's "
-                       "last split (the whole step)") if plan["fused"] else
-                      "split_kernel (stage 1: block scores + per-split top-16)",
+                       "last split (the whole step, one launch)") if plan["fused"] else
+                      "split_kernel + merge_kernel (the whole step)",
             "bound": "hbm",
             "achieved": round(k_gbs, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(k_gbs / HBM_PEAK_GBS, 4),
-            "traffic": traffic,
-            "kernel_us": round(k_ms * 1e3, 2),
+            "traffic": measured_traffic(engine) if plan["fused"] and args.step == "decode" else None,
+            "kernel_us": round(kernel_us, 2),
+            "kernel_time_source": f"one HIP event pair on the launch stream around the {args.steps} "
+                                  "timed back-to-back launches, divided by their number",
             "algorithmic_bytes_per_launch": nbytes,
         },
+        "timed_region": f"{args.steps} steps launched back to back from the host, one ctypes call "
+                        "each (arguments marshalled once)",
+        "graph": {"us_per_step": round(graph_us, 2),
+                  "GBs": round(nbytes / (graph_us * 1e-6) / 1e9, 2), "protocol": GRAPH_PROTOCOL},
+        "output_check": headline_check,
     }
-    out["graph"] = {"us_per_step": round(graph_us, 2),
-                    "GBs": round(nbytes / (graph_us * 1e-6) / 1e9, 2),
-                    "protocol": "8 calls per HIP graph, 100 replays per round, median of 7 rounds"}
-    if extra:
-        out["page_table"] = extra
+
+    if not args.no_extra:
+        extra = {}
+        extra["page_table"] = time_page_table(msa, torch, q, k, bt, lens, topk, n_init, n_local,
+                                              args.steps, args.warmup)
+        log("four draft positions over the same bf16 cache")
+        q4 = torch.from_numpy(synth.multi_query(4).view(np.int16)).to(dev).view(torch.bfloat16)
+        extra["bf16_four_positions"] = leg_multi(msa, torch, "bf16 Q=4", q4, k, bt, lens, nbytes, topk,
+                                                 n_init, n_local, args.steps, args.warmup)
+        extra["streaming_ceiling_bf16"] = rate(nbytes, streaming_ceiling(torch, k, bt, 32768, 0))
+        extra["streaming_ceiling_bf16"]["what"] = ("the same 1 GiB of shuffled 32 KiB pages read with the "
+                                                   "split kernel's load pattern and no arithmetic "
+                                                   "(512 workgroups of 64 blocks), graph protocol")
+        del q4
+        log("generating the FP8 E4M3 cache of the same shape")
+        f8 = synth.fp8_config(1)
+        k8 = torch.from_numpy(f8.k_cache).to(dev)
+        q8 = torch.from_numpy(f8.q.view(np.int16)).to(dev).view(torch.bfloat16)
+        bt8 = torch.from_numpy(f8.block_table).to(dev)
+        l8 = torch.from_numpy(f8.seq_lens).to(dev)
+        extra["fp8_one_position"] = leg_multi(msa, torch, "FP8 Q=1", q8, k8, bt8, l8, f8.index_k_bytes,
+                                              topk, n_init, n_local, args.steps, args.warmup,
+                                              fp8_scale=f8.k_scale)
+        extra["streaming_ceiling_fp8"] = rate(f8.index_k_bytes, streaming_ceiling(torch, k8, bt8, 16384, 1))
+        extra["streaming_ceiling_fp8"]["what"] = ("the same 512 MiB of shuffled 16 KiB FP8 pages read with "
+                                                  "the verify kernel's load pattern (8 KiB chunks, three in "
+                                                  "flight per wave) and no arithmetic, graph protocol")
+        del k8, f8
+        torch.cuda.empty_cache()
+        log("the four smaller workloads")
+        extra["configs"] = leg_configs(msa, synth, np, torch)
+        out["extra"] = extra
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on the same workload")
-        out["cpu_baseline"] = cpu_baseline(inp)
+        out["cpu_baseline"] = cpu_baseline(inp, gpu_ids)
+    out["output_checks_passed"] = not FAILED_CHECKS
+    if FAILED_CHECKS:
+        out["failed_checks"] = FAILED_CHECKS
     print(json.dumps(out), flush=True)
-    return 0
+    return 0 if not FAILED_CHECKS else 1
 
 
 if __name__ == "__main__":

@@ -9,6 +9,8 @@ from ._lib import (  # noqa: F401
     ENGINE_MFMA,
     ENGINE_VALU,
     MsaError,
+    bind_decode,
+    bind_decode_multi,
     load,
     msa_indexer_block_scores,
     msa_indexer_block_scores_fp8,

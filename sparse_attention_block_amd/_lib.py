@@ -268,6 +268,51 @@ def msa_indexer_decode(q, k_cache, block_table, seq_lens, topk=16, n_init=1, n_l
     return out_ids, out_scores
 
 
+def _bound(name: str, args: list):
+    """A zero-argument call of C entry point `name` with arguments marshalled once: the tensors'
+    addresses and the stream are fixed, so each call costs one ctypes call and no Python-side
+    checks (for timing loops that must keep the launch queue full)."""
+    fn = getattr(load(), name)
+    args = tuple(args)
+
+    def call():
+        rc = fn(*args)
+        if rc != MSA_OK:
+            raise MsaError(name, rc)
+    return call
+
+
+@_on_tensor_device
+def bind_decode(q, k_cache, block_table, seq_lens, topk, n_init, n_local, out_ids, out_scores,
+                workspace, num_splits=0, stream=None):
+    """msa_indexer_decode on these tensors, marshalled once: returns a zero-argument callable
+    that enqueues the call on `stream` (default: the current stream now)."""
+    torch = _torch()
+    (pq, pk, pbt, pl), B, W, stride, pages = _inputs(q, k_cache, block_table, seq_lens)
+    return _bound("msa_indexer_decode", [
+        pq, pk, pbt, pl, B, W, stride, pages, topk, n_init, n_local,
+        _dev(out_ids, "out_ids", torch.int32, (B, HEADS, topk)),
+        _dev(out_scores, "out_scores", torch.float32, (B, HEADS, topk)),
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(), num_splits, _stream(stream)])
+
+
+@_on_tensor_device
+def bind_decode_multi(q, k_cache, block_table, seq_lens, topk, n_init, n_local, out_ids, out_scores,
+                      workspace, num_splits=0, stream=None, k_scale=None):
+    """msa_indexer_decode_multi (or, with k_scale, msa_indexer_decode_fp8 over a uint8 E4M3 cache)
+    on these tensors, marshalled once: a zero-argument callable."""
+    torch = _torch()
+    fp8 = k_scale is not None
+    (pq, pk, pbt, pl), B, Q, W, stride, pages = _inputs_multi(q, k_cache, block_table, seq_lens,
+                                                              torch.uint8 if fp8 else None)
+    head = [pq, pk, _F32(float(k_scale))] if fp8 else [pq, pk]
+    return _bound("msa_indexer_decode_fp8" if fp8 else "msa_indexer_decode_multi", head + [
+        pbt, pl, B, W, stride, pages, Q, topk, n_init, n_local,
+        _dev(out_ids, "out_ids", torch.int32, (B, Q, HEADS, topk)),
+        _dev(out_scores, "out_scores", torch.float32, (B, Q, HEADS, topk)),
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(), num_splits, _stream(stream)])
+
+
 @_on_tensor_device
 def msa_indexer_decode_noalloc(q, k_cache, block_table, seq_lens, topk=16, n_init=1, n_local=2,
                                out_ids=None, out_scores=None, error_flags=None, num_splits=0,

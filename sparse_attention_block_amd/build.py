@@ -1,4 +1,5 @@
-"""Builds the HIP library libmsa_indexer.so in-tree for gfx950 with hipcc."""
+"""Builds the HIP libraries in-tree for gfx950 with hipcc: libmsa_indexer.so (the decode pass)
+and libmsa_probe.so (the streaming-ceiling probe bench.py measures beside it)."""
 from __future__ import annotations
 
 import os
@@ -8,12 +9,17 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SOURCE = os.path.join(HERE, "csrc", "msa_indexer.hip")
+PROBE_SOURCE = os.path.join(HERE, "csrc", "stream_probe.hip")
 INCLUDE = os.path.join(ROOT, "include")
 ARCH = "gfx950"
 
 
 def library_path() -> str:
     return os.path.join(HERE, "libmsa_indexer.so")
+
+
+def probe_library_path() -> str:
+    return os.path.join(HERE, "libmsa_probe.so")
 
 
 def hipcc() -> str:
@@ -33,10 +39,9 @@ def compile_flags() -> list[str]:
     ]
 
 
-def build(verbose: bool = False, extra: list[str] | None = None, out: str | None = None) -> str:
-    out = out or library_path()
+def _compile(source: str, out: str, verbose: bool, extra: list[str] | None) -> str:
     tmp = out + ".tmp"
-    cmd = [hipcc(), *compile_flags(), *(extra or []), SOURCE, "-o", tmp]
+    cmd = [hipcc(), *compile_flags(), *(extra or []), source, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -49,6 +54,14 @@ def build(verbose: bool = False, extra: list[str] | None = None, out: str | None
         print(msg, flush=True)
     os.replace(tmp, out)
     return out
+
+
+def build(verbose: bool = False, extra: list[str] | None = None, out: str | None = None) -> str:
+    """Compiles libmsa_indexer.so (to `out` if given); without `out`, also libmsa_probe.so."""
+    path = _compile(SOURCE, out or library_path(), verbose, extra)
+    if out is None:
+        _compile(PROBE_SOURCE, probe_library_path(), verbose, extra)
+    return path
 
 
 if __name__ == "__main__":

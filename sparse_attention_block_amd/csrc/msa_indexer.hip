@@ -187,6 +187,44 @@ __device__ __forceinline__ uint64_t sort_desc_first(uint64_t x, int lane, int n)
   return x;
 }
 
+// sort_desc_first of T independent key sets at once, each step applied to all T before the
+// next, so that their dependency chains overlap.
+template <int T, int K>
+__device__ __forceinline__ void bitonic_stage_all(uint64_t (&x)[T], int lane) {
+#pragma unroll
+  for (int t = 0; t < T; ++t) x[t] = bitonic_step<K - 1, K / 2>(x[t], lane);
+  if constexpr (K >= 64) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) x[t] = bitonic_step<16, 16>(x[t], lane);
+  }
+  if constexpr (K >= 32) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) x[t] = bitonic_step<8, 8>(x[t], lane);
+  }
+  if constexpr (K >= 16) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) x[t] = bitonic_step<4, 4>(x[t], lane);
+  }
+  if constexpr (K >= 8) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) x[t] = bitonic_step<2, 2>(x[t], lane);
+  }
+  if constexpr (K >= 4) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) x[t] = bitonic_step<1, 1>(x[t], lane);
+  }
+}
+
+template <int T>
+__device__ __forceinline__ void sort_desc_first_all(uint64_t (&x)[T], int lane, int n) {
+  if (n > 1) bitonic_stage_all<T, 2>(x, lane);
+  if (n > 2) bitonic_stage_all<T, 4>(x, lane);
+  if (n > 4) bitonic_stage_all<T, 8>(x, lane);
+  if (n > 8) bitonic_stage_all<T, 16>(x, lane);
+  if (n > 16) bitonic_stage_all<T, 32>(x, lane);
+  if (n > 32) bitonic_stage_all<T, 64>(x, lane);
+}
+
 // Largest value over the 64 lanes of a wave (all lanes active).
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
   x = umax64(x, dpp_u64<kQuadSwap1>(x));
@@ -1221,8 +1259,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   }
   if (j0 >= nb) {
     // An empty row has no workgroup to merge it: its first workgroup writes the padding.
-    if (MODE == kFused && nb == 0 && s == 0 && (int)threadIdx.x < kHeads * a.topk) {
-      const size_t o = (size_t)b * kHeads * a.topk + threadIdx.x;
+    if (MODE == kFused && nb == 0 && s == 0 && (int)threadIdx.x < a.Q * kHeads * a.topk) {
+      const size_t o = (size_t)b * a.Q * kHeads * a.topk + threadIdx.x;
       a.out_ids[o] = -1;
       a.out_scores[o] = -__builtin_inff();
     }
@@ -1330,20 +1368,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   if (MODE == kScores) return;
   __syncthreads();
 
-  // Wave h sorts head h's keys of every position and keeps the first Lk. A block past
-  // position p's end has no key (0).
+  // Wave h sorts head h's keys of every position (the positions side by side) and keeps the
+  // first Lk. A block past position p's end has no key (0).
   const int n = j1 - j0;
   const int h = wave;
-  for (int p = 0; p < a.Q; ++p) {
+  auto key_of = [&](int p) -> uint64_t {
     const int nbp = (causal_len(L, a.Q, p) + kBlock - 1) / kBlock;
     const int jj = j0 + lane;
     const bool real = lane < n && jj < nbp;
-    uint64_t key = real ? make_key(sc[lane][4 * p + h], jj, jj < a.n_init || jj >= nbp - a.n_local) : 0;
-    key = sort_desc_first(key, lane, n);
-    if (MODE == kFused && a.Q == 1 && nb <= C) {
-      // The row's only split (one position): its sorted keys are the selection.
-      const size_t o = ((size_t)b * kHeads + h) * a.topk;
-      write_selection(key, min(a.topk, nb), a.topk, lane, a.out_ids + o, a.out_scores + o);
+    return real ? make_key(sc[lane][4 * p + h], jj, jj < a.n_init || jj >= nbp - a.n_local) : 0;
+  };
+  auto publish = [&](int p, uint64_t key) {
+    if (MODE == kFused && nb <= C) {
+      // The row's only split: each position's sorted keys are its selection.
+      const int nbp = (causal_len(L, a.Q, p) + kBlock - 1) / kBlock;
+      const size_t o = (((size_t)b * a.Q + p) * kHeads + h) * a.topk;
+      write_selection(key, min(a.topk, nbp), a.topk, lane, a.out_ids + o, a.out_scores + o);
       return;
     }
     uint64_t* out = a.keys + list_offset(b, a.S, a.Q * kHeads, a.Lk, s, 4 * p + h, Lk);
@@ -1352,8 +1392,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     } else {
       if (lane < Lk) out[lane] = key;
     }
+  };
+  if (a.Q == 1) {
+    uint64_t k[1] = {key_of(0)};
+    sort_desc_first_all<1>(k, lane, n);
+    publish(0, k[0]);
+  } else if (a.Q == 2) {
+    uint64_t k[2] = {key_of(0), key_of(1)};
+    sort_desc_first_all<2>(k, lane, n);
+    publish(0, k[0]);
+    publish(1, k[1]);
+  } else {
+    uint64_t k[4] = {key_of(0), key_of(1), key_of(2), a.Q > 3 ? key_of(3) : 0};
+    sort_desc_first_all<4>(k, lane, n);
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+      if (p < a.Q) publish(p, k[p]);
   }
-  if (MODE != kFused) return;
+  if (MODE != kFused || nb <= C) return;
 
   // Publication and the last workgroup's merge, as in split_kernel (one position: wave h
   // merges head h).
@@ -1363,11 +1419,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   if (threadIdx.x == 0) s_last = count_in(a.counters + (size_t)b * kCounterStride, s, ns);
   __syncthreads();
   if (!s_last) return;
-  const int msel = min(a.topk, nb);
   const uint64_t mine = merge_top16(a.keys + list_offset(b, a.S, kHeads, a.Lk, 0, h, Lk), (size_t)kHeads * Lk,
                                     ns, Lk, C, lane);
   const size_t o = ((size_t)b * kHeads + h) * a.topk;
-  write_selection(mine, msel, a.topk, lane, a.out_ids + o, a.out_scores + o);
+  write_selection(mine, min(a.topk, nb), a.topk, lane, a.out_ids + o, a.out_scores + o);
 }
 
 // The error word's bits, taken (read and cleared atomically) into the header's next word.
@@ -1696,13 +1751,20 @@ VerifyArgs make_verify_args(const void* q, const void* k, const int32_t* bt, con
 
 bool valid_scale(float k_scale) { return k_scale > 0.0f && k_scale <= 3.402823466e38f; }
 
-// Whether the one-position pass merges in its own launch: when merge_top16 holds each head's
-// lists in at most 4 registers (S lists of Lk keys, 64 / Lk2 per register). With more, the
-// serial merge in the row's last workgroup measured slower than the merge kernel, which
-// runs every (row, head) at once (FP8 at batch 32 x 128K: 32 lists of 16, 89.8 vs 88.7 us).
-bool fuse_verify(const Plan& p, int topk) {
-  if (p.S > 64 || topk > kNetworkMaxM) return false;
-  if (p.device) return true;  // the device plan keeps every row's lists within merge_top16
+// Whether a one-position pass merges in its own launch (the row's last workgroup merging,
+// wave h head h): always under the device plan, whose rows have at most 256 splits of at most
+// 16 keys (merge_top16 prunes what does not fit); under a host plan when each head's lists fit
+// 4 registers (S lists of Lk keys, 64 / Lk2 per register). With more, the serial merge in the
+// row's last workgroup measured slower than the merge kernel, which runs every (row, head) at
+// once (FP8 at batch 32 x 128K: 32 lists of 16, 89.8 vs 88.7 us). Passes of several positions
+// always merge in the merge kernel: one workgroup merging every position of a row in its tail
+// (the positions side by side in the network) measured slower than the merge kernel's wave per
+// (row, position, head) at every shape tried (bf16, 4 positions, batch 32 x 128K: 168.8 vs
+// 166.2 us; batch 16 with one 128K row among 1K rows: 23.4 vs 16.1 us).
+bool fuse_verify(const Plan& p, int topk, int qlen) {
+  if (qlen > 1 || topk > kNetworkMaxM) return false;
+  if (p.device) return true;
+  if (p.S > 64) return false;
   int lk2 = 1;
   while (lk2 < p.Lk) lk2 <<= 1;
   return ceil_div(p.S, 64 / lk2) <= 4;
@@ -1738,7 +1800,7 @@ int32_t verify_decode_impl(const void* q, const void* k_cache, bool fp8, float k
                                   ws_view(workspace, workspace_bytes, keys_bytes(batch, qlen, p)), batch,
                                   k_scale);
   const int grid = p.device ? p.grid : 0;
-  if (qlen == 1 && fuse_verify(p, topk)) {  // one position, few lists: merge in the same launch
+  if (fuse_verify(p, topk, qlen)) {  // one position, a cheap merge: in the same launch
     a.out_ids = out_ids;
     a.out_scores = out_scores;
     launch_verify<kFused>(a, fp8, batch, st, grid);

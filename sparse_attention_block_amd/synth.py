@@ -235,11 +235,16 @@ def multi_planted(qlen: int = 4) -> Inputs:
                   meta={"planted": planted})
 
 
+def multi_query(qlen: int = 4) -> np.ndarray:
+    """The queries of multi_config: ~N(0,1) bf16 [32, qlen, 4, 128]."""
+    return normal_bf16(3, 5, (32, qlen, HEADS, DIM))
+
+
 def multi_config(qlen: int = 4) -> Inputs:
     """The benchmark shape with qlen draft positions per row: batch 32 x 131072 tokens (1024
     blocks, 1 GiB of index-K, the same cache as config3), q ~N(0,1) [32, qlen, 4, 128]."""
     inp = config3()
-    inp.q = normal_bf16(3, 5, (inp.batch, qlen, HEADS, DIM))
+    inp.q = multi_query(qlen)
     inp.name = f"B=32 x 131072, Q={qlen}"
     return inp
 

@@ -191,3 +191,64 @@ def test_widest_table_2m_token_row(msa):
     assert np.array_equal(pages.cpu().numpy(), wp) and np.array_equal(tokens.cpu().numpy(), wt)
     # the last block (partial: 51 valid tokens) is pinned, so every head selects it
     assert all(W - 1 in ids[0, h] for h in range(4))
+
+
+def test_bound_calls_match_the_binding(msa):
+    # bind_decode / bind_decode_multi (arguments marshalled once, for timing loops) enqueue the
+    # same C calls as the plain binding.
+    inp = synth.paged_case(148, [128 * 40 - 5, 128 * 3, 0, 128 * 40], 40)
+    q, k, bt, lens = to_device(inp)
+    ws = msa.new_workspace(4, 40, 16)
+    ids = torch.empty((4, 4, 16), dtype=torch.int32, device="cuda")
+    sc = torch.empty((4, 4, 16), dtype=torch.float32, device="cuda")
+    msa.bind_decode(q, k, bt, lens, 16, 1, 2, ids, sc, ws)()
+    want_ids, want_sc = msa.msa_indexer_decode(q, k, bt, lens)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, want_ids) and torch.equal(sc, want_sc)
+    f8 = synth.fp8_case(149, [128 * 40 - 5, 128 * 3, 0, 128 * 40], 40, 4, k_scale=0.25)
+    q8 = torch.from_numpy(f8.q.view(np.int16)).cuda().view(torch.bfloat16)
+    k8 = torch.from_numpy(f8.k_cache).cuda()
+    bt8 = torch.from_numpy(f8.block_table).cuda()
+    l8 = torch.from_numpy(f8.seq_lens).cuda()
+    ws8 = torch.zeros(msa.workspace_bytes_multi(4, 40, 4, 16), dtype=torch.uint8, device="cuda")
+    ids8 = torch.empty((4, 4, 4, 16), dtype=torch.int32, device="cuda")
+    sc8 = torch.empty((4, 4, 4, 16), dtype=torch.float32, device="cuda")
+    msa.bind_decode_multi(q8, k8, bt8, l8, 16, 1, 2, ids8, sc8, ws8, k_scale=0.25)()
+    w_ids, w_sc = msa.msa_indexer_decode_fp8(q8, k8, 0.25, bt8, l8)
+    torch.cuda.synchronize()
+    assert torch.equal(ids8, w_ids) and torch.equal(sc8, w_sc)
+
+
+@pytest.mark.parametrize("pattern,elem", [(0, 2), (1, 2), (0, 1), (1, 1)])
+def test_streaming_probe_reads_exactly_the_tables_pages(pattern, elem):
+    # The streaming-ceiling probe (msa_probe.h) folds every 16-byte chunk it loads into its
+    # thread's word: the folds equal a host XOR over exactly the pages the table names, in the
+    # decode kernels' assignment of blocks to waves and lanes.
+    import ctypes
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import bench
+    fn = bench.probe_lib()
+    B, W, C, P = 3, 24, 8, 80
+    page_bytes = 128 * 128 * elem
+    rng = np.random.default_rng(150 + pattern + elem)
+    cache = rng.integers(0, 2 ** 32, size=(P, page_bytes // 4), dtype=np.uint32)
+    bt = rng.permutation(P)[:B * W].astype(np.int32).reshape(B, W)
+    kd = torch.from_numpy(cache.view(np.int32)).cuda()
+    btd = torch.from_numpy(bt).cuda()
+    S = W // C
+    out = torch.zeros(B * S * 256, dtype=torch.int32, device="cuda")
+    rc = fn(kd.data_ptr(), page_bytes, btd.data_ptr(), B, W, W, C, pattern, out.data_ptr(), None)
+    torch.cuda.synchronize()
+    assert rc == 0
+    got = out.cpu().numpy().view(np.uint32).reshape(B, S, 256)
+    chunks = cache.reshape(P, -1, 4)  # [page][16-byte chunk][word]
+    words = np.bitwise_xor.reduce(chunks, axis=2)  # x ^ y ^ z ^ w of each chunk
+    for b in range(B):
+        for s in range(S):
+            for t in range(256):
+                w, lane = t // 64, t % 64
+                want = np.uint32(0)
+                for j in range(s * C + w, s * C + C, 4):
+                    want ^= np.bitwise_xor.reduce(words[bt[b, j], lane::64])
+                assert got[b, s, t] == want, (b, s, t)

@@ -189,3 +189,21 @@ def test_split_limit_edges_multi_and_fp8(msa, name, W, lens, topk):
     assert msa.plan(len(lens), W, topk)["blocks_per_split"] == 0
     run_multi(msa, synth.multi_case(411, lens, W, 4, poison=False, topk=topk))
     run_fp8(msa, synth.fp8_case(412, lens, W, 1, k_scale=0.5, poison=False, topk=topk), 1e-3 * 4.0 * 0.5)
+
+
+# Several positions per row (the split kernel ranks the positions' keys side by side; the merge
+# kernel merges each (row, position, head)): 2 and 3 positions, and FP8 with 2 to 4 positions,
+# at the edges above.
+@pytest.mark.parametrize("name,Q,fp8", [("c4-256-splits", 2, False), ("c4-256-splits", 3, True),
+                                        ("prune-c8-64-65", 3, False), ("prune-c4-128-129", 2, True),
+                                        ("c32-64-splits", 4, True), ("topk8-c16", 3, False)])
+def test_multi_position_split_limit_edges(msa, name, Q, fp8):
+    from test_gpu_fp8 import run_fp8
+    from test_gpu_multi import run_multi
+
+    _, W, lens, topk = [c for c in EDGE_CASES if c[0] == name][0]
+    assert msa.plan(len(lens), W, topk)["blocks_per_split"] == 0
+    if fp8:
+        run_fp8(msa, synth.fp8_case(413, lens, W, Q, k_scale=0.5, poison=False, topk=topk), 1e-3 * 4.0 * 0.5)
+    else:
+        run_multi(msa, synth.multi_case(414, lens, W, Q, poison=False, topk=topk))
