@@ -175,8 +175,9 @@ def check(name: str, bad: int, rows: int) -> dict:
             "against": "the selection over the GPU's own fp32 block scores"}
 
 
-def check_single(msa, q, k, bt, lens, ids, sc, topk, n_init, n_local, name):
-    s = msa.msa_indexer_block_scores(q, k, bt, lens).cpu().numpy()
+def check_single(msa, q, k, bt, lens, ids, sc, topk, n_init, n_local, name, engine=0):
+    """The call's ids / scores against the selection over the same engine's block scores."""
+    s = msa.msa_indexer_block_scores(q, k, bt, lens, engine=engine).cpu().numpy()
     bad = selection_mismatches(ids.cpu().numpy(), sc.cpu().numpy(), s, lens.cpu().numpy(), topk,
                                n_init, n_local)
     return check(name, bad, s.shape[0] * 4)
@@ -520,6 +521,24 @@ def bench_shard(args, msa, synth, np, torch) -> int:
     return 0
 
 
+def bench_ceiling(msa, synth, np, torch) -> int:
+    """The streaming ceilings alone (the probe of msa_probe.h over the benchmark's bf16 cache and
+    its FP8 counterpart), one JSON line each."""
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    for name, inp, page_bytes, pattern in (("bf16", synth.config3(), 32768, 0),
+                                           ("fp8", synth.fp8_config(1), 16384, 1)):
+        k = (torch.from_numpy(inp.k_cache).to(dev) if inp.fp8 else
+             torch.from_numpy(inp.k_cache.view(np.int16)).to(dev).view(torch.bfloat16))
+        bt = torch.from_numpy(inp.block_table).to(dev)
+        us = streaming_ceiling(torch, k, bt, page_bytes, pattern)
+        print(json.dumps({"ceiling": name, "pattern": ["split", "chunk"][pattern], **rate(inp.index_k_bytes, us),
+                          "index_k_bytes": inp.index_k_bytes, "protocol": GRAPH_PROTOCOL}), flush=True)
+        del k, inp
+        torch.cuda.empty_cache()
+    return 0
+
+
 def bench_multi(args, msa, synth, np, torch) -> int:
     """A multi-token (draft verify) or FP8 decode step over the benchmark's cache, as its own
     JSON line (the rocprofv3 runs of these passes use it)."""
@@ -581,6 +600,8 @@ def main() -> int:
     ap.add_argument("--shard", type=int, default=0, metavar="P",
                     help="time each rank's share of the benchmark workload under P-way context "
                          "parallelism (round-robin blocks), on this one GPU")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="time only the streaming probe over the benchmark's bf16 and FP8 caches")
     ap.add_argument("--no-extra", action="store_true",
                     help="time the headline step alone (no extra rows)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -618,6 +639,8 @@ def main() -> int:
     if args.qlen or args.fp8:
         args.qlen = args.qlen or 1
         return bench_multi(args, msa, synth, np, torch)
+    if args.ceiling:
+        return bench_ceiling(msa, synth, np, torch)
 
     log("generating the batch 32 x 131072 workload (1 GiB of bf16 index-K)")
     t0 = time.time()
@@ -665,7 +688,8 @@ def main() -> int:
     # event pair on the launch stream around the same K launches gives the kernel time.
     us_per_step, kernel_us = timed_steps(torch, step, args.steps, args.warmup)
     log(f"timed {args.steps} steps: {us_per_step:.2f} us/step wall, {kernel_us:.2f} us/launch on the stream")
-    headline_check = check_single(msa, q, k, bt, lens, ids, sc, topk, n_init, n_local, "headline")
+    headline_check = check_single(msa, q, k, bt, lens, ids, sc, topk, n_init, n_local, "headline",
+                                  engine=args.engine)
     gpu_ids = ids.cpu().numpy()
     if msa.msa_indexer_read_error(ws) != 0:
         FAILED_CHECKS.append("headline: device error flag set")

@@ -79,7 +79,11 @@ extern "C" {
 /* Device error bits, OR-ed into the workspace's error word by the kernels. */
 #define MSA_DEVERR_PAGE_OUT_OF_RANGE 1u  /* a needed block_table entry was outside [0, num_pages) */
 
-/* Human-readable text for a status code. Never NULL. */
+/*
+ * Human-readable text for a status code. Never NULL. Every entry point reports a rejected
+ * configuration as a status before it enqueues anything, as the pages' integration fails
+ * unsupported configurations at startup instead of running them (vLLM PR #57832, Test Result).
+ */
 const char *msa_status_string(int32_t status);
 
 /*
@@ -146,7 +150,16 @@ size_t msa_indexer_workspace_bytes(int32_t batch, int32_t max_blocks_per_seq, in
                                    int32_t num_splits);
 
 /*
- * The whole decode pass: block scores, per-split top-k, exact merge.
+ * The whole decode pass: block scores, per-split top-k, exact merge (vLLM PR #57832, Solution:
+ * every block scored, per-head top-k of packed (score, block id) keys, an exact merge of per-shard
+ * top-k lists with the init/sink and sliding-window blocks pinned; SGLang PR #41488,
+ * Modifications: max over each 128-token block, 4 heads scored from one read of each K tile;
+ * TensorRT-LLM PR #17008, Changes and Accuracy: the KV axis split into contiguous tile ranges,
+ * each range's maximum seeded at -inf, so the split count cannot change a score).
+ * Beyond the plain form of this call (q, k_cache, block_table, seq_lens, sizes, topk, pins,
+ * outputs, workspace, stream) it takes num_splits, the split-count knob TensorRT-LLM PR #17008
+ * sweeps (Performance: num_kv_splits 1..32) and checks for invariance (Accuracy); 0 leaves the
+ * choice to the library.
  *
  *   q            bf16 [batch][4][128], contiguous, 16-byte aligned: post-RoPE index queries,
  *                one decode token per row.
@@ -391,7 +404,11 @@ int32_t msa_indexer_merge(const int32_t *seq_lens, int32_t batch, int32_t max_bl
 /*
  * Test and debugging aid: the full block-score matrix out[b][h][j], fp32
  * [batch][4][max_blocks_per_seq], -inf for j >= nb_b and for blocks whose page is out of
- * range. Uses the same scoring code as stage 1. num_splits and engine as above.
+ * range, from the same scoring code as stage 1. It is the max-score output the pages compare
+ * across split counts (TensorRT-LLM PR #17008, Accuracy: max_score bitwise identical for every
+ * num_kv_splits). Besides the plain form (inputs, sizes, out, stream) it takes num_splits, to
+ * reproduce that check, and engine, to score with either instruction path (the MFMA-versus-VALU
+ * comparison); 0 and MSA_ENGINE_DEFAULT are the decode call's choices.
  */
 int32_t msa_indexer_block_scores(const void *q, const void *k_cache, const int32_t *block_table,
                                  const int32_t *seq_lens, int32_t batch,
