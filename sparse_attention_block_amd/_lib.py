@@ -93,6 +93,15 @@ def load(path: str | None = None):
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with sparse_attention_block_amd.build.build() "
                            "(or __graft_entry__.build()); there is no non-HIP fallback")
+    # The library needs libamdhip64.so.7. PyTorch ships its own HIP runtime under that soname
+    # but links it by another name, so loading the library first would bring in the system's
+    # runtime and then PyTorch its copy: two runtimes in one process, and the library's
+    # launches on PyTorch's streams and memory fail. With PyTorch loaded first, the library
+    # binds to the runtime already in the process.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     for name, (args, res) in _SIGNATURES.items():
         fn = getattr(lib, name)

@@ -1596,12 +1596,19 @@ int32_t check_select(int32_t topk, int32_t n_init, int32_t n_local) {
   return MSA_OK;
 }
 
+// hipGetLastError reports (and clears) the last error of any HIP call of this thread,
+// including one left by other code before this library's call (another library's failed
+// query, say). Each launch site clears that first, so the status it reads after its launch
+// is its own launch's.
+void clear_stale_error() { (void)hipGetLastError(); }
+
 template <int MODE>
 int32_t launch_split(const SplitArgs& a, int32_t batch, int32_t engine, size_t lds, hipStream_t st,
                      int device_grid = 0) {
   dim3 grid(a.S, batch), block(kThreads);
   if (device_grid > 0) grid = dim3(device_grid, 1);
   if (engine == MSA_ENGINE_DEFAULT) engine = MSA_ENGINE_VALU;
+  clear_stale_error();
   if (engine == MSA_ENGINE_VALU)
     hipLaunchKernelGGL((split_kernel<MSA_ENGINE_VALU, MODE>), grid, block, lds, st, a);
   else if (engine == MSA_ENGINE_MFMA)
@@ -1692,6 +1699,7 @@ int32_t launch_merge(const uint64_t* keys, const int32_t* lens, int32_t W, int32
   a.batch = batch;
   a.device_plan = p.device ? 1 : 0;
   a.lim = split_limits(p.S, topk);
+  clear_stale_error();
   hipLaunchKernelGGL(merge_kernel, dim3(Q * kHeads, batch), dim3(64), merge_lds_bytes(p.S, p.Lk, topk), st, a);
   return hipGetLastError() == hipSuccess ? MSA_OK : MSA_ERR_HIP;
 }
@@ -1773,6 +1781,7 @@ bool fuse_verify(const Plan& p, int topk, int qlen) {
 template <int MODE>
 void launch_verify(const VerifyArgs& a, bool fp8, int32_t batch, hipStream_t st, int device_grid = 0) {
   const dim3 grid = device_grid > 0 ? dim3(device_grid, 1) : dim3(a.S, batch);
+  clear_stale_error();
   if (fp8)
     hipLaunchKernelGGL((verify_kernel<MODE, true>), grid, dim3(kThreads), 0, st, a);
   else
@@ -1858,6 +1867,7 @@ int32_t scratch_on_current_device(hipStream_t st, char** out) {
     void* ptr = nullptr;
     if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return MSA_ERR_HIP;
     const size_t words = counters_end(kNoallocMaxBatch) / sizeof(uint32_t);
+    clear_stale_error();
     hipLaunchKernelGGL(zero_words_kernel, dim3(256), dim3(256), 0, st, static_cast<uint32_t*>(ptr), words);
     if (hipGetLastError() != hipSuccess) return MSA_ERR_HIP;
     g_scratch[dev] = static_cast<char*>(ptr);
@@ -2062,6 +2072,7 @@ int32_t msa_indexer_expand_pages_multi(const int32_t* ids, const int32_t* block_
   a.Q = qlen;
   a.out_pages = out_pages;
   a.out_tokens = out_tokens;
+  clear_stale_error();
   hipLaunchKernelGGL(expand_kernel, dim3(batch * qlen), dim3(kThreads), 0, static_cast<hipStream_t>(stream), a);
   return hipGetLastError() == hipSuccess ? MSA_OK : MSA_ERR_HIP;
 }
@@ -2092,6 +2103,7 @@ int32_t msa_indexer_read_error(void* workspace, uint32_t* host_flags, void* stre
   // Read and clear in one atomic step on the caller's stream (so a bit a kernel sets between
   // the read and the clear cannot be lost, and the clear is ordered before the stream's next
   // kernel), then copy the staged word out.
+  clear_stale_error();
   hipLaunchKernelGGL(take_error_kernel, dim3(1), dim3(1), 0, st, hdr);
   if (hipGetLastError() != hipSuccess) return MSA_ERR_HIP;
   if (hipMemcpyAsync(host_flags, hdr + 1, sizeof(uint32_t), hipMemcpyDeviceToHost, st) != hipSuccess)

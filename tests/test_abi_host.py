@@ -396,3 +396,22 @@ def test_binding_refuses_host_tensors():
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(RuntimeError, match="no non-HIP fallback"):
         _lib.load(str(tmp_path / "absent.so"))
+
+
+def test_binding_shares_pytorchs_hip_runtime():
+    # Loaded through the binding before anything imports PyTorch, the library must still end
+    # up on the one HIP runtime PyTorch uses: a second copy of the runtime in the process makes
+    # every launch on PyTorch's streams and memory fail.
+    pytest.importorskip("torch")
+    script = (
+        "import re, sys\n"
+        f"sys.path.insert(0, {os.path.dirname(os.path.dirname(os.path.abspath(__file__)))!r})\n"
+        "from sparse_attention_block_amd import _lib\n"
+        "_lib.load()\n"
+        "import torch\n"
+        "maps = open('/proc/self/maps').read()\n"
+        "print(len(set(re.findall(r'\\S*/libamdhip64\\.so\\S*', maps))))\n"
+    )
+    out = subprocess.run(["python3", "-c", script], capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.strip().splitlines()[-1] == "1"

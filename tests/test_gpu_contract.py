@@ -219,6 +219,31 @@ def test_bound_calls_match_the_binding(msa):
     assert torch.equal(ids8, w_ids) and torch.equal(sc8, w_sc)
 
 
+def test_an_earlier_failed_hip_call_is_not_reported_as_the_calls_error(msa):
+    # A HIP call made by other code before the library's call fails and leaves its error for
+    # hipGetLastError (here hipSetDevice with a device ordinal that does not exist, a host-side
+    # argument error that changes nothing). The decode and multi-token calls still return ok
+    # and their results equal those of calls made without the stale error.
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    inp = synth.paged_case(150, [128 * 40 - 5, 128 * 3, 0, 128 * 40], 40)
+    q, k, bt, lens = to_device(inp)
+    want_ids, want_sc = msa.msa_indexer_decode(q, k, bt, lens)
+    torch.cuda.synchronize()
+    assert hip.hipSetDevice(ctypes.c_int(1 << 20)) != 0
+    ids, sc = msa.msa_indexer_decode(q, k, bt, lens)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, want_ids) and torch.equal(sc, want_sc)
+    q4 = torch.from_numpy(synth.normal_bf16(151, 3, (4, 2, 4, 128)).view(np.int16)).cuda().view(torch.bfloat16)
+    want_ids4, want_sc4 = msa.msa_indexer_decode_multi(q4, k, bt, lens)
+    torch.cuda.synchronize()
+    assert hip.hipSetDevice(ctypes.c_int(1 << 20)) != 0
+    ids4, sc4 = msa.msa_indexer_decode_multi(q4, k, bt, lens)
+    torch.cuda.synchronize()
+    assert torch.equal(ids4, want_ids4) and torch.equal(sc4, want_sc4)
+    assert hip.hipGetLastError() == 0
+
+
 @pytest.mark.parametrize("pattern,elem", [(0, 2), (1, 2), (0, 1), (1, 1)])
 def test_streaming_probe_reads_exactly_the_tables_pages(pattern, elem):
     # The streaming-ceiling probe (msa_probe.h) folds every 16-byte chunk it loads into its
