@@ -98,22 +98,25 @@ def graph_us_per_call(torch, fn, calls: int = 8, replays: int = 100, rounds: int
 
 def timed_steps(torch, step, steps: int, warmup: int):
     """`warmup` untimed steps, then exactly `steps` back-to-back steps bracketed by device
-    synchronizations, with one HIP event pair on the launch stream around them (nothing is
-    enqueued between the launches). Returns (wall us per step, event us per step): the event
-    time covers the launches alone, so it cannot exceed the wall time."""
+    synchronizations. Returns (wall us per step, event us per launch). The event pair on the
+    launch stream sits after the first timed launch and after the last: the first launch waits
+    for the host to enqueue it, the others are already queued when their predecessor ends, so
+    the interval divided by steps - 1 is the launch-to-launch time of back-to-back launches
+    (each kernel plus the dispatch gap to the next), and cannot exceed the wall time per step."""
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    step()
     e0.record(stream)
-    for _ in range(steps):
+    for _ in range(steps - 1):
         step()
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return wall * 1e6 / steps, e0.elapsed_time(e1) * 1e3 / steps
+    return wall * 1e6 / steps, e0.elapsed_time(e1) * 1e3 / max(1, steps - 1)
 
 
 def rate(nbytes: int, us: float) -> dict:
@@ -608,6 +611,9 @@ def main() -> int:
                     help="run only a 1 GiB device copy (for scaling HBM counters)")
     args = ap.parse_args()
 
+    if args.steps < 2:
+        print("bench.py times launches 2 .. K against each other: use --steps 2 or more", file=sys.stderr)
+        return 2
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path, and this box has "
               "one GPU (run with --gpus 1)", file=sys.stderr)
@@ -736,8 +742,9 @@ def main() -> int:
             "frac": round(k_gbs / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(engine) if plan["fused"] and args.step == "decode" else None,
             "kernel_us": round(kernel_us, 2),
-            "kernel_time_source": f"one HIP event pair on the launch stream around the {args.steps} "
-                                  "timed back-to-back launches, divided by their number",
+            "kernel_time_source": f"one HIP event pair on the launch stream around timed launches 2 .. "
+                                  f"{args.steps} (back to back: each already queued when its predecessor "
+                                  f"ends), divided by {args.steps - 1}",
             "algorithmic_bytes_per_launch": nbytes,
         },
         "timed_region": f"{args.steps} steps launched back to back from the host, one ctypes call "
