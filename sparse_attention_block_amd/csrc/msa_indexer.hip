@@ -1186,17 +1186,24 @@ __device__ __forceinline__ bf16x8_t chunk_operand(const uint4* region, int t, in
 template <bool FP8>
 __device__ __forceinline__ void chunk_mfma(const uint4* region, int ok_g, const QMulti& qr, int lane,
                                            float (&m)[kHeads]) {
+  constexpr int TG = KvGeom<FP8>::kChunkTokens / 16;
   const int n = lane & 15, g = lane >> 4;
+  // The token groups' accumulations are independent: k-step by k-step across the groups,
+  // so each MFMA's latency overlaps the other groups' instead of stalling its own chain.
+  f32x4_t acc[TG];
 #pragma unroll
-  for (int tg = 0; tg < KvGeom<FP8>::kChunkTokens / 16; ++tg) {
-    const int t = 16 * tg + n;
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int tg = 0; tg < TG; ++tg) acc[tg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qr.a[s], chunk_operand<FP8>(region, t, s, g), acc, 0, 0, 0);
-    const bool ok = t < ok_g;
+  for (int s = 0; s < 4; ++s)
 #pragma unroll
-    for (int h = 0; h < kHeads; ++h) m[h] = ok ? fmaxf(m[h], acc[h]) : m[h];
+    for (int tg = 0; tg < TG; ++tg)
+      acc[tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qr.a[s], chunk_operand<FP8>(region, 16 * tg + n, s, g),
+                                                        acc[tg], 0, 0, 0);
+#pragma unroll
+  for (int tg = 0; tg < TG; ++tg) {
+    const bool ok = 16 * tg + n < ok_g;
+#pragma unroll
+    for (int h = 0; h < kHeads; ++h) m[h] = fmaxf(m[h], ok ? acc[tg][h] : -__builtin_inff());
   }
 }
 
