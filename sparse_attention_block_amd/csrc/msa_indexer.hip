@@ -1207,6 +1207,16 @@ __device__ __forceinline__ void chunk_mfma(const uint4* region, int ok_g, const 
   }
 }
 
+// Entry j of a block-table row, read with a scalar load (wave-uniform j). The table is
+// only read during a call, and the scalar cache starts each dispatch invalidated. A vector
+// load here would count in the wave's vector memory counter, which completes in order: the
+// wait for the page number would also wait for every chunk load issued before it, draining
+// the pipeline at each block boundary; the scalar load waits on the LDS/scalar counter only.
+__device__ __forceinline__ int table_entry(const int32_t* row, int j) {
+  typedef const __attribute__((address_space(4))) int32_t* const_row_t;
+  return ((const_row_t)row)[j];
+}
+
 struct VerifyArgs {
   const uint16_t* q;    // [batch][Q][4][128]
   const uint8_t* k;     // bf16 or E4M3 pages
@@ -1234,7 +1244,7 @@ struct VerifyArgs {
 // merge_top16 holds in at most 4 registers): kSplit, then the row's last workgroup merges
 // the lists as split_kernel does.
 template <int MODE, bool FP8>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void verify_kernel(VerifyArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void verify_kernel(VerifyArgs a) {
   using G = KvGeom<FP8>;
   __shared__ float sc[kMaxSplitBlocks][16];
   __shared__ uint4 stage[kWaves * kChunkSlots];  // one 8 KiB chunk region per wave
@@ -1299,7 +1309,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   // its page in *page. Everything here is wave-uniform and kept in scalar registers.
   auto next_block = [&](int j, int& page) {
     for (; j < j1; j += kWaves) {
-      page = __builtin_amdgcn_readfirstlane(btrow[j]);
+      page = table_entry(btrow, j);
       if (page >= 0 && (int64_t)page < a.num_pages) return j;
       if (a.err != nullptr && lane == 0) atomicOr(a.err, (uint32_t)MSA_DEVERR_PAGE_OUT_OF_RANGE);
       float m[kHeads];
@@ -1338,9 +1348,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   float m[kHeads];
 #pragma unroll
   for (int h = 0; h < kHeads; ++h) m[h] = -__builtin_inff();
-  auto process = [&](const Cursor& cur, uint4 (&A)[kChunkLoads], const Cursor& ahead) {
+  // ALWAYS: the chunk ahead is known to exist, so its load is issued without a branch.
+  auto process = [&](auto always, const Cursor& cur, uint4 (&A)[kChunkLoads], const Cursor& ahead) {
     chunk_to_lds<FP8>(region, A, lane);
-    if (ahead.j < j1) chunk_load(page_ptr(ahead), ahead.c, lane, A);
+    if (decltype(always)::value || ahead.j < j1) chunk_load(page_ptr(ahead), ahead.c, lane, A);
     chunk_mfma<FP8>(region, Lg - cur.j * kBlock - cur.c * G::kChunkTokens, qr, lane, m);
     if (cur.c + 1 == cur.nch) {
 #pragma unroll
@@ -1350,26 +1361,54 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
       for (int h = 0; h < kHeads; ++h) m[h] = -__builtin_inff();
     }
   };
+  const std::true_type always;
+  const std::false_type if_any;
   Cursor c0 = first();
   if (c0.j < j1) {
-    Cursor c1 = advance(c0), c2 = advance(c1);
+    Cursor c1 = advance(c0), c2 = advance(c1), c3, c4, c5;
     uint4 A[kChunkLoads], B[kChunkLoads], D[kChunkLoads];
-    chunk_load(page_ptr(c0), c0.c, lane, A);
-    if (c1.j < j1) chunk_load(page_ptr(c1), c1.c, lane, B);
-    if (c2.j < j1) chunk_load(page_ptr(c2), c2.c, lane, D);
-    while (true) {  // three chunks per trip so that the buffers rotate without copies
-      Cursor c3 = advance(c2);
-      process(c0, A, c3);
+    // Steady state, three chunks per trip so that the buffers rotate without copies: while
+    // the three chunks after the buffered ones all exist, every refill is issued, and the
+    // loop is entered only with all three buffers loaded. The loads in flight then follow one
+    // fixed order on every path into the loop head, so the compiler's wait for a buffer leaves
+    // the two younger buffers' loads in flight; where a load may have been skipped on some
+    // path, it has to wait for all of them.
+    if (c2.j < j1) {
+      chunk_load(page_ptr(c0), c0.c, lane, A);
+      chunk_load(page_ptr(c1), c1.c, lane, B);
+      chunk_load(page_ptr(c2), c2.c, lane, D);
+      c3 = advance(c2);
+      c4 = advance(c3);
+      c5 = advance(c4);
+      while (c5.j < j1) {
+        process(always, c0, A, c3);
+        process(always, c1, B, c4);
+        process(always, c2, D, c5);
+        c0 = c3;
+        c1 = c4;
+        c2 = c5;
+        c3 = advance(c2);
+        c4 = advance(c3);
+        c5 = advance(c4);
+      }
+    } else {
+      chunk_load(page_ptr(c0), c0.c, lane, A);
+      if (c1.j < j1) chunk_load(page_ptr(c1), c1.c, lane, B);
+      c3 = c4 = c5 = c2;
+    }
+    while (true) {  // the last chunks: refills only where a chunk remains
+      process(if_any, c0, A, c3);
       if (c1.j >= j1) break;
-      Cursor c4 = advance(c3);
-      process(c1, B, c4);
+      process(if_any, c1, B, c4);
       if (c2.j >= j1) break;
-      Cursor c5 = advance(c4);
-      process(c2, D, c5);
+      process(if_any, c2, D, c5);
       if (c3.j >= j1) break;
       c0 = c3;
       c1 = c4;
       c2 = c5;
+      c3 = advance(c2);
+      c4 = advance(c3);
+      c5 = advance(c4);
     }
   }
   if (MODE == kScores) return;
