@@ -47,6 +47,11 @@ constexpr int kBlock = MSA_BLOCK_TOKENS;
 constexpr int kWaves = 4;                       // waves per split workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxSplitBlocks = 64;             // C <= 64: one split candidate per lane
+// Verify kernel: 8 KiB chunks in flight per wave (two measured faster than three or four).
+#ifndef MSA_CHUNK_BUFFERS
+#define MSA_CHUNK_BUFFERS 2
+#endif
+constexpr int kChunkBuffers = MSA_CHUNK_BUFFERS;
 constexpr int kMaxSplits = 256;                 // merge: at most 4 lists per lane
 constexpr int kMaxMergeKeys = 4096;             // S * Lk keys of one (row, head) in LDS
 constexpr int kMaxFusedKeys = 1024;             // fused merge: S * topk keys per head, 4 heads in LDS
@@ -1342,9 +1347,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   };
   auto page_ptr = [&](const Cursor& u) { return a.k + (size_t)u.page * G::kPageBytes; };
 
-  // Three register buffers, three chunks in flight: the chunk in the oldest buffer (landed)
-  // is copied to LDS, that buffer is refilled at once with the chunk three ahead, and the
-  // MFMAs of the copied chunk run while the next two chunks and that one are loading.
+  // kChunkBuffers register buffers, as many chunks in flight: the chunk in the oldest buffer
+  // (landed) is copied to LDS, that buffer is refilled at once with the chunk kChunkBuffers
+  // ahead, and the MFMAs of the copied chunk run while the younger chunks and that one load.
   float m[kHeads];
 #pragma unroll
   for (int h = 0; h < kHeads; ++h) m[h] = -__builtin_inff();
@@ -1363,52 +1368,56 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   };
   const std::true_type always;
   const std::false_type if_any;
-  Cursor c0 = first();
-  if (c0.j < j1) {
-    Cursor c1 = advance(c0), c2 = advance(c1), c3, c4, c5;
-    uint4 A[kChunkLoads], B[kChunkLoads], D[kChunkLoads];
-    // Steady state, three chunks per trip so that the buffers rotate without copies: while
-    // the three chunks after the buffered ones all exist, every refill is issued, and the
-    // loop is entered only with all three buffers loaded. The loads in flight then follow one
-    // fixed order on every path into the loop head, so the compiler's wait for a buffer leaves
-    // the two younger buffers' loads in flight; where a load may have been skipped on some
-    // path, it has to wait for all of them.
-    if (c2.j < j1) {
-      chunk_load(page_ptr(c0), c0.c, lane, A);
-      chunk_load(page_ptr(c1), c1.c, lane, B);
-      chunk_load(page_ptr(c2), c2.c, lane, D);
-      c3 = advance(c2);
-      c4 = advance(c3);
-      c5 = advance(c4);
-      while (c5.j < j1) {
-        process(always, c0, A, c3);
-        process(always, c1, B, c4);
-        process(always, c2, D, c5);
-        c0 = c3;
-        c1 = c4;
-        c2 = c5;
-        c3 = advance(c2);
-        c4 = advance(c3);
-        c5 = advance(c4);
+  // kChunkBuffers register buffers rotate through the wave's stream: cs[0 .. NB) are the
+  // buffered chunks, cs[NB .. 2 NB) the chunks after them (a cursor past the stream: j >= j1).
+  constexpr int NB = kChunkBuffers;
+  Cursor cs[2 * NB];
+  cs[0] = first();
+  if (cs[0].j < j1) {
+    uint4 buf[NB][kChunkLoads];
+#pragma unroll
+    for (int i = 1; i < NB; ++i) cs[i] = advance(cs[i - 1]);
+    // Steady state, NB chunks per trip so that the buffers rotate without copies: while the
+    // NB chunks after the buffered ones all exist, every refill is issued, and the loop is
+    // entered only with every buffer loaded. The loads in flight then follow one fixed order
+    // on every path into the loop head, so the compiler's wait for a buffer leaves the younger
+    // buffers' loads in flight; where a load may have been skipped on some path, it has to
+    // wait for all of them.
+    if (cs[NB - 1].j < j1) {
+#pragma unroll
+      for (int i = 0; i < NB; ++i) chunk_load(page_ptr(cs[i]), cs[i].c, lane, buf[i]);
+#pragma unroll
+      for (int i = NB; i < 2 * NB; ++i) cs[i] = advance(cs[i - 1]);
+      while (cs[2 * NB - 1].j < j1) {
+#pragma unroll
+        for (int i = 0; i < NB; ++i) process(always, cs[i], buf[i], cs[NB + i]);
+#pragma unroll
+        for (int i = 0; i < NB; ++i) cs[i] = cs[NB + i];
+#pragma unroll
+        for (int i = NB; i < 2 * NB; ++i) cs[i] = advance(cs[i - 1]);
       }
     } else {
-      chunk_load(page_ptr(c0), c0.c, lane, A);
-      if (c1.j < j1) chunk_load(page_ptr(c1), c1.c, lane, B);
-      c3 = c4 = c5 = c2;
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+        if (cs[i].j < j1) chunk_load(page_ptr(cs[i]), cs[i].c, lane, buf[i]);
+#pragma unroll
+      for (int i = NB; i < 2 * NB; ++i) cs[i] = cs[NB - 1];
     }
-    while (true) {  // the last chunks: refills only where a chunk remains
-      process(if_any, c0, A, c3);
-      if (c1.j >= j1) break;
-      process(if_any, c1, B, c4);
-      if (c2.j >= j1) break;
-      process(if_any, c2, D, c5);
-      if (c3.j >= j1) break;
-      c0 = c3;
-      c1 = c4;
-      c2 = c5;
-      c3 = advance(c2);
-      c4 = advance(c3);
-      c5 = advance(c4);
+    bool more = true;
+    while (more) {  // the last chunks: refills only where a chunk remains
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        if (more) {
+          process(if_any, cs[i], buf[i], cs[NB + i]);
+          more = cs[i + 1].j < j1;
+        }
+      }
+      if (more) {
+#pragma unroll
+        for (int i = 0; i < NB; ++i) cs[i] = cs[NB + i];
+#pragma unroll
+        for (int i = NB; i < 2 * NB; ++i) cs[i] = advance(cs[i - 1]);
+      }
     }
   }
   if (MODE == kScores) return;
