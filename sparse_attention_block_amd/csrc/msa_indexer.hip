@@ -698,6 +698,13 @@ struct SplitLimits {
   int32_t blocks[5];
 };
 
+// The device plan's split width and splits per row in the case that every row is W blocks
+// long, computed on the host with the arithmetic of device_split_width (C = 0: not under
+// the device plan). See rows_full.
+struct FullRowPlan {
+  int32_t C, ns;
+};
+
 SplitLimits split_limits(int S, int topk) {
   SplitLimits l;
   for (int t = 0; t < 5; ++t) l.blocks[t] = device_max_splits(4 << t, S, topk) * (4 << t);
@@ -715,6 +722,7 @@ struct SplitArgs {
   int32_t batch;
   int32_t device_plan;  // fused mode: C and each workgroup's (row, split) chosen on the device
   SplitLimits lim;      // device plan: per-row block limits of each split width
+  FullRowPlan full;     // device plan: the plan when every row is W blocks long
   uint64_t* keys;       // [batch][S][4][Lk]
   uint32_t* err;        // device error word (may be null)
   uint32_t* counters;   // [batch][kCounterStride]: row and group counters (count_in); zero between calls
@@ -805,6 +813,7 @@ __device__ __forceinline__ bool count_in(uint32_t* row, int s, int ns) {
 struct DevicePlan {
   int C, b, s;
   bool active;
+  int L;  // the row's tokens (clamped), so the workgroup need not read its length again
 };
 
 // Wave-uniform: every lane of every wave computes the same plan. Lane l reads the lengths
@@ -835,25 +844,47 @@ __device__ __forceinline__ int device_split_width(const int32_t* lens, int batch
   return min(max(pow2_at_least(max(1, (N + kDeviceTarget - 1) / kDeviceTarget)), C_min), kMaxSplitBlocks);
 }
 
+// Whether every row (at most 64 of them) is W blocks long, given this lane's row's block
+// count nb0. The plan is then the full-row plan the host computed (the same arithmetic as
+// device_split_width over W-block rows), and the workgroups take it from one ballot instead
+// of the general plan's ballot sums and prefix scans (0.7-1.1 us per call at the
+// 32 x 1024-block benchmark shape).
+__device__ __forceinline__ bool rows_full(int batch, int W, int lane, int nb0, const FullRowPlan& full) {
+  return full.C > 0 && batch <= 64 && __ballot(lane < batch && nb0 != W) == 0;
+}
+
+// The device plan's split width (the same in every lane and every kernel of a call).
+__device__ __forceinline__ int device_width(const int32_t* lens, int batch, int W, int lane, int nb0,
+                                            const SplitLimits& lim, const FullRowPlan& full) {
+  return rows_full(batch, W, lane, nb0, full) ? full.C : device_split_width(lens, batch, W, lane, nb0, lim);
+}
+
 __device__ __forceinline__ DevicePlan device_plan(const int32_t* lens, int batch, int W,
-                                                  const SplitLimits& lim, int g, int lane) {
-  auto blocks = [&](int r) { return device_blocks(lens, batch, W, r); };
-  const int nb0 = blocks(lane);
+                                                  const SplitLimits& lim, const FullRowPlan& full,
+                                                  int g, int lane) {
+  auto tokens = [&](int r) { return r < batch ? row_tokens(lens, r, W) : 0; };
+  const int L0 = tokens(lane);
+  const int nb0 = (L0 + kBlock - 1) / kBlock;
+  if (rows_full(batch, W, lane, nb0, full)) {
+    const int b = g / full.ns;
+    return DevicePlan{full.C, b, g - b * full.ns, b < batch, __builtin_amdgcn_readlane(L0, min(b, 63))};
+  }
   const int C = device_split_width(lens, batch, W, lane, nb0, lim);
   int base = 0;
   for (int r0 = 0; r0 < batch; r0 += 64) {
     const int r = r0 + lane;
-    const int nb = r0 == 0 ? nb0 : blocks(r);
+    const int L = r0 == 0 ? L0 : tokens(r);
+    const int nb = (L + kBlock - 1) / kBlock;
     const int cnt = r < batch ? max(1, (nb + C - 1) / C) : 0;
     const int first = base + wave_prefix_small<9>(cnt);
     const uint64_t hit = __ballot(r < batch && g >= first && g < first + cnt);
     if (hit) {
       const int l = __builtin_ctzll(hit);
-      return DevicePlan{C, r0 + l, g - __builtin_amdgcn_readlane(first, l), true};
+      return DevicePlan{C, r0 + l, g - __builtin_amdgcn_readlane(first, l), true, __builtin_amdgcn_readlane(L, l)};
     }
     base += wave_sum_bits<9>(cnt);
   }
-  return DevicePlan{C, 0, 0, false};
+  return DevicePlan{C, 0, 0, false, 0};
 }
 
 // Block j of the row, held in cache page `page`: the maximum of head (lane & 3), valid in
@@ -887,7 +918,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int s = blockIdx.x, b = blockIdx.y, C = a.C;
   if (MODE == kFused && a.device_plan) {
-    const DevicePlan dp = device_plan(a.lens, a.batch, a.W, a.lim, blockIdx.x, lane);
+    const DevicePlan dp = device_plan(a.lens, a.batch, a.W, a.lim, a.full, blockIdx.x, lane);
     if (!dp.active) return;
     s = dp.s;
     b = dp.b;
@@ -1024,6 +1055,7 @@ struct MergeArgs {
   int32_t batch;
   int32_t device_plan;  // C (and Lk = min(topk, C)) chosen on the device, as the split pass did
   SplitLimits lim;
+  FullRowPlan full;     // device plan: the plan when every row is W blocks long
   const uint64_t* keys;
   int32_t* out_ids;     // [batch][Q][4][topk]
   float* out_scores;
@@ -1047,8 +1079,8 @@ __global__ __launch_bounds__(64) void merge_kernel(MergeArgs a) {
   const int nb = (L + kBlock - 1) / kBlock;
   const int Lp = causal_len(L, a.Q, p);
   const int m = min(a.topk, (Lp + kBlock - 1) / kBlock);
-  const int C = a.device_plan ? device_split_width(a.lens, a.batch, a.W, lane,
-                                                   device_blocks(a.lens, a.batch, a.W, lane), a.lim)
+  const int C = a.device_plan ? device_width(a.lens, a.batch, a.W, lane,
+                                             device_blocks(a.lens, a.batch, a.W, lane), a.lim, a.full)
                               : a.C;
   const int ns = (nb + C - 1) / C;
   const int Lk = a.device_plan ? min(a.topk, C) : a.Lk, stride = Lk + 1, QH = a.Q * kHeads;
@@ -1234,6 +1266,7 @@ struct VerifyArgs {
   int32_t batch;
   int32_t device_plan;  // split modes: C and each workgroup's (row, split) chosen on the device
   SplitLimits lim;
+  FullRowPlan full;     // device plan: the plan when every row is W blocks long
   uint64_t* keys;       // [batch][S][Q*4][Lk]
   uint32_t* err;        // device error word (may be null)
   float* scores;        // [batch][Q][4][W] (block-score mode)
@@ -1257,16 +1290,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4;
-  int s = blockIdx.x, b = blockIdx.y, C = a.C, Lk = a.Lk;
+  int s = blockIdx.x, b = blockIdx.y, C = a.C, Lk = a.Lk, L;
   if (MODE != kScores && a.device_plan) {
-    const DevicePlan dp = device_plan(a.lens, a.batch, a.W, a.lim, blockIdx.x, lane);
+    const DevicePlan dp = device_plan(a.lens, a.batch, a.W, a.lim, a.full, blockIdx.x, lane);
     if (!dp.active) return;
     s = dp.s;
     b = dp.b;
     C = dp.C;
     Lk = min(a.topk, C);
+    L = dp.L;
+  } else {
+    L = row_tokens(a.lens, b, a.W);
   }
-  const int L = row_tokens(a.lens, b, a.W);
   const int nb = (L + kBlock - 1) / kBlock;
   const int Lg = g < a.Q ? causal_len(L, a.Q, g) : 0;
   const int32_t* btrow = a.bt + (size_t)b * a.bt_stride;
@@ -1673,6 +1708,17 @@ int32_t launch_split(const SplitArgs& a, int32_t batch, int32_t engine, size_t l
   return hipGetLastError() == hipSuccess ? MSA_OK : MSA_ERR_HIP;
 }
 
+// The device plan at full rows (device_split_width with every row W blocks long).
+FullRowPlan full_row_plan(bool device, int32_t batch, int32_t W, const SplitLimits& lim) {
+  if (!device || W <= 0 || batch <= 0) return FullRowPlan{0, 1};
+  int C_min = 4;
+  for (int t = 0; t < 5; ++t)
+    if (W > lim.blocks[t]) C_min = 4 << (t + 1);
+  const int64_t per_wg = std::max<int64_t>(1, ((int64_t)batch * W + kDeviceTarget - 1) / kDeviceTarget);
+  const int C = std::min(std::max(pow2_at_least((int)std::min<int64_t>(per_wg, 1 << 20)), C_min), kMaxSplitBlocks);
+  return FullRowPlan{C, (W + C - 1) / C};
+}
+
 SplitArgs make_split_args(const void* q, const void* k, const int32_t* bt, const int32_t* lens,
                           int32_t W, int32_t bt_stride, int64_t num_pages, const Plan& p,
                           int32_t topk, int32_t n_init, int32_t n_local, const WsView& w, int32_t batch) {
@@ -1693,6 +1739,7 @@ SplitArgs make_split_args(const void* q, const void* k, const int32_t* bt, const
   a.batch = batch;
   a.device_plan = p.device ? 1 : 0;
   a.lim = split_limits(p.S, topk);
+  a.full = full_row_plan(p.device, batch, W, a.lim);
   a.err = w.err;
   a.counters = w.counters;
   a.keys = w.keys;
@@ -1754,6 +1801,7 @@ int32_t launch_merge(const uint64_t* keys, const int32_t* lens, int32_t W, int32
   a.batch = batch;
   a.device_plan = p.device ? 1 : 0;
   a.lim = split_limits(p.S, topk);
+  a.full = full_row_plan(p.device, batch, W, a.lim);
   clear_stale_error();
   hipLaunchKernelGGL(merge_kernel, dim3(Q * kHeads, batch), dim3(64), merge_lds_bytes(p.S, p.Lk, topk), st, a);
   return hipGetLastError() == hipSuccess ? MSA_OK : MSA_ERR_HIP;
@@ -1809,6 +1857,7 @@ VerifyArgs make_verify_args(const void* q, const void* k, const int32_t* bt, con
   a.batch = batch;
   a.device_plan = p.device ? 1 : 0;
   a.lim = split_limits(p.S, topk);
+  a.full = full_row_plan(p.device, batch, W, a.lim);
   return a;
 }
 

@@ -79,6 +79,21 @@ def test_planted_exact_under_device_plan(msa):
     assert np.array_equal(sc.cpu().numpy().astype(np.float64), want_sc)
 
 
+def test_full_rows_take_the_full_row_plan(msa):
+    # Every row W blocks long: the workgroups take the host's full-row plan from one ballot
+    # instead of computing the general plan. The same rows with one row a block short take the
+    # general plan; both (and the multi-token and FP8 passes on each) select as the oracle does.
+    from test_gpu_fp8 import run_fp8
+    from test_gpu_multi import run_multi
+
+    W, B = 600, 16
+    assert msa.plan(B, W, 16)["blocks_per_split"] == 0
+    for name, lens in (("full", [128 * W] * B), ("one row short", [128 * W] * 5 + [128 * (W - 1)] + [128 * W] * 10)):
+        check(msa, synth.paged_case(415, lens, W, poison=False))
+        run_multi(msa, synth.multi_case(416, lens, W, 2, poison=False))
+        run_fp8(msa, synth.fp8_case(417, lens, W, 1, k_scale=0.5, poison=False), 1e-3 * 4.0 * 0.5)
+
+
 def test_split_width_changes_between_graph_replays(msa):
     # The captured grid covers any lengths; replays with lengths that move the device's
     # split width (C = 4 .. 64) and the long row's split count must match eager calls.
