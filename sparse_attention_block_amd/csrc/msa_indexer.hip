@@ -1254,6 +1254,16 @@ __device__ __forceinline__ int table_entry(const int32_t* row, int j) {
   return ((const_row_t)row)[j];
 }
 
+// Inserts key k into each 16-lane row of x (sorted best first, zero padded, k the same in
+// every lane of a row): a row's lanes below k's place keep their keys, the lane at its place
+// takes k and the lanes after it take their predecessor's key, so the row's last key drops
+// out. Zero keys change nothing.
+__device__ __forceinline__ uint64_t row_insert(uint64_t x, uint64_t k, int lane) {
+  constexpr int kRowShr1 = 0x111;  // row_shr:1: the key of lane - 1 within the row
+  const uint64_t prev = dpp_u64<kRowShr1>(x);
+  return x > k ? x : (((lane & 15) == 0 || prev > k) ? k : prev);
+}
+
 struct VerifyArgs {
   const uint16_t* q;    // [batch][Q][4][128]
   const uint8_t* k;     // bf16 or E4M3 pages
@@ -1281,7 +1291,7 @@ struct VerifyArgs {
 // split's top Lk keys, best first, zero padded. kFused (one position, topk <= 16, lists that
 // merge_top16 holds in at most 4 registers): kSplit, then the row's last workgroup merges
 // the lists as split_kernel does.
-template <int MODE, bool FP8>
+template <int MODE, bool FP8, bool RUNNING>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void verify_kernel(VerifyArgs a) {
   using G = KvGeom<FP8>;
   __shared__ float sc[kMaxSplitBlocks][16];
@@ -1326,6 +1336,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   QMulti qr;
   load_q_multi(a.q, b, a.Q, lane, qr);
   uint4* region = stage + wave * kChunkSlots;
+  // RUNNING (several positions, topk <= 16; chosen on the host): each wave keeps the top 16 of
+  // its own blocks per (position, head) as it goes: register h, row p (lanes 16 p .. 16 p +
+  // 15) holds position p's keys of head h, best first. Its lanes hold position p's block
+  // maxima (lane group p), so a block's keys are inserted where they are, and at the end the
+  // four waves' lists merge in a few steps instead of the Q sorts of the split's 64 keys
+  // after the last block (bf16 four positions 164.4 -> 162.7 us, FP8 four positions 87.0 ->
+  // 86.1 us). One position pays the same insertions for a single sort and keeps the sort.
+  constexpr bool running = RUNNING && MODE != kScores;
+  uint64_t top[kHeads] = {0, 0, 0, 0};
+  const int nbp_g = (causal_len(L, a.Q, min(g, a.Q - 1)) + kBlock - 1) / kBlock;  // lane group g's position
 
   // The wave's blocks j0 + wave, j0 + wave + 4, ... as one stream of 32-token chunks: chunk
   // c of block j holds tokens 32c .. 32c+31; a block has ceil(vmax / 32) chunks, vmax the
@@ -1334,6 +1354,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     if (FP8) {
 #pragma unroll
       for (int h = 0; h < kHeads; ++h) m[h] *= a.k_scale;
+    }
+    if constexpr (running) {
+      // A block past position g's end has no key.
+      const bool real = g < a.Q && j < nbp_g;
+      const bool pinned = j < a.n_init || j >= nbp_g - a.n_local;
+#pragma unroll
+      for (int h = 0; h < kHeads; ++h) top[h] = row_insert(top[h], real ? make_key(m[h], j, pinned) : 0, lane);
+      return;
     }
     if ((lane & 15) == 0 && g < a.Q) {
       if (MODE == kScores) {
@@ -1456,12 +1484,45 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
   }
   if (MODE == kScores) return;
+  if constexpr (running) {  // the wave's lists to its own staging region, which it alone has used
+    uint64_t* own = reinterpret_cast<uint64_t*>(region);
+#pragma unroll
+    for (int h = 0; h < kHeads; ++h) own[h * 64 + lane] = top[h];
+  }
   __syncthreads();
+
+  const int h = wave;
+  if constexpr (running) {
+    // Wave h merges the four waves' lists of head h, every position's row at once: the split's
+    // top 16 per (position, head), best first, in row p.
+    uint64_t r[16];
+#pragma unroll
+    for (int w = 0; w < 16; ++w)
+      r[w] = w < kWaves ? reinterpret_cast<const uint64_t*>(stage + w * kChunkSlots)[h * 64 + lane] : 0;
+    merge_level<2>(r, lane);
+    merge_level<1>(r, lane);
+    const int i = lane & 15;
+    if (g < a.Q) {
+      if (MODE == kFused && nb <= C) {
+        // The row's only split: each position's keys are its selection.
+        const int m = min(a.topk, nbp_g);
+        const size_t o = (((size_t)b * a.Q + g) * kHeads + h) * a.topk;
+        if (i < a.topk) {
+          a.out_ids[o + i] = i < m ? key_id(r[0]) : -1;
+          a.out_scores[o + i] = i < m ? key_score(r[0]) : -__builtin_inff();
+        }
+      } else if (i < Lk) {
+        uint64_t* out = a.keys + list_offset(b, a.S, a.Q * kHeads, a.Lk, s, 4 * g + h, Lk);
+        if (MODE == kFused) __hip_atomic_store(out + i, r[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else out[i] = r[0];
+      }
+    }
+    if (MODE != kFused || nb <= C) return;
+  }
 
   // Wave h sorts head h's keys of every position (the positions side by side) and keeps the
   // first Lk. A block past position p's end has no key (0).
   const int n = j1 - j0;
-  const int h = wave;
   auto key_of = [&](int p) -> uint64_t {
     const int nbp = (causal_len(L, a.Q, p) + kBlock - 1) / kBlock;
     const int jj = j0 + lane;
@@ -1483,7 +1544,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       if (lane < Lk) out[lane] = key;
     }
   };
-  if (a.Q == 1) {
+  if constexpr (running) {
+    // published above
+  } else if (a.Q == 1) {
     uint64_t k[1] = {key_of(0)};
     sort_desc_first_all<1>(k, lane, n);
     publish(0, k[0]);
@@ -1885,11 +1948,16 @@ bool fuse_verify(const Plan& p, int topk, int qlen) {
 template <int MODE>
 void launch_verify(const VerifyArgs& a, bool fp8, int32_t batch, hipStream_t st, int device_grid = 0) {
   const dim3 grid = device_grid > 0 ? dim3(device_grid, 1) : dim3(a.S, batch);
+  const bool running = MODE != kScores && a.Q > 1 && a.topk <= kNetworkMaxM;
   clear_stale_error();
-  if (fp8)
-    hipLaunchKernelGGL((verify_kernel<MODE, true>), grid, dim3(kThreads), 0, st, a);
+  if (fp8 && running)
+    hipLaunchKernelGGL((verify_kernel<MODE, true, true>), grid, dim3(kThreads), 0, st, a);
+  else if (fp8)
+    hipLaunchKernelGGL((verify_kernel<MODE, true, false>), grid, dim3(kThreads), 0, st, a);
+  else if (running)
+    hipLaunchKernelGGL((verify_kernel<MODE, false, true>), grid, dim3(kThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((verify_kernel<MODE, false>), grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((verify_kernel<MODE, false, false>), grid, dim3(kThreads), 0, st, a);
 }
 
 int32_t verify_decode_impl(const void* q, const void* k_cache, bool fp8, float k_scale,
