@@ -1336,13 +1336,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   QMulti qr;
   load_q_multi(a.q, b, a.Q, lane, qr);
   uint4* region = stage + wave * kChunkSlots;
-  // RUNNING (several positions, topk <= 16; chosen on the host): each wave keeps the top 16 of
-  // its own blocks per (position, head) as it goes: register h, row p (lanes 16 p .. 16 p +
-  // 15) holds position p's keys of head h, best first. Its lanes hold position p's block
-  // maxima (lane group p), so a block's keys are inserted where they are, and at the end the
-  // four waves' lists merge in a few steps instead of the Q sorts of the split's 64 keys
+  // RUNNING (three or four positions, topk <= 16; chosen on the host): each wave keeps the
+  // top 16 of its own blocks per (position, head) as it goes: register h, row p (lanes 16 p ..
+  // 16 p + 15) holds position p's keys of head h, best first. Its lanes hold position p's
+  // block maxima (lane group p), so a block's keys are inserted where they are, and at the end
+  // the four waves' lists merge in a few steps instead of the Q sorts of the split's keys
   // after the last block (bf16 four positions 164.4 -> 162.7 us, FP8 four positions 87.0 ->
-  // 86.1 us). One position pays the same insertions for a single sort and keeps the sort.
+  // 86.1 us). Fewer positions pay the same insertions for fewer sorts and keep the sorts.
   constexpr bool running = RUNNING && MODE != kScores;
   uint64_t top[kHeads] = {0, 0, 0, 0};
   const int nbp_g = (causal_len(L, a.Q, min(g, a.Q - 1)) + kBlock - 1) / kBlock;  // lane group g's position
@@ -1948,7 +1948,11 @@ bool fuse_verify(const Plan& p, int topk, int qlen) {
 template <int MODE>
 void launch_verify(const VerifyArgs& a, bool fp8, int32_t batch, hipStream_t st, int device_grid = 0) {
   const dim3 grid = device_grid > 0 ? dim3(device_grid, 1) : dim3(a.S, batch);
-  const bool running = MODE != kScores && a.Q > 1 && a.topk <= kNetworkMaxM;
+  // The running lists pay per block and save the sorts after the last one: measured ahead
+  // with three or four positions at every shape tried (bf16 four positions at the benchmark
+  // shape 165.1 -> 163.4 us, at 16 x 8700 tokens 12.4 -> 12.1 us), behind with two positions
+  // on short splits (16 x 8700 tokens 11.5 -> 11.7 us).
+  const bool running = MODE != kScores && a.Q >= 3 && a.topk <= kNetworkMaxM;
   clear_stale_error();
   if (fp8 && running)
     hipLaunchKernelGGL((verify_kernel<MODE, true, true>), grid, dim3(kThreads), 0, st, a);
