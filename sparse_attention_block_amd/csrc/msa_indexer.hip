@@ -757,28 +757,27 @@ constexpr int kDeviceMaxSplits = 64;   // splits per row at 16 or more blocks pe
 // row lengths read before any page) costs ~1 us, which only pays where a row can be long.
 constexpr int64_t kDeviceMinBlocks = 8192;
 
-// Exclusive prefix sum over the wave of c in [0, 2^BITS), without LDS: one ballot per bit.
-template <int BITS>
-__device__ __forceinline__ int wave_prefix_small(int c) {
-  int off = 0;
-#pragma unroll
-  for (int bit = 0; bit < BITS; ++bit) {
-    const uint64_t mask = __ballot((c >> bit) & 1);
-    const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
-                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-    off += (int)below << bit;
-  }
-  return off;
+// Inclusive prefix sum over the 64 lanes, without LDS: DPP adds within each 16-lane row (the
+// lanes 1, 2 and 3 below, then 4 and 8 below with the bank masks that keep a row's lower lanes
+// out), then the row broadcasts of lane 15 to rows 1 and 3 and of lane 31 to rows 2 and 3.
+// Seven dependent adds, where a ballot per bit takes one ballot, two mbcnt and an add per bit.
+template <int CTRL, int ROW_MASK, int BANK_MASK>
+__device__ __forceinline__ int dpp_or_zero(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, ROW_MASK, BANK_MASK, false);
 }
 
-// Sum over the wave of x in [0, 2^BITS), without LDS: one ballot per bit.
-template <int BITS>
-__device__ __forceinline__ int wave_sum_bits(int x) {
-  int total = 0;
-#pragma unroll
-  for (int bit = 0; bit < BITS; ++bit) total += __popcll(__ballot((x >> bit) & 1)) << bit;
-  return total;
+__device__ __forceinline__ int wave_scan(int x) {
+  int s = x + dpp_or_zero<0x111, 0xF, 0xF>(x);   // row_shr:1
+  s += dpp_or_zero<0x112, 0xF, 0xF>(x);          // row_shr:2
+  s += dpp_or_zero<0x113, 0xF, 0xF>(x);          // row_shr:3
+  s += dpp_or_zero<0x114, 0xF, 0xE>(s);          // row_shr:4, lanes 4..15 of each row
+  s += dpp_or_zero<0x118, 0xF, 0xC>(s);          // row_shr:8, lanes 8..15 of each row
+  s += dpp_or_zero<0x142, 0xA, 0xF>(s);          // row_bcast:15 into rows 1 and 3
+  s += dpp_or_zero<0x143, 0xC, 0xF>(s);          // row_bcast:31 into rows 2 and 3
+  return s;
 }
+
+__device__ __forceinline__ int wave_sum(int x) { return __builtin_amdgcn_readlane(wave_scan(x), 63); }
 
 // Where the list of split s, task t (position-head p * 4 + h) of row b starts in the
 // workspace keys: rows lie S * QH * LkMax keys apart (LkMax = the plan's Lk; topk under
@@ -818,8 +817,8 @@ struct DevicePlan {
 
 // Wave-uniform: every lane of every wave computes the same plan. Lane l reads the lengths
 // of rows l, l+64, ... (rows past the first 64 are read again in the second pass; they are
-// cache hits); sums, the longest-row bound and prefix sums are ballots, without LDS. Block
-// counts are at most 4096 (13 bits) and split counts at most 256 (9 bits).
+// cache hits); sums and prefix sums are DPP scans and the longest-row bounds ballots, without
+// LDS.
 __device__ __forceinline__ int device_blocks(const int32_t* lens, int batch, int W, int r) {
   return r < batch ? (row_tokens(lens, r, W) + kBlock - 1) / kBlock : 0;
 }
@@ -834,7 +833,7 @@ __device__ __forceinline__ int device_split_width(const int32_t* lens, int batch
   bool over[5] = {false, false, false, false, false};  // a row does not fit splits of 4 << t blocks
   for (int r0 = 0; r0 < batch; r0 += 64) {
     const int nb = r0 == 0 ? nb0 : blocks(r0 + lane);
-    N += wave_sum_bits<13>(nb);
+    N += wave_sum(nb);
 #pragma unroll
     for (int t = 0; t < 5; ++t) over[t] = over[t] || __ballot(nb > lim.blocks[t]) != 0;
   }
@@ -870,19 +869,21 @@ __device__ __forceinline__ DevicePlan device_plan(const int32_t* lens, int batch
     return DevicePlan{full.C, b, g - b * full.ns, b < batch, __builtin_amdgcn_readlane(L0, min(b, 63))};
   }
   const int C = device_split_width(lens, batch, W, lane, nb0, lim);
+  const int log2C = __builtin_ctz(C);  // C is a power of two
   int base = 0;
   for (int r0 = 0; r0 < batch; r0 += 64) {
     const int r = r0 + lane;
     const int L = r0 == 0 ? L0 : tokens(r);
     const int nb = (L + kBlock - 1) / kBlock;
-    const int cnt = r < batch ? max(1, (nb + C - 1) / C) : 0;
-    const int first = base + wave_prefix_small<9>(cnt);
+    const int cnt = r < batch ? max(1, (nb + C - 1) >> log2C) : 0;
+    const int inclusive = wave_scan(cnt);
+    const int first = base + inclusive - cnt;
     const uint64_t hit = __ballot(r < batch && g >= first && g < first + cnt);
     if (hit) {
       const int l = __builtin_ctzll(hit);
       return DevicePlan{C, r0 + l, g - __builtin_amdgcn_readlane(first, l), true, __builtin_amdgcn_readlane(L, l)};
     }
-    base += wave_sum_bits<9>(cnt);
+    base += __builtin_amdgcn_readlane(inclusive, 63);
   }
   return DevicePlan{C, 0, 0, false, 0};
 }
