@@ -786,7 +786,7 @@ def main() -> int:
                                               fp8_scale=f8.k_scale)
         extra["streaming_ceiling_fp8"] = rate(f8.index_k_bytes, streaming_ceiling(torch, k8, bt8, 16384, 1))
         extra["streaming_ceiling_fp8"]["what"] = ("the same 512 MiB of shuffled 16 KiB FP8 pages read with "
-                                                  "the verify kernel's load pattern (8 KiB chunks, three in "
+                                                  "the verify kernel's load pattern (8 KiB chunks, two in "
                                                   "flight per wave) and no arithmetic, graph protocol")
         del k8, f8
         torch.cuda.empty_cache()

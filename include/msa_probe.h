@@ -16,7 +16,7 @@ extern "C" {
 #endif
 
 #define MSA_PROBE_SPLIT_PATTERN 0  /* the VALU decode kernel: pages in batches of 16 KiB */
-#define MSA_PROBE_CHUNK_PATTERN 1  /* the verify kernel: 8 KiB chunks, three in flight per wave */
+#define MSA_PROBE_CHUNK_PATTERN 1  /* the verify kernel: 8 KiB chunks, two in flight per wave */
 
 /*
  * Reads every page block_table[b][j], j < W, of `page_bytes` bytes (a multiple of 16 KiB: 32 KiB

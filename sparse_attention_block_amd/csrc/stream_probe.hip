@@ -10,7 +10,7 @@
 //   kSplitPattern   the VALU decode kernel's: each page in batches of 16 loads (16 KiB),
 //                   one batch landing before the next is issued;
 //   kChunkPattern   the verify kernel's (multi-token and FP8 passes): a wave's pages as one
-//                   stream of 8 KiB chunks (8 loads), three chunks in flight.
+//                   stream of 8 KiB chunks (8 loads), two chunks in flight.
 
 #include <hip/hip_runtime.h>
 
@@ -84,19 +84,15 @@ __global__ __launch_bounds__(256) void probe_kernel(ProbeArgs a) {
 #pragma unroll
       for (int i = 0; i < kChunk; ++i) fold(x, v[i]);
     };
-    uint4 A[kChunk], B[kChunk], D[kChunk];
+    uint4 A[kChunk], B[kChunk];
     load(0, A);
     load(1, B);
-    load(2, D);
-    for (int c = 0; c < n; c += 3) {
+    for (int c = 0; c < n; c += 2) {
       take(A);
-      load(c + 3, A);
+      load(c + 2, A);
       if (c + 1 >= n) break;
       take(B);
-      load(c + 4, B);
-      if (c + 2 >= n) break;
-      take(D);
-      load(c + 5, D);
+      load(c + 3, B);
     }
   }
   a.out[((size_t)b * gridDim.x + s) * 256 + threadIdx.x] = x.x ^ x.y ^ x.z ^ x.w;
