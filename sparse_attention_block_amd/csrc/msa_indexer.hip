@@ -349,6 +349,32 @@ __device__ __forceinline__ float score_block_valu(const uint16_t* __restrict__ p
   return dpp_f32<kQuadSwapMid>(m);  // lane l & 3 = h now holds head h
 }
 
+// Spread layout: wave w scores quarter w of a block, tokens 32 w .. 32 w + 31, which are wave
+// loads 8 w .. 8 w + 7 of the page. The maximum over its first `vw` tokens (vw <= 0: none,
+// -inf) of head (lane & 3), in lanes 0..3 (and every lane with the same lane & 3).
+__device__ __forceinline__ float quarter_max(const uint4 (&kv)[8], int vw, const QValu& qr, int lane) {
+  const int row = lane >> 4;
+  const bool b0 = (lane & 1) != 0, b1 = (lane & 2) != 0;
+  float m = -__builtin_inff();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float x = row_sum4_scatter(dot8(kv[i], qr.d[0]), dot8(kv[i], qr.d[1]), dot8(kv[i], qr.d[2]),
+                                     dot8(kv[i], qr.d[3]), b0, b1);
+    m = 4 * i + row < vw ? fmaxf(m, x) : m;
+  }
+  m = fmaxf(m, __shfl_xor(m, 16));
+  m = fmaxf(m, __shfl_xor(m, 32));
+  return dpp_f32<kQuadSwapMid>(m);
+}
+
+// Loads a wave's quarter of a page (p: the page's first uint4 plus this lane's offset and
+// the quarter's; only loads that hold one of the first vw tokens when not FULL).
+template <bool FULL>
+__device__ __forceinline__ void quarter_load(const uint4* p, int vw, uint4 (&kv)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) kv[i] = (FULL || 4 * i < vw) ? load_stream(p + i * 64) : make_uint4(0, 0, 0, 0);
+}
+
 // MFMA engine. v_mfma_f32_16x16x32_bf16 with A = q (rows = heads, padded 4 -> 16 with
 // zeros) and B = K^T (columns = 16 tokens of a tile). Lane l supplies row/column l%16 and
 // 8 consecutive k-slots of lane group g = l/16; A and B use the same slots, so any fixed
@@ -721,6 +747,7 @@ struct SplitArgs {
   int32_t S, C, Lk, topk, n_init, n_local;
   int32_t batch;
   int32_t device_plan;  // fused mode: C and each workgroup's (row, split) chosen on the device
+  int32_t spread;       // VALU engine, not block-score mode: each wave scores a quarter of every block
   SplitLimits lim;      // device plan: per-row block limits of each split width
   FullRowPlan full;     // device plan: the plan when every row is W blocks long
   uint64_t* keys;       // [batch][S][4][Lk]
@@ -778,6 +805,17 @@ __device__ __forceinline__ int wave_scan(int x) {
 }
 
 __device__ __forceinline__ int wave_sum(int x) { return __builtin_amdgcn_readlane(wave_scan(x), 63); }
+
+// Largest of the 64 lanes' non-negative values.
+__device__ __forceinline__ int wave_max_nonneg(int x) {
+  uint32_t u = (uint32_t)x;
+  u = max(u, dpp_u32<kQuadSwap1>(u));
+  u = max(u, dpp_u32<kQuadSwap2>(u));
+  u = max(u, dpp_u32<kRowHalfMirror>(u));
+  u = max(u, dpp_u32<kRowMirror>(u));
+  return (int)max(max((uint32_t)__builtin_amdgcn_readlane((int)u, 0), (uint32_t)__builtin_amdgcn_readlane((int)u, 16)),
+                  max((uint32_t)__builtin_amdgcn_readlane((int)u, 32), (uint32_t)__builtin_amdgcn_readlane((int)u, 48)));
+}
 
 // Where the list of split s, task t (position-head p * 4 + h) of row b starts in the
 // workspace keys: rows lie S * QH * LkMax keys apart (LkMax = the plan's Lk; topk under
@@ -870,6 +908,31 @@ __device__ __forceinline__ DevicePlan device_plan(const int32_t* lens, int batch
   }
   const int C = device_split_width(lens, batch, W, lane, nb0, lim);
   const int log2C = __builtin_ctz(C);  // C is a power of two
+  if (batch <= 64) {
+    // The row with the most splits (the first such) takes workgroups 0, 1, .., the rows after
+    // it follow in order and wrap around. Workgroups are dispatched in order, one per CU
+    // until every CU holds one; a later one shares a CU with an earlier one, whose waves are
+    // older and win the CU's arbitration, so it finishes later. The longest row, whose merge
+    // also ends the call, then never waits for a second workgroup on its CUs.
+    const int cnt = lane < batch ? max(1, (nb0 + C - 1) >> log2C) : 0;
+    const int inclusive = wave_scan(cnt);
+    const int total = __builtin_amdgcn_readlane(inclusive, 63);
+    const int top = wave_max_nonneg(cnt);
+    const int r0 = __builtin_ctzll(__ballot(lane < batch && cnt == top));
+    const int shift = __builtin_amdgcn_readlane(inclusive, r0) - __builtin_amdgcn_readlane(cnt, r0);
+    int gr = g;
+    if (g < total) {
+      gr = g + shift;
+      if (gr >= total) gr -= total;
+    }
+    const uint64_t hit = __ballot(lane < batch && gr >= inclusive - cnt && gr < inclusive);
+    if (hit) {
+      const int l = __builtin_ctzll(hit);
+      return DevicePlan{C, l, gr - (__builtin_amdgcn_readlane(inclusive, l) - __builtin_amdgcn_readlane(cnt, l)),
+                        true, __builtin_amdgcn_readlane(L0, l)};
+    }
+    return DevicePlan{C, 0, 0, false, 0};
+  }
   int base = 0;
   for (int r0 = 0; r0 < batch; r0 += 64) {
     const int r = r0 + lane;
@@ -890,6 +953,16 @@ __device__ __forceinline__ DevicePlan device_plan(const int32_t* lens, int batch
 
 // Block j of the row, held in cache page `page`: the maximum of head (lane & 3), valid in
 // lanes 0..3.
+// Entry j of a block-table row, read with a scalar load (wave-uniform j). The table is
+// only read during a call, and the scalar cache starts each dispatch invalidated. A vector
+// load here would count in the wave's vector memory counter, which completes in order: the
+// wait for the page number would also wait for every chunk load issued before it, draining
+// the pipeline at each block boundary; the scalar load waits on the LDS/scalar counter only.
+__device__ __forceinline__ int table_entry(const int32_t* row, int j) {
+  typedef const __attribute__((address_space(4))) int32_t* const_row_t;
+  return ((const_row_t)row)[j];
+}
+
 template <int ENGINE>
 __device__ __forceinline__ float score_page(const SplitArgs& a, int page, int j, int L, int lane,
                                             const void* qr) {
@@ -909,14 +982,18 @@ __device__ __forceinline__ float score_page(const SplitArgs& a, int page, int j,
   }
 }
 
-template <int ENGINE, int MODE>
+// SPREAD (VALU engine, not block-score mode): the spread layout, each wave scoring a quarter of
+// every block of the split (chosen on the host, SplitArgs::spread).
+template <int ENGINE, int MODE, bool SPREAD>
 __global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
+  static_assert(!SPREAD || (ENGINE == MSA_ENGINE_VALU && MODE != kScores), "spread: VALU engine, lists");
   extern __shared__ uint64_t lk[];  // fused mode: [S][4][Lk] lists of one row, then merge scratch
-  __shared__ float sc[kMaxSplitBlocks][kHeads];
+  __shared__ float sc[SPREAD ? kWaves : 1][kMaxSplitBlocks][kHeads];  // block maxima (spread: per quarter)
   __shared__ int s_last;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  constexpr bool spread = SPREAD;
   int s = blockIdx.x, b = blockIdx.y, C = a.C;
   if (MODE == kFused && a.device_plan) {
     const DevicePlan dp = device_plan(a.lens, a.batch, a.W, a.lim, a.full, blockIdx.x, lane);
@@ -932,7 +1009,9 @@ __global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
   // being scored.
   const int32_t* btrow = a.bt + (size_t)b * a.bt_stride;
   const int j_first = s * C + wave;
-  int page = j_first < a.W ? btrow[j_first] : 0;
+  int page = !spread && j_first < a.W ? btrow[j_first] : 0;
+  // Spread layout: lane u < C holds the page number of the split's block s * C + u.
+  const int pg_spread = spread && lane < C && s * C + lane < a.W ? btrow[s * C + lane] : -1;
   typename std::conditional<ENGINE == MSA_ENGINE_MFMA, QMfma, QValu>::type qr;
   if constexpr (ENGINE == MSA_ENGINE_MFMA) load_q_mfma(a.q, b, lane, qr);
   else load_q_valu(a.q, b, lane, qr);
@@ -975,11 +1054,85 @@ __global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
     }
     return;
   }
-  for (int j = j0 + wave; j < j1; j += kWaves) {
-    const int next = j + kWaves < j1 ? btrow[j + kWaves] : 0;
-    const float m = score_page<ENGINE>(a, page, j, L, lane, &qr);
-    if (lane < kHeads) sc[j - j0][lane] = m;
-    page = next;
+  if constexpr (SPREAD) {
+    {
+      // Wave w takes quarter w of each of the split's n blocks ("units" 0 .. n-1), read
+      // through NB rotating register buffers of 8 wave loads: NB units in flight. Lane u holds
+      // unit u's page number (read with the row length). A quarter past the block's valid
+      // tokens scores -inf (quarter 0 of a block of the row always holds a token, so the
+      // maximum over the four quarters is the block's). When every page is in range, each
+      // unit is read whole whatever its valid tokens (in bounds: the page exists), so every
+      // load of the steady state is issued unconditionally and the wait for a buffer leaves
+      // the younger buffers' loads in flight (a load that may have been skipped would force
+      // a wait for all of them). A page out of range is reported and its unit not read.
+      constexpr int NB = 2;
+      const int n = j1 - j0;
+      const bool in_range = pg_spread >= 0 && (int64_t)pg_spread < a.num_pages;
+      if (a.err != nullptr && lane < n && !in_range) atomicOr(a.err, (uint32_t)MSA_DEVERR_PAGE_OUT_OF_RANGE);
+      const uint64_t okm = __ballot(lane < n && in_range);
+      auto valid_of = [&](int u) { return min(32, min(kBlock, L - (j0 + u) * kBlock) - 32 * wave); };
+      auto quarter_of = [&](int u) {
+        const int pg = __builtin_amdgcn_readlane(pg_spread, u);
+        return reinterpret_cast<const uint4*>(a.k + (size_t)pg * kPageElems) + wave * 512 + lane;
+      };
+      auto issue = [&](int u, uint4 (&kv)[8]) { quarter_load<true>(quarter_of(u), 32, kv); };
+      auto score = [&](int u, const uint4 (&kv)[8]) {
+        const float m = quarter_max(kv, valid_of(u), qr, lane);
+        if (lane < kHeads) sc[wave][u][lane] = m;
+      };
+      uint4 buf[NB][8];
+      if (okm == (n == 64 ? ~0ull : (1ull << n) - 1)) {
+        if (n <= NB) {
+          // All n units in flight at once, n a compile-time constant in each case (a load
+          // under a branch here made the compiler wait for every earlier load first).
+          auto all = [&](auto count) {
+            constexpr int K = decltype(count)::value;
+#pragma unroll
+            for (int i = 0; i < K; ++i) issue(i, buf[i]);
+#pragma unroll
+            for (int i = 0; i < K; ++i) score(i, buf[i]);
+          };
+          if (n == 1) all(std::integral_constant<int, 1>{});
+          else all(std::integral_constant<int, NB>{});
+        } else {
+#pragma unroll
+          for (int i = 0; i < NB; ++i) issue(i, buf[i]);
+          int u = 0;
+          while (u + 2 * NB <= n) {
+#pragma unroll
+            for (int i = 0; i < NB; ++i) {
+              score(u + i, buf[i]);
+              issue(u + NB + i, buf[i]);
+            }
+            u += NB;
+          }
+          const int r = n - u - NB;  // units after the buffered ones: 0 .. NB-1
+#pragma unroll
+          for (int i = 0; i < NB; ++i) {
+            score(u + i, buf[i]);
+            if (i < r) issue(u + NB + i, buf[i]);
+          }
+#pragma unroll
+          for (int i = 0; i < NB; ++i)
+            if (i < r) score(u + NB + i, buf[i]);
+        }
+      } else {
+        for (int u = 0; u < n; ++u) {
+          const int vw = ((okm >> u) & 1) ? valid_of(u) : 0;
+          quarter_load<false>(quarter_of(u), vw, buf[0]);
+          const float m = quarter_max(buf[0], vw, qr, lane);
+          if (lane < kHeads) sc[wave][u][lane] = m;
+        }
+      }
+    }
+  }
+  if constexpr (!SPREAD) {
+    for (int j = j0 + wave; j < j1; j += kWaves) {
+      const int next = j + kWaves < j1 ? btrow[j + kWaves] : 0;
+      const float m = score_page<ENGINE>(a, page, j, L, lane, &qr);
+      if (lane < kHeads) sc[0][j - j0][lane] = m;
+      page = next;
+    }
   }
   __syncthreads();
 
@@ -990,7 +1143,9 @@ __global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
   uint64_t key = 0;
   if (lane < n) {
     const int jj = j0 + lane;
-    key = make_key(sc[lane][h], jj, jj < a.n_init || jj >= nb - a.n_local);
+    float v = sc[0][lane][h];
+    if constexpr (SPREAD) v = fmaxf(fmaxf(v, sc[1 % kWaves][lane][h]), fmaxf(sc[2 % kWaves][lane][h], sc[3 % kWaves][lane][h]));
+    key = make_key(v, jj, jj < a.n_init || jj >= nb - a.n_local);
   }
   key = sort_desc_first(key, lane, n);
   if (MODE == kFused && ns == 1) {
@@ -1243,16 +1398,6 @@ __device__ __forceinline__ void chunk_mfma(const uint4* region, int ok_g, const 
 #pragma unroll
     for (int h = 0; h < kHeads; ++h) m[h] = fmaxf(m[h], ok ? acc[tg][h] : -__builtin_inff());
   }
-}
-
-// Entry j of a block-table row, read with a scalar load (wave-uniform j). The table is
-// only read during a call, and the scalar cache starts each dispatch invalidated. A vector
-// load here would count in the wave's vector memory counter, which completes in order: the
-// wait for the page number would also wait for every chunk load issued before it, draining
-// the pipeline at each block boundary; the scalar load waits on the LDS/scalar counter only.
-__device__ __forceinline__ int table_entry(const int32_t* row, int j) {
-  typedef const __attribute__((address_space(4))) int32_t* const_row_t;
-  return ((const_row_t)row)[j];
 }
 
 // Inserts key k into each 16-lane row of x (sorted best first, zero padded, k the same in
@@ -1596,6 +1741,8 @@ struct Plan {
 
 int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
+constexpr int64_t kSpreadBlocks = 256;  // single-block splits up to this many blocks per call
+
 int pow2_ceil(int x) {
   int p = 1;
   while (p < x) p <<= 1;
@@ -1663,6 +1810,23 @@ int32_t make_decode_plan(int32_t batch, int32_t W, int32_t topk, int32_t num_spl
   return MSA_OK;
 }
 
+// The single-token decode's plan (msa_indexer_decode and the calls built on it): the decode
+// plan, except that a small table (batch * W <= 512 blocks) with the split count left automatic
+// and the VALU engine splits into single blocks (at most 256 blocks in all) or pairs. The split
+// kernel then reads it in the spread layout, the four waves of a workgroup taking the four
+// quarters of each block with every load of the split in flight at once: four times the
+// workgroups of 4-block splits, on as many more CUs (batch 1 x 64 blocks: 7.8 -> 6.4 us).
+int32_t make_single_plan(int32_t batch, int32_t W, int32_t topk, int32_t num_splits, int32_t engine,
+                         Plan* p) {
+  int32_t rc = make_decode_plan(batch, W, topk, num_splits, p);
+  if (rc != MSA_OK || num_splits != 0 || p->device || engine == MSA_ENGINE_MFMA || W == 0) return rc;
+  const int64_t blocks = (int64_t)batch * W;
+  if (blocks > 2 * kSpreadBlocks) return rc;
+  Plan t;
+  if (plan_from_width(W, topk, blocks <= kSpreadBlocks ? 1 : 2, &t) == MSA_OK) *p = t;
+  return MSA_OK;
+}
+
 // Workspace layout (the caller's buffer of ws_size bytes, 256-byte aligned):
 //   [0, 256)                   header: the device error word, then the word read_error stages
 //   [256 + 4352 b, + 4352)     row b's 17 counter lines (row counter, 16 group counters)
@@ -1689,7 +1853,7 @@ size_t fused_lds_bytes(const Plan& p, int topk) {
 // (For the device plan p.S and p.Lk bound the per-call values: S splits, Lk <= topk.)
 
 // Key bytes per row that a call with these (W, topk, num_splits, Q) may use at any batch size:
-// an explicit split count fixes the width; the automatic one takes a width of 4 .. 64 blocks
+// an explicit split count fixes the width; the automatic one takes a width of 1 .. 64 blocks
 // from the batch, or the device plan (S * topk keys per head). Sizing every call's workspace
 // with this bound (workspace_bytes) is what lets calls of any batch share one buffer: a call of
 // batch B writes at most B times this many key bytes at the buffer's end, which stay clear of
@@ -1704,7 +1868,7 @@ size_t row_key_bytes(int32_t W, int32_t topk, int32_t num_splits, int32_t Q) {
     if (make_plan(1, W, topk, num_splits, &p) == MSA_OK) consider(p);
     return best;
   }
-  for (int c0 = 4; c0 <= kMaxSplitBlocks; c0 *= 2)
+  for (int c0 = 1; c0 <= kMaxSplitBlocks; c0 *= 2)  // 1 and 2: the single-token decode's small tables
     if (plan_from_width(W, topk, c0, &p) == MSA_OK) consider(p);
   if (make_decode_plan(kDeviceMinBlocks, W, topk, 0, &p) == MSA_OK && p.device) consider(p);
   return best;
@@ -1763,10 +1927,12 @@ int32_t launch_split(const SplitArgs& a, int32_t batch, int32_t engine, size_t l
   if (device_grid > 0) grid = dim3(device_grid, 1);
   if (engine == MSA_ENGINE_DEFAULT) engine = MSA_ENGINE_VALU;
   clear_stale_error();
-  if (engine == MSA_ENGINE_VALU)
-    hipLaunchKernelGGL((split_kernel<MSA_ENGINE_VALU, MODE>), grid, block, lds, st, a);
+  if (engine == MSA_ENGINE_VALU && a.spread && MODE != kScores)
+    hipLaunchKernelGGL((split_kernel<MSA_ENGINE_VALU, MODE == kScores ? kSplit : MODE, true>), grid, block, lds, st, a);
+  else if (engine == MSA_ENGINE_VALU)
+    hipLaunchKernelGGL((split_kernel<MSA_ENGINE_VALU, MODE, false>), grid, block, lds, st, a);
   else if (engine == MSA_ENGINE_MFMA)
-    hipLaunchKernelGGL((split_kernel<MSA_ENGINE_MFMA, MODE>), grid, block, lds, st, a);
+    hipLaunchKernelGGL((split_kernel<MSA_ENGINE_MFMA, MODE, false>), grid, block, lds, st, a);
   else
     return MSA_ERR_INVALID_ARG;
   return hipGetLastError() == hipSuccess ? MSA_OK : MSA_ERR_HIP;
@@ -1802,6 +1968,7 @@ SplitArgs make_split_args(const void* q, const void* k, const int32_t* bt, const
   a.n_local = n_local;
   a.batch = batch;
   a.device_plan = p.device ? 1 : 0;
+  a.spread = p.C % kWaves != 0 ? 1 : 0;
   a.lim = split_limits(p.S, topk);
   a.full = full_row_plan(p.device, batch, W, a.lim);
   a.err = w.err;
@@ -2071,6 +2238,7 @@ int32_t decode_impl(const void* q, const void* k_cache, const int32_t* block_tab
   if (batch > 0 && (rc = check_pages(out_pages, out_tokens, block_table, W, num_pages)) != MSA_OK)
     return rc;
   if (batch == 0) return MSA_OK;
+  if ((rc = make_single_plan(batch, W, topk, num_splits, engine, &p)) != MSA_OK) return rc;
   const size_t kb = keys_bytes(batch, 1, p);
   WsView w;
   if (scratch != nullptr) {
@@ -2117,7 +2285,7 @@ const char* msa_status_string(int32_t status) {
 int32_t msa_indexer_num_splits(int32_t batch, int32_t max_blocks_per_seq, int32_t topk,
                                int32_t num_splits) {
   Plan p;
-  const int32_t rc = make_decode_plan(batch, max_blocks_per_seq, topk, num_splits, &p);
+  const int32_t rc = make_single_plan(batch, max_blocks_per_seq, topk, num_splits, MSA_ENGINE_DEFAULT, &p);
   return rc == MSA_OK ? p.S : rc;
 }
 
@@ -2125,7 +2293,7 @@ int32_t msa_indexer_plan(int32_t batch, int32_t max_blocks_per_seq, int32_t topk
                          int32_t num_splits, int32_t* splits, int32_t* blocks_per_split,
                          int32_t* candidates_per_split, int32_t* fused) {
   Plan p;
-  const int32_t rc = make_decode_plan(batch, max_blocks_per_seq, topk, num_splits, &p);
+  const int32_t rc = make_single_plan(batch, max_blocks_per_seq, topk, num_splits, MSA_ENGINE_DEFAULT, &p);
   if (rc != MSA_OK) return rc;
   if (splits) *splits = p.S;
   if (blocks_per_split) *blocks_per_split = p.C;

@@ -50,8 +50,12 @@ def test_split_plan(lib):
     assert ns(32, 1024, 16, 0) == 64
     assert ns(16, 4096, 16, 0) == 64
     assert ns(8, 1024, 16, 0) == 64
-    # small tables (batch * W < 8192 blocks) keep the host plan
-    assert ns(1, 64, 16, 0) == 16
+    # small tables (batch * W < 8192 blocks) keep the host plan; the smallest (batch * W <= 512
+    # blocks) split into single blocks (up to 256 blocks) or pairs, for the spread layout
+    assert ns(1, 64, 16, 0) == 64
+    assert ns(4, 64, 16, 0) == 64
+    assert ns(2, 200, 16, 0) == 100
+    assert ns(3, 200, 16, 0) == 50
     assert ns(16, 68, 16, 0) == 17
     assert ns(7, 1024, 16, 0) == 128
     # Wider tables or larger topk: the host plan, about batch*W/1024 blocks per split.

@@ -282,18 +282,22 @@ def test_pruned_merge_host_plans(msa):
 
 @pytest.mark.parametrize("topk,n_init,n_local", [(16, 1, 2), (2, 1, 1), (3, 0, 0)])
 def test_single_split_rows(msa, topk, n_init, n_local):
-    # Every row fits one split (at most 4 blocks under the host plan's 4-block splits), so
-    # each workgroup writes its row's selection and page table directly, without publishing
-    # its lists: the decode, page-table and FP8 calls against the oracle, with empty, partial
-    # and full rows, and fewer blocks than topk as well as more.
+    # Every row fits one split (one split of the table's 4 blocks asked for; the FP8 call's
+    # host plan takes 4-block splits by itself), so each workgroup writes its row's selection
+    # and page table directly, without publishing its lists: the decode, page-table and FP8
+    # calls against the oracle, with empty, partial and full rows, and fewer blocks than topk
+    # as well as more. The automatic single-token plan of this small table (single-block
+    # splits, spread layout) is checked too.
     from test_gpu_fp8 import run_fp8
     lens = [0, 1, 127, 128, 129, 300, 511, 512, 64, 256 + 3, 1, 0]
     inp = synth.paged_case(114, lens, 4, topk=topk, n_init=n_init, n_local=n_local)
-    assert msa.plan(len(lens), 4, topk)["blocks_per_split"] == 4
+    assert msa.plan(len(lens), 4, topk, 1)["blocks_per_split"] == 4
+    assert msa.plan(len(lens), 4, topk)["blocks_per_split"] == 1
     ref = oracle.block_scores(inp.q, inp.k_cache, inp.block_table, inp.seq_lens)
-    ids, sc = run_case(msa, inp, ref, engine_list=[1], splits=(0,))
+    ids, sc = run_case(msa, inp, ref, engine_list=[1], splits=(0, 1))
     q, k, bt, dl = to_device(inp)
-    ids_p, sc_p, pages, tokens = msa.msa_indexer_decode_pages(q, k, bt, dl, topk, n_init, n_local)
+    ids_p, sc_p, pages, tokens = msa.msa_indexer_decode_pages(q, k, bt, dl, topk, n_init, n_local,
+                                                              num_splits=1)
     assert np.array_equal(ids_p.cpu().numpy(), ids) and np.array_equal(sc_p.cpu().numpy(), sc)
     want_p, want_t = oracle.expand_pages(ids, inp.block_table, inp.seq_lens)
     assert np.array_equal(pages.cpu().numpy(), want_p) and np.array_equal(tokens.cpu().numpy(), want_t)
