@@ -134,7 +134,8 @@ int32_t msa_indexer_plan(int32_t batch, int32_t max_blocks_per_seq, int32_t topk
  *   [256 + 4352 b, 256 + 4352 (b+1))   the counter lines of row b (uint32 [17][64]: line 0
  *                                      counts the row's finished splits, lines 1..16 count
  *                                      groups of 16 splits for rows of more than 128 splits);
- *   the last K bytes (256-aligned)     the per-split candidate keys, uint64 [batch][S][4][Lk],
+ *   the last K bytes (256-aligned)     the per-split candidate keys, uint64 [batch][4][S * Lk]
+ *                                      (each head's split lists one after another),
  *                                      K = this size minus 256 minus 4352 * batch.
  * The whole buffer must be zero before its first use (e.g. hipMemset once after allocation).
  * Every call leaves the counters at zero when it ends, and a row's counter lines sit at an
@@ -296,7 +297,7 @@ int32_t msa_indexer_expand_pages_multi(const int32_t *ids, const int32_t *block_
 /*
  * Workspace bytes of msa_indexer_decode_multi and msa_indexer_decode_fp8 (0 on invalid
  * arguments): the layout of msa_indexer_workspace_bytes with keys uint64
- * [batch][S][qlen*4][Lk]. Zeroed once before its first use, like the single-token workspace,
+ * [batch][qlen*4][S * Lk]. Zeroed once before its first use, like the single-token workspace,
  * and shareable with it under the same rule.
  */
 size_t msa_indexer_workspace_bytes_multi(int32_t batch, int32_t max_blocks_per_seq, int32_t qlen,

@@ -750,7 +750,7 @@ struct SplitArgs {
   int32_t spread;       // VALU engine, not block-score mode: each wave scores a quarter of every block
   SplitLimits lim;      // device plan: per-row block limits of each split width
   FullRowPlan full;     // device plan: the plan when every row is W blocks long
-  uint64_t* keys;       // [batch][S][4][Lk]
+  uint64_t* keys;       // [batch][4][S * LkMax] (list_offset)
   uint32_t* err;        // device error word (may be null)
   uint32_t* counters;   // [batch][kCounterStride]: row and group counters (count_in); zero between calls
   int32_t* out_ids;     // [batch][4][topk] (fused mode)
@@ -819,9 +819,12 @@ __device__ __forceinline__ int wave_max_nonneg(int x) {
 
 // Where the list of split s, task t (position-head p * 4 + h) of row b starts in the
 // workspace keys: rows lie S * QH * LkMax keys apart (LkMax = the plan's Lk; topk under
-// the device plan), and a row's lists are [s][t][Lk] with this call's Lk = min(topk, C).
+// the device plan), a row's tasks S * LkMax keys apart, and a task's lists follow one another
+// (this call's Lk = min(topk, C) keys each; at most S * LkMax keys in all). The merging wave
+// of a task then reads its lists from consecutive lines: the heads of 256 lists of 4 lie in
+// 64 lines of 128 bytes, not 256 (the agent-scope loads go to the memory side line by line).
 __device__ __forceinline__ size_t list_offset(int b, int S, int QH, int LkMax, int s, int t, int Lk) {
-  return (size_t)b * S * QH * LkMax + ((size_t)s * QH + t) * Lk;
+  return ((size_t)b * QH + t) * S * LkMax + (size_t)s * Lk;
 }
 
 // Thread 0 of a workgroup that has published its lists (split s of the row's ns): whether it
@@ -1178,18 +1181,24 @@ __global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
   if (!s_last) return;
   if (MODE != kFused) return;
 
-  // Row b's lists are one contiguous range [s][h][i] of the workspace. Wave h merges
-  // head h's lists straight from it with the network; otherwise the lists are staged in
-  // LDS, each workgroup's four lists with one pad key after them so that lanes reading
-  // list s (stride 4 Lk + 1 keys) fall on different banks.
+  // Head h's lists of row b are one contiguous range [s][i] of the workspace, the heads
+  // S * LkMax keys apart. Wave h merges head h's lists straight from it with the network;
+  // otherwise the lists are staged in LDS as [s][h][i], each workgroup's four lists with one
+  // pad key after them so that lanes reading list s (stride 4 Lk + 1 keys) fall on different
+  // banks.
   const uint64_t* row_keys = a.keys + list_offset(b, a.S, kHeads, a.Lk, 0, 0, Lk);
+  const size_t head_stride = (size_t)a.S * a.Lk;
   const int m = min(a.topk, nb);
   uint64_t mine;
   if (network_fits(ns, Lk, a.topk)) {
-    mine = merge_top16(row_keys + h * Lk, (size_t)kHeads * Lk, ns, Lk, C, lane);
+    mine = merge_top16(row_keys + h * head_stride, (size_t)Lk, ns, Lk, C, lane);
   } else {
     const int row_len = kHeads * Lk, stride = row_len + 1;
-    stage_keys(row_keys, lk, ns * row_len, threadIdx.x, kThreads, [](int e) { return e; },
+    stage_keys(row_keys, lk, ns * row_len, threadIdx.x, kThreads,
+               [row_len, Lk, head_stride](int e) {
+                 const int sp = e / row_len, r = e % row_len;
+                 return (size_t)(r / Lk) * head_stride + (size_t)sp * Lk + r % Lk;
+               },
                [row_len](int e) { return e + e / row_len; });
     __syncthreads();
     mine = merge_rounds(lk + h * Lk, ns, Lk, stride, m, lane);
@@ -1203,7 +1212,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
 
 // ---------------------------------------------------------------------------------------
 // Stage 2 on its own: one wave per (row, position-head task), grid (Q*4, batch). Keys are
-// [batch][S][Q*4][Lk]; Q = 1 is the single-token layout [batch][S][4][Lk].
+// [batch][Q*4][S * LkMax] (list_offset); Q = 1 is the single-token layout [batch][4][S * LkMax].
 
 struct MergeArgs {
   const int32_t* lens;
@@ -1243,9 +1252,9 @@ __global__ __launch_bounds__(64) void merge_kernel(MergeArgs a) {
   const uint64_t* src = a.keys + list_offset(b, a.S, QH, a.Lk, 0, task, Lk);
   uint64_t mine;
   if (network_fits(ns, Lk, a.topk)) {
-    mine = merge_top16(src, (size_t)QH * Lk, ns, Lk, C, lane);
+    mine = merge_top16(src, (size_t)Lk, ns, Lk, C, lane);
   } else {
-    stage_keys(src, lk, ns * Lk, lane, 64, [Lk, QH](int e) { return (e / Lk) * QH * Lk + e % Lk; },
+    stage_keys(src, lk, ns * Lk, lane, 64, [](int e) { return e; },
                [Lk, stride](int e) { return (e / Lk) * stride + e % Lk; });
     __syncthreads();
     mine = merge_rounds(lk, ns, Lk, stride, m, lane);
@@ -1423,7 +1432,7 @@ struct VerifyArgs {
   int32_t device_plan;  // split modes: C and each workgroup's (row, split) chosen on the device
   SplitLimits lim;
   FullRowPlan full;     // device plan: the plan when every row is W blocks long
-  uint64_t* keys;       // [batch][S][Q*4][Lk]
+  uint64_t* keys;       // [batch][Q*4][S * LkMax] (list_offset)
   uint32_t* err;        // device error word (may be null)
   float* scores;        // [batch][Q][4][W] (block-score mode)
   uint32_t* counters;   // fused mode: [batch][kCounterStride], zero between calls
@@ -1718,7 +1727,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   if (threadIdx.x == 0) s_last = count_in(a.counters + (size_t)b * kCounterStride, s, ns);
   __syncthreads();
   if (!s_last) return;
-  const uint64_t mine = merge_top16(a.keys + list_offset(b, a.S, kHeads, a.Lk, 0, h, Lk), (size_t)kHeads * Lk,
+  const uint64_t mine = merge_top16(a.keys + list_offset(b, a.S, kHeads, a.Lk, 0, h, Lk), (size_t)Lk,
                                     ns, Lk, C, lane);
   const size_t o = ((size_t)b * kHeads + h) * a.topk;
   write_selection(mine, min(a.topk, nb), a.topk, lane, a.out_ids + o, a.out_scores + o);
@@ -1830,7 +1839,7 @@ int32_t make_single_plan(int32_t batch, int32_t W, int32_t topk, int32_t num_spl
 // Workspace layout (the caller's buffer of ws_size bytes, 256-byte aligned):
 //   [0, 256)                   header: the device error word, then the word read_error stages
 //   [256 + 4352 b, + 4352)     row b's 17 counter lines (row counter, 16 group counters)
-//   the last keys_bytes        keys uint64 [batch][S][Q*4][Lk], starting 256-byte aligned
+//   the last keys_bytes        keys uint64 [batch][Q*4][S * Lk] (list_offset), 256-byte aligned
 // A row's counter lines sit at an offset that depends on nothing but the row, and a call's
 // keys fill the end of the buffer. So calls that share one buffer and pass its full size
 // never write keys over a counter line another of them counts on, whatever their batch sizes
