@@ -628,7 +628,30 @@ __device__ __forceinline__ uint64_t merge_top16(const uint64_t* __restrict__ lis
                  ? __hip_atomic_load(lists + sp * list_stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                  : 0;
     }
-    const uint64_t head = network_top16(r, RH, 0, lane);
+    uint64_t head;
+    if (RH >= 2) {
+      // Lanes pruned first, by the same argument with a lane's heads as its list: the 16 best
+      // heads lie among the heads of the 16 lanes with the best maxima. Those lanes' heads
+      // (at most 64) are gathered into one register, head t of the i-th best lane into lane
+      // 4 i + t, and ranked there: two one-register networks instead of one over RH.
+      uint64_t mx = r[0];
+#pragma unroll
+      for (int t = 1; t < 4; ++t) mx = t < RH ? umax64(mx, r[t]) : mx;
+      uint64_t q[16] = {mx};
+      const uint64_t best = network_top16(q, 1, 0, lane);         // lane i < 16: i-th best maximum
+      const int holder = best != 0 ? (key_id(best) / C) & 63 : -1;  // the lane that holds it
+      const int from = __shfl(holder, lane >> 2);
+      uint64_t c = 0;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const uint64_t v = bpermute_u64(r[t], from < 0 ? lane : from);
+        c = (from >= 0 && (lane & 3) == t) ? v : c;
+      }
+      uint64_t g[16] = {c};
+      head = network_top16(g, 1, 0, lane);
+    } else {
+      head = network_top16(r, RH, 0, lane);
+    }
     const int src = head != 0 ? key_id(head) / C : -1;  // lane i < 16: the list of the i-th best head
     const int R2 = max(1, (16 << lg) / 64);             // registers of the 16 lists' keys
 #pragma unroll
