@@ -52,6 +52,7 @@ constexpr int kMaxSplitBlocks = 64;             // C <= 64: one split candidate 
 #define MSA_CHUNK_BUFFERS 2
 #endif
 constexpr int kChunkBuffers = MSA_CHUNK_BUFFERS;
+constexpr int kSpreadMaxUnits = 5;              // spread layout: splits of up to 5 blocks read at once
 constexpr int kMaxSplits = 256;                 // merge: at most 4 lists per lane
 constexpr int kMaxMergeKeys = 4096;             // S * Lk keys of one (row, head) in LDS
 constexpr int kMaxFusedKeys = 1024;             // fused merge: S * topk keys per head, 4 heads in LDS
@@ -771,6 +772,7 @@ struct SplitArgs {
   int32_t batch;
   int32_t device_plan;  // fused mode: C and each workgroup's (row, split) chosen on the device
   int32_t spread;       // VALU engine, not block-score mode: each wave scores a quarter of every block
+  int32_t even;         // host plan: split s covers blocks [s W / S, (s + 1) W / S) (C: the widest)
   SplitLimits lim;      // device plan: per-row block limits of each split width
   FullRowPlan full;     // device plan: the plan when every row is W blocks long
   uint64_t* keys;       // [batch][4][S * LkMax] (list_offset)
@@ -1034,10 +1036,12 @@ __global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
   // whatever the length); each page number after it is read while the page before it is
   // being scored.
   const int32_t* btrow = a.bt + (size_t)b * a.bt_stride;
-  const int j_first = s * C + wave;
+  // The split's first block (with even splits, s W / S: widths C - 1 and C).
+  const int j_start = MODE != kScores && a.even ? (int)((int64_t)s * a.W / a.S) : s * C;
+  const int j_first = j_start + wave;
   int page = !spread && j_first < a.W ? btrow[j_first] : 0;
-  // Spread layout: lane u < C holds the page number of the split's block s * C + u.
-  const int pg_spread = spread && lane < C && s * C + lane < a.W ? btrow[s * C + lane] : -1;
+  // Spread layout: lane u < C holds the page number of the split's block j_start + u.
+  const int pg_spread = spread && lane < C && j_start + lane < a.W ? btrow[j_start + lane] : -1;
   typename std::conditional<ENGINE == MSA_ENGINE_MFMA, QMfma, QValu>::type qr;
   if constexpr (ENGINE == MSA_ENGINE_MFMA) load_q_mfma(a.q, b, lane, qr);
   else load_q_valu(a.q, b, lane, qr);
@@ -1061,9 +1065,10 @@ __global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
     return;
   }
 
-  const int ns = (nb + C - 1) / C;  // workgroups that take part in this row
-  const int j0 = s * C;
-  const int j1 = min(j0 + C, nb);
+  // Workgroups that take part in this row (with even splits, those with s W / S < nb).
+  const int ns = a.even ? (int)(((int64_t)nb * a.S + a.W - 1) / a.W) : (nb + C - 1) / C;
+  const int j0 = j_start;
+  const int j1 = min(a.even ? (int)((int64_t)(s + 1) * a.W / a.S) : j0 + C, nb);
   if (s >= ns) {
     // An empty row has no workgroup to merge it: its first workgroup writes the padding.
     if (MODE == kFused && nb == 0 && s == 0) {
@@ -1120,6 +1125,28 @@ __global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
           };
           if (n == 1) all(std::integral_constant<int, 1>{});
           else all(std::integral_constant<int, NB>{});
+        } else if (n >= 4 && n <= kSpreadMaxUnits) {
+          // Four or five units (even splits): the first four in flight at once, the fifth
+          // issued as soon as the first is scored; n a compile-time constant in each case, in
+          // straight-line code (a rotating loop of four buffers copies registers at its back
+          // edge and needs twice the registers; a third case for three units spilled; all five
+          // in flight measured slower).
+          auto upto5 = [&](auto count) {
+            constexpr int K = decltype(count)::value;
+            uint4 kv[4][8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) issue(i, kv[i]);
+            score(0, kv[0]);
+            if constexpr (K == 5) {
+              __builtin_amdgcn_sched_barrier(0);  // the fifth unit's loads after the first's use
+              issue(4, kv[0]);
+            }
+#pragma unroll
+            for (int i = 1; i < 4; ++i) score(i, kv[i]);
+            if constexpr (K == 5) score(4, kv[0]);
+          };
+          if (n == 4) upto5(std::integral_constant<int, 4>{});
+          else upto5(std::integral_constant<int, 5>{});
         } else {
 #pragma unroll
           for (int i = 0; i < NB; ++i) issue(i, buf[i]);
@@ -1769,11 +1796,13 @@ struct Plan {
   bool fused;
   bool device = false;  // C and the (row, split) of each workgroup are chosen on the device
   int grid = 0;         // device plan: workgroups launched (1-D)
+  bool even = false;    // split s covers blocks [s W / S, (s + 1) W / S); C = ceil(W / S), the widest
 };
 
 int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
 constexpr int64_t kSpreadBlocks = 256;  // single-block splits up to this many blocks per call
+constexpr int kEvenWorkgroups = 256;      // even splits: one workgroup per CU
 
 int pow2_ceil(int x) {
   int p = 1;
@@ -1848,14 +1877,31 @@ int32_t make_decode_plan(int32_t batch, int32_t W, int32_t topk, int32_t num_spl
 // kernel then reads it in the spread layout, the four waves of a workgroup taking the four
 // quarters of each block with every load of the split in flight at once: four times the
 // workgroups of 4-block splits, on as many more CUs (batch 1 x 64 blocks: 7.8 -> 6.4 us).
+size_t row_key_bytes(int32_t W, int32_t topk, int32_t num_splits, int32_t Q);
+
 int32_t make_single_plan(int32_t batch, int32_t W, int32_t topk, int32_t num_splits, int32_t engine,
                          Plan* p) {
   int32_t rc = make_decode_plan(batch, W, topk, num_splits, p);
   if (rc != MSA_OK || num_splits != 0 || p->device || engine == MSA_ENGINE_MFMA || W == 0) return rc;
   const int64_t blocks = (int64_t)batch * W;
-  if (blocks > 2 * kSpreadBlocks) return rc;
-  Plan t;
-  if (plan_from_width(W, topk, blocks <= kSpreadBlocks ? 1 : 2, &t) == MSA_OK) *p = t;
+  if (blocks <= 2 * kSpreadBlocks) {
+    Plan t;
+    if (plan_from_width(W, topk, blocks <= kSpreadBlocks ? 1 : 2, &t) == MSA_OK) *p = t;
+    return MSA_OK;
+  }
+  // Even splits: where the plan's workgroups just exceed the CU count (some CUs would hold
+  // two, and those end the call), rows of 4 to 64 (batch * S > 256) take S = 256 / batch
+  // splits of C - 1 or C <= 5 blocks each, read in the spread layout, so every CU holds one
+  // workgroup. Kept out of the pruned merge (S <= 64) and within the workspace's key bound.
+  if (batch >= 4 && batch <= 64 && (int64_t)batch * p->S > kEvenWorkgroups) {
+    const int S = kEvenWorkgroups / batch, C = (W + S - 1) / S, Lk = std::min(topk, C);
+    if (S < p->S && C <= kSpreadMaxUnits && network_fits(S, Lk, topk) &&
+        (size_t)S * Lk * kHeads * sizeof(uint64_t) <= row_key_bytes(W, topk, 0, 1)) {
+      Plan e{S, C, Lk, true};
+      e.even = true;
+      *p = e;
+    }
+  }
   return MSA_OK;
 }
 
@@ -2000,7 +2046,8 @@ SplitArgs make_split_args(const void* q, const void* k, const int32_t* bt, const
   a.n_local = n_local;
   a.batch = batch;
   a.device_plan = p.device ? 1 : 0;
-  a.spread = p.C % kWaves != 0 ? 1 : 0;
+  a.spread = p.even || p.C % kWaves != 0 ? 1 : 0;
+  a.even = p.even ? 1 : 0;
   a.lim = split_limits(p.S, topk);
   a.full = full_row_plan(p.device, batch, W, a.lim);
   a.err = w.err;

@@ -56,7 +56,12 @@ def test_split_plan(lib):
     assert ns(4, 64, 16, 0) == 64
     assert ns(2, 200, 16, 0) == 100
     assert ns(3, 200, 16, 0) == 50
-    assert ns(16, 68, 16, 0) == 17
+    # where 4-block splits would put a few CUs at two workgroups, rows of 4..64 take 256 / batch
+    # even splits of at most 5 blocks (widths C - 1 and C), one workgroup per CU
+    assert ns(16, 68, 16, 0) == 16
+    assert ns(4, 300, 16, 0) == 64
+    assert ns(32, 68, 16, 0) == 17      # 8 even splits would be 9 blocks wide: kept
+    assert ns(16, 64, 16, 0) == 16      # 256 workgroups already
     assert ns(7, 1024, 16, 0) == 128
     # Wider tables or larger topk: the host plan, about batch*W/1024 blocks per split.
     assert ns(32, 1024, 17, 0) == 32

@@ -305,6 +305,27 @@ def test_single_split_rows(msa, topk, n_init, n_local):
             1e-3 * 4.0 * 0.5)
 
 
+@pytest.mark.parametrize("B,W,seed", [(8, 150, 171), (16, 68, 172), (4, 300, 173), (64, 17, 174)])
+def test_even_splits(msa, B, W, seed):
+    # Tables whose 4-block splits would just exceed one workgroup per CU take 256 / B even
+    # splits of 4 or 5 blocks (the spread layout, the first four blocks in flight and the fifth
+    # after): full rows, empty and one-token rows, partial last blocks and rows that end inside
+    # any split, against the oracle, and the same ids as an explicit 4-block plan.
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(0, 128 * W + 1, size=B).astype(np.int32)
+    lens[0], lens[1 % B] = 128 * W, 0
+    if B > 2:
+        lens[2] = 1
+    inp = synth.paged_case(seed, lens.tolist(), W)
+    p = msa.plan(B, W, 16)
+    assert p["splits"] == 256 // B and p["blocks_per_split"] == -(-W // (256 // B))
+    ref = oracle.block_scores(inp.q, inp.k_cache, inp.block_table, inp.seq_lens)
+    ids, _ = run_case(msa, inp, ref, engine_list=[1], splits=(0,))
+    q, k, bt, dl = to_device(inp)
+    ids4, _ = msa.msa_indexer_decode(q, k, bt, dl, num_splits=-(-W // 4))
+    assert np.array_equal(ids, ids4.cpu().numpy())
+
+
 def test_workspace_reuse_and_counter_reset(msa):
     # One workspace across calls with changing lengths and split counts: the per-row
     # counters must come back to zero after every fused call.
