@@ -81,3 +81,36 @@ def test_one_full_row_among_empty_ones(W, B):
         nb[B // 2] = W
         check(nb, W, topk)
         check(np.full(B, W, dtype=np.int64), W, topk)
+
+
+def workgroup_map(nb, C):
+    """Workgroup g -> (row, split) for batch <= 64: row b takes max(1, ceil(nb_b / C))
+    consecutive ids, starting with the first row of the most splits and wrapping around."""
+    cnt = np.maximum(1, -(-nb // C))
+    incl = np.cumsum(cnt)
+    total = int(incl[-1])
+    r0 = int(np.argmax(cnt))  # the first row of the most splits
+    shift = int(incl[r0] - cnt[r0])
+    out = {}
+    for g in range(total):
+        gr = (g + shift) % total
+        b = int(np.searchsorted(incl, gr, side="right"))
+        out[g] = (b, gr - int(incl[b] - cnt[b]))
+    return out, cnt
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_the_longest_row_takes_the_first_workgroups(seed):
+    # Every (row, split) gets exactly one workgroup, and the row of the most splits gets
+    # workgroups 0, 1, ..: dispatched first, they never share a CU with an earlier workgroup.
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 65))
+    W = int(rng.choice([64, 256, 1024, 4096]))
+    nb = rng.integers(0, 9, size=B).astype(np.int64)
+    nb[int(rng.integers(B))] = int(rng.integers(W // 2, W + 1))
+    C = int(rng.choice([4, 8, 16]))
+    m, cnt = workgroup_map(nb, C)
+    pairs = sorted(m.values())
+    assert pairs == sorted((b, s) for b in range(B) for s in range(int(cnt[b])))
+    r0 = int(np.argmax(cnt))
+    assert [m[g] for g in range(int(cnt[r0]))] == [(r0, s) for s in range(int(cnt[r0]))]
