@@ -606,21 +606,26 @@ __device__ __forceinline__ uint64_t network_top16(uint64_t (&r)[16], int R, int 
 // of them share a register: lane l of register t holds element l % Lk2 of list
 // t * 64 / Lk2 + l / Lk2.
 // Many short lists (more than 8 registers of lists of at most 8 keys, e.g. 256 splits of 4
-// blocks) are pruned first: the 16th largest list head is at most the 16th largest key (the
+// blocks; more than 3 registers of lists of 2 to 8 keys; 2 or more of one-key lists) are
+// pruned first: the 16th largest list head is at most the 16th largest key (the
 // 16 best heads are 16 keys), and a list's keys are at most its head, so every key of the
 // top 16 lies in one of the 16 lists with the best heads. The heads (at most 256, 4
 // registers) are ranked first, and only those 16 lists (16 Lk2 keys, 1 or 2 registers) are
 // read and merged: a second round of loads, but about a third of the network's steps
 // (sorting 16 registers of short runs is its largest part). A head names its list: its
-// block id divided by C.
+// block id divided by C (so lists of even splits, whose widths differ, are never pruned:
+// prune = false).
 __device__ __forceinline__ uint64_t merge_top16(const uint64_t* __restrict__ lists, size_t list_stride,
-                                                int ns, int Lk, int C, int lane) {
+                                                int ns, int Lk, int C, int lane, bool prune = true) {
   const int lg = Lk <= 1 ? 0 : Lk <= 2 ? 1 : Lk <= 4 ? 2 : Lk <= 8 ? 3 : 4;
   const int per_reg = 64 >> lg;
   const int R = (ns + per_reg - 1) / per_reg;  // registers that hold a list
   const int e = lane & ((1 << lg) - 1);
   uint64_t r[16];
-  if (lg < 4 && R > 8) {
+  // Pruned: more than 8 registers of lists, or more than 3 of lists of 2 to 8 keys (measured
+  // ahead there since the lists of one head lie together), or 2 or more registers of one-key
+  // lists, whose heads are the keys (the ranking of the heads is then the answer).
+  if (prune && lg < 4 && (R > 8 || (lg >= 1 && R > 3) || (lg == 0 && R >= 2))) {
     const int RH = (ns + 63) / 64;  // registers of list heads, one head per lane
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
@@ -653,6 +658,7 @@ __device__ __forceinline__ uint64_t merge_top16(const uint64_t* __restrict__ lis
     } else {
       head = network_top16(r, RH, 0, lane);
     }
+    if (lg == 0) return head;  // one key per list: the best heads are the best keys
     const int src = head != 0 ? key_id(head) / C : -1;  // lane i < 16: the list of the i-th best head
     const int R2 = max(1, (16 << lg) / 64);             // registers of the 16 lists' keys
 #pragma unroll
@@ -1241,7 +1247,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
   const int m = min(a.topk, nb);
   uint64_t mine;
   if (network_fits(ns, Lk, a.topk)) {
-    mine = merge_top16(row_keys + h * head_stride, (size_t)Lk, ns, Lk, C, lane);
+    mine = merge_top16(row_keys + h * head_stride, (size_t)Lk, ns, Lk, C, lane, !a.even);
   } else {
     const int row_len = kHeads * Lk, stride = row_len + 1;
     stage_keys(row_keys, lk, ns * row_len, threadIdx.x, kThreads,

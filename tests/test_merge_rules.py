@@ -60,3 +60,4 @@ def test_best_heads_lie_in_the_lanes_with_the_best_maxima(ns, lk):
         best_lanes = sorted(lanes, key=lambda l: max(lanes[l]), reverse=True)[:16]
         gathered = [h for l in best_lanes for h in lanes[l]]
         assert top16(gathered) == top16(heads)
+
