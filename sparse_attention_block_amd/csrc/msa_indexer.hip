@@ -615,17 +615,30 @@ __device__ __forceinline__ uint64_t network_top16(uint64_t (&r)[16], int R, int 
 // (sorting 16 registers of short runs is its largest part). A head names its list: its
 // block id divided by C (so lists of even splits, whose widths differ, are never pruned:
 // prune = false).
-__device__ __forceinline__ uint64_t merge_top16(const uint64_t* __restrict__ lists, size_t list_stride,
-                                                int ns, int Lk, int C, int lane, bool prune = true) {
-  const int lg = Lk <= 1 ? 0 : Lk <= 2 ? 1 : Lk <= 4 ? 2 : Lk <= 8 ? 3 : 4;
-  const int per_reg = 64 >> lg;
-  const int R = (ns + per_reg - 1) / per_reg;  // registers that hold a list
-  const int e = lane & ((1 << lg) - 1);
-  uint64_t r[16];
+// merge_top16 in two phases, for a caller that can issue the first round of loads before it
+// needs their values: merge_issue reads every key (or, pruned, every list head) into r,
+// merge_finish merges them.
+struct MergeShape {
+  int lg;       // log2 Lk2
+  int R;        // registers that hold a list
+  bool pruned;
+};
+
+__device__ __forceinline__ MergeShape merge_shape(int ns, int Lk, bool prune) {
+  MergeShape m;
+  m.lg = Lk <= 1 ? 0 : Lk <= 2 ? 1 : Lk <= 4 ? 2 : Lk <= 8 ? 3 : 4;
+  const int per_reg = 64 >> m.lg;
+  m.R = (ns + per_reg - 1) / per_reg;
   // Pruned: more than 8 registers of lists, or more than 3 of lists of 2 to 8 keys (measured
   // ahead there since the lists of one head lie together), or 2 or more registers of one-key
   // lists, whose heads are the keys (the ranking of the heads is then the answer).
-  if (prune && lg < 4 && (R > 8 || (lg >= 1 && R > 3) || (lg == 0 && R >= 2))) {
+  m.pruned = prune && m.lg < 4 && (m.R > 8 || (m.lg >= 1 && m.R > 3) || (m.lg == 0 && m.R >= 2));
+  return m;
+}
+
+__device__ __forceinline__ void merge_issue(const uint64_t* __restrict__ lists, size_t list_stride, int ns,
+                                            int Lk, const MergeShape& m, int lane, uint64_t (&r)[16]) {
+  if (m.pruned) {
     const int RH = (ns + 63) / 64;  // registers of list heads, one head per lane
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
@@ -634,52 +647,68 @@ __device__ __forceinline__ uint64_t merge_top16(const uint64_t* __restrict__ lis
                  ? __hip_atomic_load(lists + sp * list_stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                  : 0;
     }
-    uint64_t head;
-    if (RH >= 2) {
-      // Lanes pruned first, by the same argument with a lane's heads as its list: the 16 best
-      // heads lie among the heads of the 16 lanes with the best maxima. Those lanes' heads
-      // (at most 64) are gathered into one register, head t of the i-th best lane into lane
-      // 4 i + t, and ranked there: two one-register networks instead of one over RH.
-      uint64_t mx = r[0];
-#pragma unroll
-      for (int t = 1; t < 4; ++t) mx = t < RH ? umax64(mx, r[t]) : mx;
-      uint64_t q[16] = {mx};
-      const uint64_t best = network_top16(q, 1, 0, lane);         // lane i < 16: i-th best maximum
-      const int holder = best != 0 ? (key_id(best) / C) & 63 : -1;  // the lane that holds it
-      const int from = __shfl(holder, lane >> 2);
-      uint64_t c = 0;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const uint64_t v = bpermute_u64(r[t], from < 0 ? lane : from);
-        c = (from >= 0 && (lane & 3) == t) ? v : c;
-      }
-      uint64_t g[16] = {c};
-      head = network_top16(g, 1, 0, lane);
-    } else {
-      head = network_top16(r, RH, 0, lane);
-    }
-    if (lg == 0) return head;  // one key per list: the best heads are the best keys
-    const int src = head != 0 ? key_id(head) / C : -1;  // lane i < 16: the list of the i-th best head
-    const int R2 = max(1, (16 << lg) / 64);             // registers of the 16 lists' keys
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const int i = (t * 64 + lane) >> lg;  // rank of the list this slot holds
-      const int sp = t < R2 ? __shfl(src, i & 15) : -1;
-      r[t] = (t < R2 && i < 16 && e < Lk && sp >= 0)
-                 ? __hip_atomic_load(lists + sp * list_stride + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                 : 0;
-    }
-    return network_top16(r, R2, lg, lane);
+    return;
   }
-  const int sub = lane >> lg;
+  const int per_reg = 64 >> m.lg, sub = lane >> m.lg, e = lane & ((1 << m.lg) - 1);
 #pragma unroll
   for (int t = 0; t < 16; ++t) {
     const int sp = t * per_reg + sub;
-    r[t] = (t < R && sp < ns && e < Lk)
+    r[t] = (t < m.R && sp < ns && e < Lk)
                ? __hip_atomic_load(lists + sp * list_stride + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                : 0;
   }
-  return network_top16(r, R, lg, lane);
+}
+
+__device__ __forceinline__ uint64_t merge_finish(const uint64_t* __restrict__ lists, size_t list_stride, int ns,
+                                                 int Lk, int C, const MergeShape& m, int lane,
+                                                 uint64_t (&r)[16]) {
+  if (!m.pruned) return network_top16(r, m.R, m.lg, lane);
+  const int lg = m.lg, RH = (ns + 63) / 64;
+  const int e = lane & ((1 << lg) - 1);
+  uint64_t head;
+  if (RH >= 2) {
+    // Lanes pruned first, by the same argument with a lane's heads as its list: the 16 best
+    // heads lie among the heads of the 16 lanes with the best maxima. Those lanes' heads
+    // (at most 64) are gathered into one register, head t of the i-th best lane into lane
+    // 4 i + t, and ranked there: two one-register networks instead of one over RH.
+    uint64_t mx = r[0];
+#pragma unroll
+    for (int t = 1; t < 4; ++t) mx = t < RH ? umax64(mx, r[t]) : mx;
+    uint64_t q[16] = {mx};
+    const uint64_t best = network_top16(q, 1, 0, lane);         // lane i < 16: i-th best maximum
+    const int holder = best != 0 ? (key_id(best) / C) & 63 : -1;  // the lane that holds it
+    const int from = __shfl(holder, lane >> 2);
+    uint64_t c = 0;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint64_t v = bpermute_u64(r[t], from < 0 ? lane : from);
+      c = (from >= 0 && (lane & 3) == t) ? v : c;
+    }
+    uint64_t g[16] = {c};
+    head = network_top16(g, 1, 0, lane);
+  } else {
+    head = network_top16(r, RH, 0, lane);
+  }
+  if (lg == 0) return head;  // one key per list: the best heads are the best keys
+  const int src = head != 0 ? key_id(head) / C : -1;  // lane i < 16: the list of the i-th best head
+  const int R2 = max(1, (16 << lg) / 64);             // registers of the 16 lists' keys
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    const int i = (t * 64 + lane) >> lg;  // rank of the list this slot holds
+    const int sp = t < R2 ? __shfl(src, i & 15) : -1;
+    r[t] = (t < R2 && i < 16 && e < Lk && sp >= 0)
+               ? __hip_atomic_load(lists + sp * list_stride + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+               : 0;
+  }
+  return network_top16(r, R2, lg, lane);
+}
+
+__device__ __forceinline__ uint64_t merge_top16(const uint64_t* __restrict__ lists, size_t list_stride,
+                                                int ns, int Lk, int C, int lane, bool prune = true) {
+  const MergeShape m = merge_shape(ns, Lk, prune);
+  uint64_t r[16];
+  merge_issue(lists, list_stride, ns, Lk, m, lane, r);
+  return merge_finish(lists, list_stride, ns, Lk, C, m, lane, r);
 }
 
 __device__ __forceinline__ void write_selection(uint64_t mine, int m, int topk, int lane,
@@ -1296,18 +1325,36 @@ __global__ __launch_bounds__(64) void merge_kernel(MergeArgs a) {
   extern __shared__ uint64_t lk[];  // merge_rounds: [ns][Lk + 1] lists
   const int task = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
   const int p = task >> 2;
+  const int QH = a.Q * kHeads;
+  // Where the lists lie depends on the row's length and, under the device plan, on every row's
+  // (one memory round trip). The lists are complete (the split launch has ended), so the first
+  // round of loads is issued at once for a full row under the full-row plan the host computed
+  // (the decode case of uniform batches), alongside the lengths, and kept if the row takes that
+  // plan; otherwise the lists are read once the plan is known. The lengths are read first, so
+  // that the waits for them do not wait for the list loads.
   const int L = row_tokens(a.lens, b, a.W);
+  int raw0 = a.lens[min(lane, a.batch - 1)];  // row `lane`'s length, unclamped (batch >= 1)
+  const int Cg = a.device_plan ? a.full.C : a.C;
+  const int Lkg = a.device_plan ? min(a.topk, Cg) : a.Lk;
+  const int nsg = Cg > 0 ? (a.W + Cg - 1) / Cg : 0;
+  const bool guess = Cg > 0 && network_fits(nsg, Lkg, a.topk);
+  MergeShape shape = merge_shape(nsg, Lkg, true);
+  uint64_t r[16];
+  if (guess) merge_issue(a.keys + list_offset(b, a.S, QH, a.Lk, 0, task, Lkg), (size_t)Lkg, nsg, Lkg, shape, lane, r);
+  asm volatile("" : "+v"(raw0));  // keeps the length's first use (and its wait) after the list loads
   const int nb = (L + kBlock - 1) / kBlock;
   const int Lp = causal_len(L, a.Q, p);
   const int m = min(a.topk, (Lp + kBlock - 1) / kBlock);
-  const int C = a.device_plan ? device_width(a.lens, a.batch, a.W, lane,
-                                             device_blocks(a.lens, a.batch, a.W, lane), a.lim, a.full)
-                              : a.C;
+  // device_blocks(lens, batch, W, lane) from the length read above
+  const int nb0 = lane < a.batch ? (min(max(raw0, 0), a.W * kBlock) + kBlock - 1) / kBlock : 0;
+  const int C = a.device_plan ? device_width(a.lens, a.batch, a.W, lane, nb0, a.lim, a.full) : a.C;
   const int ns = (nb + C - 1) / C;
-  const int Lk = a.device_plan ? min(a.topk, C) : a.Lk, stride = Lk + 1, QH = a.Q * kHeads;
+  const int Lk = a.device_plan ? min(a.topk, C) : a.Lk, stride = Lk + 1;
   const uint64_t* src = a.keys + list_offset(b, a.S, QH, a.Lk, 0, task, Lk);
   uint64_t mine;
-  if (network_fits(ns, Lk, a.topk)) {
+  if (guess && C == Cg && ns == nsg) {
+    mine = merge_finish(src, (size_t)Lk, ns, Lk, C, shape, lane, r);
+  } else if (network_fits(ns, Lk, a.topk)) {
     mine = merge_top16(src, (size_t)Lk, ns, Lk, C, lane);
   } else {
     stage_keys(src, lk, ns * Lk, lane, 64, [](int e) { return e; },
