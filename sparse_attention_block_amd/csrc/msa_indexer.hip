@@ -807,7 +807,7 @@ struct SplitArgs {
   int32_t batch;
   int32_t device_plan;  // fused mode: C and each workgroup's (row, split) chosen on the device
   int32_t spread;       // VALU engine, not block-score mode: each wave scores a quarter of every block
-  int32_t even;         // host plan: split s covers blocks [s W / S, (s + 1) W / S) (C: the widest)
+  int32_t even;         // host plan: the first W - S (C - 1) splits of a row cover C blocks, the rest C - 1
   SplitLimits lim;      // device plan: per-row block limits of each split width
   FullRowPlan full;     // device plan: the plan when every row is W blocks long
   uint64_t* keys;       // [batch][4][S * LkMax] (list_offset)
@@ -1065,14 +1065,30 @@ __global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
     b = dp.b;
     C = dp.C;
   }
+  // Even splits: the first `wide` = W - S (C - 1) splits of a row are C blocks long, the rest
+  // C - 1. Workgroups start in the order of their linear id, the 256th ~1.6 us after the first,
+  // so every row's wide splits take the first ids: they start earliest and end with the
+  // narrow ones instead of after them.
+  const int wide = a.W - a.S * (C - 1);
+  if (MODE != kScores && a.even) {
+    const int g = blockIdx.y * a.S + blockIdx.x;
+    if (g < a.batch * wide) {
+      b = g / wide;
+      s = g - b * wide;
+    } else {
+      const int k = g - a.batch * wide, narrow = a.S - wide;
+      b = k / narrow;
+      s = wide + (k - b * narrow);
+    }
+  }
   const int Lk = min(a.topk, C);
   // The wave's first page number and the row's query are read together with the row
   // length rather than after it (the table row has W entries, so the read is in bounds
   // whatever the length); each page number after it is read while the page before it is
   // being scored.
   const int32_t* btrow = a.bt + (size_t)b * a.bt_stride;
-  // The split's first block (with even splits, s W / S: widths C - 1 and C).
-  const int j_start = MODE != kScores && a.even ? (int)((int64_t)s * a.W / a.S) : s * C;
+  // The split's first block (with even splits, s (C - 1) + min(s, wide)).
+  const int j_start = MODE != kScores && a.even ? s * (C - 1) + min(s, wide) : s * C;
   const int j_first = j_start + wave;
   int page = !spread && j_first < a.W ? btrow[j_first] : 0;
   // Spread layout: lane u < C holds the page number of the split's block j_start + u.
@@ -1100,10 +1116,11 @@ __global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
     return;
   }
 
-  // Workgroups that take part in this row (with even splits, those with s W / S < nb).
-  const int ns = a.even ? (int)(((int64_t)nb * a.S + a.W - 1) / a.W) : (nb + C - 1) / C;
+  // Workgroups that take part in this row (with even splits, those that start below nb).
+  const int ns = !a.even ? (nb + C - 1) / C
+                 : nb <= wide * C ? (nb + C - 1) / C : wide + (nb - wide * C + C - 2) / (C - 1);
   const int j0 = j_start;
-  const int j1 = min(a.even ? (int)((int64_t)(s + 1) * a.W / a.S) : j0 + C, nb);
+  const int j1 = min(a.even ? (s + 1) * (C - 1) + min(s + 1, wide) : j0 + C, nb);
   if (s >= ns) {
     // An empty row has no workgroup to merge it: its first workgroup writes the padding.
     if (MODE == kFused && nb == 0 && s == 0) {
@@ -1849,7 +1866,7 @@ struct Plan {
   bool fused;
   bool device = false;  // C and the (row, split) of each workgroup are chosen on the device
   int grid = 0;         // device plan: workgroups launched (1-D)
-  bool even = false;    // split s covers blocks [s W / S, (s + 1) W / S); C = ceil(W / S), the widest
+  bool even = false;    // widths C and C - 1, the wide splits first; C = ceil(W / S), the widest
 };
 
 int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }

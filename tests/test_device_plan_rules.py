@@ -114,3 +114,48 @@ def test_the_longest_row_takes_the_first_workgroups(seed):
     assert pairs == sorted((b, s) for b in range(B) for s in range(int(cnt[b])))
     r0 = int(np.argmax(cnt))
     assert [m[g] for g in range(int(cnt[r0]))] == [(r0, s) for s in range(int(cnt[r0]))]
+
+
+# ---------------------------------------------------------------------------------------
+# Even splits (host plan; 4 <= batch <= 64 rows of W blocks split into S = 256 / batch splits
+# of C = ceil(W / S) or C - 1 blocks): the first wide = W - S (C - 1) splits of a row are the
+# C-block ones, and the linear workgroup id g = y * S + x (the dispatch order) gives every row's
+# wide splits the first ids. Restated from the split kernel's arithmetic.
+
+def even_map(g, batch, S, wide):
+    if g < batch * wide:
+        return g // wide, g % wide
+    k = g - batch * wide
+    narrow = S - wide
+    return k // narrow, wide + k % narrow
+
+
+def even_start(s, C, wide):
+    return s * (C - 1) + min(s, wide)
+
+
+def even_taking_part(nb, C, wide):
+    if nb <= wide * C:
+        return -(-nb // C)
+    return wide + (nb - wide * C + C - 2) // (C - 1)
+
+
+@pytest.mark.parametrize("batch,W", [(16, 68), (8, 150), (4, 300), (64, 17), (32, 40), (5, 251), (16, 80)])
+def test_even_split_layout(batch, W):
+    S = 256 // batch
+    C = -(-W // S)
+    wide = W - S * (C - 1)
+    assert 1 <= wide <= S and C >= 2
+    seen = set()
+    order = []
+    for g in range(batch * S):                      # every workgroup a distinct (row, split)
+        b, s = even_map(g, batch, S, wide)
+        assert 0 <= b < batch and 0 <= s < S and (b, s) not in seen
+        seen.add((b, s))
+        order.append(C if s < wide else C - 1)
+    assert order == sorted(order, reverse=True)      # the wide splits first in dispatch order
+    starts = [even_start(s, C, wide) for s in range(S + 1)]
+    assert starts[0] == 0 and starts[S] == W        # the splits tile the row
+    assert all(starts[s + 1] - starts[s] == (C if s < wide else C - 1) for s in range(S))
+    for nb in range(W + 1):                          # splits that start below nb take part
+        assert even_taking_part(nb, C, wide) == sum(1 for s in range(S) if starts[s] < nb), nb
