@@ -2,7 +2,10 @@
 and full blocks, lengths past the table), topk and pins, split counts, engines, query
 positions and cache types, each drawn from a fixed seed. Every case must select exactly what
 the oracle selects on the GPU's own fp32 block scores (same precision on both sides), report
-those scores bit for bit, and stay within the near-tie rule against the fp64 oracle."""
+those scores bit for bit, and stay within the near-tie rule against the fp64 oracle.
+MSA_RANDOM_SEEDS=lo:hi adds seeds lo..hi-1 to every generator (a wider sweep than the default)."""
+import os
+
 import numpy as np
 import pytest
 
@@ -25,6 +28,15 @@ def msa():
     return m
 
 
+def seeds(default):
+    """The test's seeds, plus lo..hi-1 when MSA_RANDOM_SEEDS=lo:hi asks for a wider sweep."""
+    extra = os.environ.get("MSA_RANDOM_SEEDS", "")
+    if not extra:
+        return list(default)
+    lo, hi = (int(x) for x in extra.split(":"))
+    return list(default) + list(range(lo, hi))
+
+
 def draw_case(seed):
     rng = np.random.default_rng(seed)
     B = int(rng.integers(1, 41))
@@ -45,7 +57,7 @@ def feasible(splits, W):
     return 0 if splits == 0 else min(max(splits, lo), 256)
 
 
-@pytest.mark.parametrize("seed", range(500, 530))
+@pytest.mark.parametrize("seed", seeds(range(500, 530)))
 def test_random_single_token(msa, seed):
     B, W, lens, topk, n_init, n_local, splits = draw_case(seed)
     inp = synth.paged_case(seed, lens.tolist(), W, topk=topk, n_init=n_init, n_local=n_local)
@@ -64,7 +76,7 @@ def test_random_single_token(msa, seed):
     check_selection_vs_oracle(ids, ref, L, topk, n_init, n_local)
 
 
-@pytest.mark.parametrize("seed", range(700, 712))
+@pytest.mark.parametrize("seed", seeds(range(700, 712)))
 def test_random_long_rows_small_batch(msa, seed):
     # Small batches of long rows among short ones, where rows take up to 256 splits: the
     # pruned merge, the two-level count and single-split rows, under automatic and asked-for
@@ -89,7 +101,7 @@ def test_random_long_rows_small_batch(msa, seed):
     check_selection_vs_oracle(ids, ref, inp.seq_lens, topk, n_init, n_local)
 
 
-@pytest.mark.parametrize("seed", range(600, 615))
+@pytest.mark.parametrize("seed", seeds(range(600, 615)))
 def test_random_multi_and_fp8(msa, seed):
     B, W, lens, topk, n_init, n_local, splits = draw_case(seed)
     Q = int(np.random.default_rng(seed + 1).integers(1, 5))
