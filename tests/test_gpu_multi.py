@@ -215,3 +215,22 @@ def test_multi_workspace_reuse_and_graph_replay(msa, Q):
         torch.cuda.synchronize()
         eager_ids, eager_sc = msa.msa_indexer_decode_multi(q, k, bt, lens)
         assert torch.equal(ids, eager_ids) and torch.equal(sc, eager_sc), it
+
+
+@pytest.mark.parametrize("Q", [2, 4])
+def test_merge_kernel_full_row_guess(msa, Q):
+    # The merge kernel reads a task's lists for a full row under the full-row plan before the row
+    # lengths arrive, and keeps that read only when the row takes that plan. Host plan (4 rows of
+    # 100 blocks, splits of 4): full rows (kept), a row ending inside its last split (kept, fewer
+    # blocks than the table), rows of half the table (read again). Device plan (64 rows of 128
+    # blocks): every row full (kept), then rows of mixed lengths (a general plan).
+    W = 100
+    for lens in ([128 * W] * 4, [128 * 98 + 5, 128 * W, 128 * 97 + 1, 128 * W], [128 * 50, 128 * 49 + 3, 128 * W, 0]):
+        run_multi(msa, synth.multi_case(230 + Q, lens, W, Q, poison=False))
+    W = 128
+    rng = np.random.default_rng(231 + Q)
+    mixed = rng.integers(0, 128 * W + 1, size=64)
+    for lens in ([128 * W] * 64, mixed.tolist()):
+        run_multi(msa, synth.multi_case(232 + Q, lens, W, Q, poison=False))
+    from test_gpu_fp8 import run_fp8
+    run_fp8(msa, synth.fp8_case(234 + Q, [128 * W] * 64, W, Q, k_scale=0.5, poison=False), 1e-3 * 4.0 * 0.5)
