@@ -124,13 +124,31 @@ def rate(nbytes: int, us: float) -> dict:
     return {"us": round(us, 2), "GBs": round(gbs, 1), "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2)}
 
 
+def lscpu_model(text: str) -> str | None:
+    """The model name lscpu prints, with the CPU family, model and stepping numbers (virtual
+    machines often print a bare family name such as "AMD EPYC") and the hypervisor, if any."""
+    fields = {}
+    for line in text.splitlines():
+        if ":" in line:
+            key, value = line.split(":", 1)
+            fields[key.strip()] = value.strip()
+    name = fields.get("Model name")
+    if not name:
+        return None
+    ids = [f"{label} {fields[key]}" for key, label in (("CPU family", "family"), ("Model", "model"),
+                                                        ("Stepping", "stepping")) if fields.get(key)]
+    if fields.get("Hypervisor vendor"):
+        ids.append(f"{fields['Hypervisor vendor']} guest")
+    return f"{name} ({', '.join(ids)})" if ids else name
+
+
 def cpu_model() -> str:
-    """The host CPU's model name as lscpu reports it (/proc/cpuinfo if lscpu is missing)."""
+    """The host CPU's model as lscpu reports it (/proc/cpuinfo if lscpu is missing)."""
     try:
         out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
-        for line in out.splitlines():
-            if line.strip().startswith("Model name:"):
-                return line.split(":", 1)[1].strip()
+        model = lscpu_model(out)
+        if model:
+            return model
     except (OSError, subprocess.SubprocessError):
         pass
     try:

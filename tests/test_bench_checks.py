@@ -83,3 +83,12 @@ def test_oracle_agreement_rule():
     res = bench.oracle_agreement(swapped, (ids3, sc3, s3.astype(np.float64)), lens, 16, 1, 2)
     assert not res["ok"] and res["rows_failing"] == 1
     bench.FAILED_CHECKS[:] = before
+
+
+def test_lscpu_model_adds_family_model_and_hypervisor():
+    text = ("Architecture:            x86_64\nVendor ID:               AuthenticAMD\n"
+            "Model name:              AMD EPYC\nCPU family:              26\nModel:                   2\n"
+            "Thread(s) per core:      1\nStepping:                1\nHypervisor vendor:       KVM\n")
+    assert bench.lscpu_model(text) == "AMD EPYC (family 26, model 2, stepping 1, KVM guest)"
+    assert bench.lscpu_model("Model name: Some CPU\n") == "Some CPU"
+    assert bench.lscpu_model("Architecture: x86_64\n") is None
