@@ -1058,12 +1058,14 @@ __global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   constexpr bool spread = SPREAD;
   int s = blockIdx.x, b = blockIdx.y, C = a.C;
+  int Ldp = -1;  // the device plan's row length (clamped): no second read of it
   if (MODE == kFused && a.device_plan) {
     const DevicePlan dp = device_plan(a.lens, a.batch, a.W, a.lim, a.full, blockIdx.x, lane);
     if (!dp.active) return;
     s = dp.s;
     b = dp.b;
     C = dp.C;
+    Ldp = dp.L;
   }
   // Even splits: the first `wide` = W - S (C - 1) splits of a row are C blocks long, the rest
   // C - 1. Workgroups start in the order of their linear id, the 256th ~1.6 us after the first,
@@ -1096,7 +1098,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
   typename std::conditional<ENGINE == MSA_ENGINE_MFMA, QMfma, QValu>::type qr;
   if constexpr (ENGINE == MSA_ENGINE_MFMA) load_q_mfma(a.q, b, lane, qr);
   else load_q_valu(a.q, b, lane, qr);
-  const int L = row_tokens(a.lens, b, a.W);
+  const int L = Ldp >= 0 ? Ldp : row_tokens(a.lens, b, a.W);
   const int nb = (L + kBlock - 1) / kBlock;
 
   if (MODE == kScores) {  // block scores out; -inf at and past the row's end
